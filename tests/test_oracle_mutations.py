@@ -1,0 +1,47 @@
+"""Planted mistakes in a copy of the oracle must fail its pins.
+
+Each case edits one line of oracle/oracle.c in a temporary copy of the
+oracle, tests and input generators, then runs tests/test_oracle_pins.py
+there; the pins must fail.  Nothing here touches a GPU.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = {
+    "mask_drops_diagonal": ("int64_t visible = P + i + 1;", "int64_t visible = P + i;"),
+    "mask_sees_next_token": ("int64_t visible = P + i + 1;",
+                             "int64_t visible = P + i + 1 + (i + 1 < (qo_indptr[b + 1] - qo_indptr[b]));"),
+    "kv_head_modulo": ("int32_t g = h / group;", "int32_t g = h % hkv;"),
+    "default_scale_from_lv": ("1.0 / sqrt((double)lq)", "1.0 / sqrt((double)lv)"),
+    "cap_without_division": ("x = logit_cap * tanh(x / logit_cap);", "x = tanh(x) * logit_cap;"),
+    "extend_row_shift": ("koff = (qo_indptr[b] + (j - P)) * ke_st",
+                         "koff = (qo_indptr[b] + (j - P) + (j > P)) * ke_st"),
+    "index_copy_shift": ("unified_kv_indices[u + p_len + o]", "unified_kv_indices[u + p_len + o - (o > 0)]"),
+    "first_weight_bias": ("double wgt = exp(s[j] - m);", "double wgt = exp(s[j] - m) * (j == 0 ? 1.0001 : 1.0);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    before, after = MUTATIONS[name]
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert before in src
+    ign = shutil.ignore_patterns("*.so", "*.so.tmp*", "__pycache__")
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle", ignore=ign)
+    os.makedirs(tmp_path / "tests")
+    for f in ("conftest.py", "test_oracle_pins.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
+    shutil.copy(os.path.join(ROOT, "workloads.py"), tmp_path / "workloads.py")
+    (tmp_path / "oracle" / "oracle.c").write_text(src.replace(before, after, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, f"pins did not catch {name}:\n{r.stdout[-2000:]}"

@@ -1,0 +1,271 @@
+"""Pins for the CPU oracle against facts fixed outside the oracle itself.
+
+Index build: a hand-worked example and list concatenation of slices.
+Attention: torch's scaled_dot_product_attention over an explicitly
+concatenated prefix + extend K/V (the reference helper redundant_attention
+on the SGLang page extend_attention.py does the same), closed forms (q = 0
+gives the running mean of the visible values; saturated soft-cap logits give
+weights e^{+-cap}), and exact invariants (pool-slot permutation, batch
+permutation, KV-head expansion, cap -> infinity).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- index build
+
+def test_index_worked_example():
+    with open(os.path.join(GOLDEN, "unified_indices_worked_example.json")) as f:
+        ex = json.load(f)
+    indptr, indices, plens = oracle.build_unified_kv_indices(
+        ex["prefix_kv_indptr"], ex["prefix_kv_indices"], ex["extend_start_loc"],
+        ex["extend_seq_lens"], ex["extend_kv_indices"], ex["bs"])
+    n = ex["expected_unified_kv_indptr"][-1]
+    assert indptr.tolist() == ex["expected_unified_kv_indptr"]
+    assert indices[:n].tolist() == ex["expected_unified_kv_indices"]
+    assert plens.tolist() == ex["expected_prefix_lens"]
+
+
+def _concat_slices(c):
+    out, indptr = [], [0]
+    for b in range(c["bs"]):
+        lo, hi = int(c["prefix_kv_indptr"][b]), int(c["prefix_kv_indptr"][b + 1])
+        es, el = int(c["extend_start_loc"][b]), int(c["extend_seq_lens"][b])
+        seg = list(c["prefix_kv_indices"][lo:hi]) + list(c["extend_kv_indices"][es:es + el])
+        out += seg
+        indptr.append(indptr[-1] + len(seg))
+    return indptr, out
+
+
+@pytest.mark.parametrize("bs,extra,base", [(0, 0, 0), (1, 0, 0), (5, 3, 0), (17, 0, 9), (64, 2, 1)])
+def test_index_matches_slice_concatenation(bs, extra, base):
+    rng = np.random.default_rng(100 + bs)
+    c = wl.index_case(rng, bs, extra_tail=extra, indptr_base=base)
+    indptr, indices, plens = oracle.build_unified_kv_indices(
+        c["prefix_kv_indptr"], c["prefix_kv_indices"], c["extend_start_loc"],
+        c["extend_seq_lens"], c["extend_kv_indices"], bs)
+    want_indptr, want = _concat_slices(c)
+    assert indptr.tolist() == want_indptr
+    assert indices[:len(want)].tolist() == want
+    assert plens.tolist() == np.diff(c["prefix_kv_indptr"]).tolist()
+    # capacity is the two input lengths; the total fits
+    assert len(indices) == len(c["prefix_kv_indices"]) + len(c["extend_kv_indices"])
+    assert indptr[-1] <= len(indices)
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _f64(x, dtype):
+    return torch.from_numpy(wl.as_f32(np.ascontiguousarray(x), dtype).astype(np.float64))
+
+
+def sdpa_reference(w, scale=None):
+    """Library attention over the explicitly concatenated prefix + extend K/V."""
+    c = w.cfg
+    g = c.hq // c.hkv
+    outs = []
+    for b in range(w.bs):
+        q0, q1 = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+        k0, k1 = int(w.kv_indptr[b]), int(w.kv_indptr[b + 1])
+        if q1 == q0:
+            continue
+        slots = w.kv_indices[k0:k1]
+        k_full = torch.cat([_f64(w.k_pool[slots], c.dtype), _f64(w.k_ext[q0:q1], c.dtype)], 0)
+        v_full = torch.cat([_f64(w.v_pool[slots], c.dtype), _f64(w.v_ext[q0:q1], c.dtype)], 0)
+        q = _f64(w.q[q0:q1], c.dtype)
+        E, P = q1 - q0, k1 - k0
+        mask = torch.ones(E, P + E, dtype=torch.bool).tril(diagonal=P)
+        k_h = k_full.transpose(0, 1).repeat_interleave(g, dim=0)  # [Hq, P+E, Lq]
+        v_h = v_full.transpose(0, 1).repeat_interleave(g, dim=0)
+        sc = scale if scale is not None else (c.sm_scale or 1.0 / math.sqrt(c.lq))
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q.transpose(0, 1), k_h, v_h, attn_mask=mask, scale=sc)
+        outs.append(o.transpose(0, 1))
+    return torch.cat(outs, 0).numpy()
+
+
+SDPA_CASES = [
+    dict(dtype="fp32", prefix_lens=[16, 0], extend_lens=[8, 12], hq=4, hkv=2, lq=64, lv=64, sm_scale=1 / 8),
+    dict(dtype="bf16", prefix_lens=[5, 0, 33, 1], extend_lens=[1, 7, 20, 3], hq=8, hkv=8, lq=32, lv=32),
+    dict(dtype="bf16", prefix_lens=[40, 9], extend_lens=[17, 1], hq=6, hkv=2, lq=192, lv=128),
+    dict(dtype="bf16", prefix_lens=[13], extend_lens=[6], hq=4, hkv=1, lq=288, lv=256),
+    dict(dtype="bf16", prefix_lens=[7, 21], extend_lens=[5, 4], hq=8, hkv=1, lq=576, lv=512,
+         v_aliases_k=True, std=0.5),
+    dict(dtype="fp32", prefix_lens=[0, 0, 0], extend_lens=[9, 1, 15], hq=2, hkv=1, lq=16, lv=24,
+         sm_scale=-0.3),
+]
+
+
+@pytest.mark.parametrize("case", SDPA_CASES, ids=lambda c: f"{c['dtype']}-{c['lq']}x{c['lv']}-h{c['hq']}/{c['hkv']}")
+def test_oracle_matches_library_attention(case):
+    w = wl.custom(**case)
+    got = oracle.extend_attention_workload(w)
+    want = sdpa_reference(w)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_default_scale_uses_query_head_dim():
+    # 192 / 128: the default scale is 1/sqrt(Lq), not 1/sqrt(Lv)
+    w = wl.custom(dtype="bf16", prefix_lens=[11], extend_lens=[4], hq=2, hkv=1, lq=192, lv=128)
+    got = oracle.extend_attention_workload(w)
+    np.testing.assert_allclose(got, sdpa_reference(w, scale=1 / math.sqrt(192)), atol=1e-12)
+    assert np.abs(got - sdpa_reference(w, scale=1 / math.sqrt(128))).max() > 1e-6
+
+
+def test_zero_prefix_is_plain_causal_attention():
+    w = wl.custom(dtype="bf16", prefix_lens=[0, 0], extend_lens=[23, 5], hq=4, hkv=2, lq=64, lv=64)
+    got = oracle.extend_attention_workload(w)
+    outs = []
+    for b in range(2):
+        q0, q1 = w.qo_indptr[b], w.qo_indptr[b + 1]
+        q = _f64(w.q[q0:q1], "bf16").transpose(0, 1)
+        k = _f64(w.k_ext[q0:q1], "bf16").transpose(0, 1).repeat_interleave(2, 0)
+        v = _f64(w.v_ext[q0:q1], "bf16").transpose(0, 1).repeat_interleave(2, 0)
+        outs.append(torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True).transpose(0, 1))
+    np.testing.assert_allclose(got, torch.cat(outs).numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("cap", [0.0, 2.5])
+def test_zero_query_gives_running_mean(cap):
+    # q = 0 makes every logit 0 (also after the cap): row i averages V over keys 0..P+i.
+    w = wl.custom(dtype="fp32", prefix_lens=[6, 0, 3], extend_lens=[4, 3, 1], hq=4, hkv=2,
+                  lq=16, lv=8, logit_cap=cap)
+    w.q[:] = 0
+    got = oracle.extend_attention_workload(w)
+    for b in range(w.bs):
+        P = int(w.kv_indptr[b + 1] - w.kv_indptr[b])
+        slots = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        q0 = int(w.qo_indptr[b])
+        for i in range(int(w.extend_lens[b])):
+            for h in range(4):
+                g = h // 2
+                vals = [w.v_pool[s, g].astype(np.float64) for s in slots]
+                vals += [w.v_ext[q0 + j, g].astype(np.float64) for j in range(i + 1)]
+                assert len(vals) == P + i + 1
+                np.testing.assert_allclose(got[q0 + i, h], np.mean(vals, axis=0), atol=1e-13)
+
+
+def test_kv_head_of_query_head_is_integer_division():
+    # V constant per KV head g (value g + 1) makes every output equal to g(h) + 1.
+    w = wl.custom(dtype="fp32", prefix_lens=[5, 2], extend_lens=[3, 4], hq=6, hkv=3, lq=8, lv=4)
+    for g in range(3):
+        w.v_pool[:, g] = g + 1
+        w.v_ext[:, g] = g + 1
+    got = oracle.extend_attention_workload(w)
+    for h in range(6):
+        np.testing.assert_allclose(got[:, h], h // 2 + 1, atol=1e-12)
+
+
+def test_saturated_soft_cap_closed_form():
+    # Logits +-1000 with cap 1: tanh saturates, the weights are exactly e and 1/e.
+    lq = 4
+    w = wl.custom(dtype="fp32", prefix_lens=[3], extend_lens=[1], hq=1, hkv=1, lq=lq, lv=2,
+                  sm_scale=1.0, logit_cap=1.0)
+    w.q[0, 0] = [1000.0, 0, 0, 0]
+    signs = [1.0, -1.0, -1.0, 1.0]  # prefix keys 0..2, then the token's own key
+    keys = [w.k_pool[s, 0] for s in w.kv_indices] + [w.k_ext[0, 0]]
+    for k, sgn in zip(keys, signs):
+        k[:] = [sgn, 0, 0, 0]
+    vals = [w.v_pool[s, 0].astype(np.float64) for s in w.kv_indices] + [w.v_ext[0, 0].astype(np.float64)]
+    wts = [math.e if s > 0 else 1 / math.e for s in signs]
+    want = sum(wt * v for wt, v in zip(wts, vals)) / sum(wts)
+    got = oracle.extend_attention_workload(w)
+    np.testing.assert_allclose(got[0, 0], want, atol=1e-14)
+
+
+def test_huge_cap_is_no_cap():
+    w = wl.custom(dtype="bf16", prefix_lens=[9, 30], extend_lens=[4, 11], hq=4, hkv=2, lq=64, lv=64)
+    base = oracle.extend_attention_workload(w)
+    object.__setattr__(w.cfg, "logit_cap", 1e30)
+    np.testing.assert_allclose(oracle.extend_attention_workload(w), base, atol=1e-12)
+
+
+def test_cap_bounds_weight_ratio():
+    # With cap 1 every logit lies in [-1, 1]: weights differ by at most e^2, so each
+    # output is within the values' range and no key dominates.
+    w = wl.custom(dtype="fp32", prefix_lens=[3], extend_lens=[1], hq=1, hkv=1, lq=8, lv=3,
+                  sm_scale=1.0, logit_cap=1.0, std=30.0)
+    got = oracle.extend_attention_workload(w)
+    vals = np.stack([w.v_pool[s, 0] for s in w.kv_indices] + [w.v_ext[0, 0]]).astype(np.float64)
+    # o = sum a_j v_j with a_j >= e^-2 / (n e^0 ...) : each weight is at least 1/(1 + (n-1) e^2)
+    n = len(vals)
+    lo = 1.0 / (1 + (n - 1) * math.e ** 2)
+    # recover weights from a second run where V is the identity basis
+    w2 = wl.custom(dtype="fp32", prefix_lens=[3], extend_lens=[1], hq=1, hkv=1, lq=8, lv=4,
+                   sm_scale=1.0, logit_cap=1.0, std=30.0)
+    basis = np.eye(4, dtype=np.float32)
+    for j, s in enumerate(w2.kv_indices):
+        w2.v_pool[s, 0] = basis[j]
+    w2.v_ext[0, 0] = basis[3]
+    wts = oracle.extend_attention_workload(w2)[0, 0]
+    assert wts.min() >= lo - 1e-12 and abs(wts.sum() - 1) < 1e-12
+    assert np.isfinite(got).all()
+
+
+def test_pool_slot_permutation_is_exact():
+    w = wl.custom(dtype="bf16", prefix_lens=[12, 0, 25], extend_lens=[3, 9, 2], hq=4, hkv=2,
+                  lq=64, lv=64, pool_slots=80)
+    base = oracle.extend_attention_workload(w)
+    perm = np.random.default_rng(3).permutation(80)  # new slot of old slot s is perm[s]
+    k2 = np.empty_like(w.k_pool)
+    v2 = np.empty_like(w.v_pool)
+    k2[perm] = w.k_pool
+    v2[perm] = w.v_pool
+    got = oracle.extend_attention(w.q, w.k_ext, w.v_ext, k2, v2, w.qo_indptr, w.kv_indptr,
+                                  perm[w.kv_indices], dtype="bf16")
+    assert np.array_equal(got, base)
+
+
+def test_batch_permutation_is_exact():
+    w = wl.custom(dtype="bf16", prefix_lens=[12, 0, 25, 4], extend_lens=[3, 9, 2, 6], hq=4,
+                  hkv=2, lq=32, lv=32)
+    base = oracle.extend_attention_workload(w)
+    order = [2, 0, 3, 1]
+    q_rows, ke, ve, kvi, e_l, p_l = [], [], [], [], [], []
+    for b in order:
+        q0, q1 = w.qo_indptr[b], w.qo_indptr[b + 1]
+        q_rows.append(np.arange(q0, q1))
+        kvi.append(w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]])
+        e_l.append(q1 - q0)
+        p_l.append(w.kv_indptr[b + 1] - w.kv_indptr[b])
+    rows = np.concatenate(q_rows)
+    qo = np.concatenate([[0], np.cumsum(e_l)]).astype(np.int32)
+    kvp = np.concatenate([[0], np.cumsum(p_l)]).astype(np.int32)
+    got = oracle.extend_attention(np.ascontiguousarray(w.q[rows]), np.ascontiguousarray(w.k_ext[rows]),
+                                  np.ascontiguousarray(w.v_ext[rows]), w.k_pool, w.v_pool, qo, kvp,
+                                  np.concatenate(kvi), dtype="bf16")
+    assert np.array_equal(got, base[rows])
+
+
+def test_kv_head_expansion_is_exact():
+    w = wl.custom(dtype="bf16", prefix_lens=[10, 3], extend_lens=[5, 7], hq=6, hkv=2, lq=32, lv=32)
+    base = oracle.extend_attention_workload(w)
+    rep = lambda x: np.ascontiguousarray(np.repeat(x, 3, axis=1))
+    got = oracle.extend_attention(w.q, rep(w.k_ext), rep(w.v_ext), rep(w.k_pool), rep(w.v_pool),
+                                  w.qo_indptr, w.kv_indptr, w.kv_indices, dtype="bf16")
+    assert np.array_equal(got, base)
+
+
+def test_sampled_rows_equal_full_rows():
+    w = wl.custom(dtype="bf16", prefix_lens=[10, 3, 0], extend_lens=[5, 7, 2], hq=4, hkv=2, lq=32, lv=32)
+    base = oracle.extend_attention_workload(w)
+    rows = np.array([13, 0, 6, 5])
+    assert np.array_equal(oracle.extend_attention_workload(w, rows=rows), base[rows])
+
+
+def test_out_of_range_slot_is_an_error():
+    w = wl.custom(dtype="fp32", prefix_lens=[3], extend_lens=[1], hq=1, hkv=1, lq=8, lv=8, pool_slots=8)
+    w.kv_indices[1] = 8
+    with pytest.raises(ValueError):
+        oracle.extend_attention_workload(w)
