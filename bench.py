@@ -1,0 +1,183 @@
+#!/usr/bin/env python3
+"""Benchmark of the extend-attention hot path on one MI355X.
+
+One step = the whole path over one batch: the unified KV index build, then
+extend attention (device planner, attention kernel, split merge).  Inputs
+are seeded synthetic tensors already resident in HBM; several copies are
+rotated so that the working set exceeds the 256 MiB last-level cache.
+
+Prints ONE JSON line:
+  value     causal-adjusted TFLOP/s of the whole step (visible (query, key)
+            pairs x Hq x 2 (Lq + Lv), divided by the mean step time)
+  roofline  the attention kernel alone: its TFLOP/s from HIP events recorded
+            on its own stream around every launch in the timed region,
+            against the MI355X dense bf16 MFMA peak
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "fp32": 157.3}  # TFLOP/s: dense MFMA bf16, fp32 vector/MFMA
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "llama8b"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = enough to exceed 512 MiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attention_traffic.json"),
+                    help="HBM bytes per attention launch measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, target_s):
+    """The oracle, as it is, on a sample of rows of the same workload."""
+    import oracle
+
+    rng = np.random.default_rng(123)
+    cores = oracle.max_threads()
+    e = w.extend_lens.astype(np.int64)
+    p = w.prefix_lens.astype(np.int64)
+    seq_of = np.repeat(np.arange(w.bs), e)
+    pos = np.arange(w.total_q) - np.repeat(w.qo_indptr[:-1].astype(np.int64), e)
+    keys_per_row = p[seq_of] + pos + 1
+    flop_per_row = keys_per_row * w.cfg.hq * 2.0 * (w.cfg.lq + w.cfg.lv)
+
+    def run(n):
+        rows = np.sort(rng.choice(w.total_q, size=min(n, w.total_q), replace=False))
+        t0 = time.perf_counter()
+        oracle.extend_attention_workload(w, rows=rows)
+        return time.perf_counter() - t0, float(flop_per_row[rows].sum()), len(rows)
+
+    dt, fl, n = run(32)
+    rate = fl / max(dt, 1e-6)
+    want_rows = int(min(w.total_q, max(32, target_s * rate / float(flop_per_row.mean()))))
+    if want_rows > n:
+        dt, fl, n = run(want_rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.total_q} new-token rows (all {w.cfg.hq} heads) of the same batch, "
+                      f"{fl / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 C loops with OpenMP"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(sharding is described in DESIGN.md, not run).", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_extend_amd as pkv
+    import workloads as wl
+
+    if not os.path.exists(pkv.LIB_PATH):
+        from paged_kv_extend_amd import _build
+        _build.build()
+    torch.cuda.init()
+    dev = torch.device("cuda", 0)
+    w = wl.get(args.workload)
+    flops = w.causal_flops()
+    algo_bytes = w.algorithmic_bytes()
+    copies = args.copies or max(1, int(np.ceil(512e6 / algo_bytes)))
+    sets = [wl.to_torch(w, dev) for _ in range(copies)]
+    for s in sets:
+        s["uni"] = (torch.empty(w.bs + 1, dtype=torch.int32, device=dev),
+                    torch.empty(w.num_prefix + w.total_q, dtype=torch.int64, device=dev),
+                    torch.empty(w.bs, dtype=torch.int32, device=dev))
+        desc = pkv.make_desc(s["q"], s["k_ext"], s["v_ext"], s["o"], s["k_pool"], s["v_pool"], w.bs,
+                             w.num_prefix)
+        s["ws"] = torch.empty(pkv.extend_attention_workspace_size(desc), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s = sets[i % copies]
+        pkv.build_unified_kv_indices(s["kv_indptr"], s["kv_indices"], s["extend_start_loc"],
+                                     s["extend_seq_lens"], s["extend_kv_indices"], w.bs, out=s["uni"])
+        pkv.extend_attention_fwd(s["q"], s["k_ext"], s["v_ext"], s["o"], s["k_pool"], s["v_pool"],
+                                 s["qo_indptr"], s["kv_indptr"], s["kv_indices"], sm_scale=w.sm_scale,
+                                 logit_cap=w.logit_cap, workspace=s["ws"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pkv.profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pkv.profile_enable(False)
+    attn_ms_total, calls = pkv.profile_read()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    ms_attn = attn_ms_total / max(calls, 1)
+
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+    peak = PEAK[w.cfg.dtype]
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        if tj.get("workload") == args.workload and tj.get("kernel_source_sha") == kernel_source_sha():
+            traffic = tj.get("bytes_per_launch")
+    line = {
+        "metric": "extend-attention TFLOP/s (causal-adjusted) + % of bf16 MFMA peak, 1 GPU",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.cfg.name, "description": w.cfg.description, "bs": w.bs,
+                   "q_heads": w.cfg.hq, "kv_heads": w.cfg.hkv, "lq": w.cfg.lq, "lv": w.cfg.lv,
+                   "extend_tokens": w.total_q, "prefix_tokens": w.num_prefix, "seed": w.cfg.seed,
+                   "causal_gflop": round(flops / 1e9, 3), "algorithmic_mb": round(algo_bytes / 1e6, 2),
+                   "input_copies_rotated": copies, "wall_s_timed": round(wall, 3)},
+        "mfma_frac_step": round(flops / (ms_per_step * 1e-3) / 1e12 / peak, 4),
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "ms_per_launch": round(ms_attn, 4),
+                     "hbm_gbs_algorithmic": round(algo_bytes / (ms_attn * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def kernel_source_sha():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("attention.hip", "plan.hip"):
+        with open(os.path.join(ROOT, "paged_kv_extend_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,197 @@
+/*
+ * pkv.h -- C ABI of the paged-KV extend-attention library (libpkv.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Extend attention is prefill with a cached prefix: every new ("extend")
+ * token of a sequence attends to the sequence's cached prefix, read from a
+ * token-granular KV pool through slot indices, and causally to the new
+ * tokens of its own sequence.  The operations follow the SGLang pages on
+ * the subject: page "extend_attention.py" (sglang 0.5.3rc2 -> 0.5.4.post1
+ * diff) and page "flashinfer_backend.py" (blame view).
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers, owned by the caller; the
+ *    library allocates nothing and keeps no state between calls (it caches
+ *    device properties only).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and is asynchronous.  No call waits for the device or copies device data
+ *    to the host, so every call may be captured into a HIP graph.
+ *  - Arguments are checked on the host only, from the sizes passed in.  A
+ *    non-zero return means nothing was enqueued; pkv_last_error() then holds a
+ *    message.  Values inside device arrays (lengths, slots) are trusted: they
+ *    must be consistent with the sizes passed in, as documented per argument.
+ *  - Index/offset arrays: indptr and length arrays are int32, slot index
+ *    arrays are int64.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define PKV_OK 0
+#define PKV_ERR_INVALID (-1)     /* null pointer, negative size, inconsistent sizes */
+#define PKV_ERR_UNSUPPORTED (-2) /* dtype, head dims, stride or alignment not supported */
+#define PKV_ERR_WORKSPACE (-3)   /* workspace missing or smaller than the size query */
+#define PKV_ERR_CAPACITY (-4)    /* output index buffer too small */
+#define PKV_ERR_HIP (-5)         /* a HIP runtime call or kernel launch failed */
+
+/* Element types of q / k / v / o and the pools. */
+#define PKV_BF16 0
+#define PKV_FP32 1
+
+/*
+ * Unified KV index build.
+ * Page "extend_attention.py": build_unified_kv_indices and
+ * _copy_unified_indices_kernel.  For b in [0, bs):
+ *   prefix_lens[b]          = prefix_kv_indptr[b+1] - prefix_kv_indptr[b]
+ *   unified_kv_indptr[0]    = 0
+ *   unified_kv_indptr[b+1]  = unified_kv_indptr[b] + prefix_lens[b] + extend_seq_lens[b]
+ *   unified_kv_indices[unified_kv_indptr[b] + o] =
+ *       prefix_kv_indices[prefix_kv_indptr[b] + o]               for o <  prefix_lens[b]
+ *       extend_kv_indices[extend_start_loc[b] + o - prefix_lens[b]] otherwise
+ *
+ * Arguments (device pointers unless noted):
+ *  prefix_kv_indptr   int32[bs+1], non-decreasing; need not start at 0.
+ *  prefix_kv_indices  int64[num_prefix_indices]; read at
+ *                     [prefix_kv_indptr[0], prefix_kv_indptr[bs]).
+ *  extend_start_loc   int32[>= bs]; only the first bs entries are read.
+ *  extend_seq_lens    int32[>= bs], >= 0; only the first bs entries are read.
+ *  extend_kv_indices  int64[num_extend_indices].
+ *  bs                 host int, >= 0; bs == 0 writes unified_kv_indptr[0] = 0 only.
+ *  num_prefix_indices, num_extend_indices
+ *                     host ints: lengths of the two input index arrays.
+ *  unified_kv_indptr  out int32[bs+1].
+ *  unified_kv_indices out int64[capacity]; entries at and past
+ *                     unified_kv_indptr[bs] are not written.
+ *  capacity           host int; must be >= num_prefix_indices + num_extend_indices
+ *                     (the page sizes its output the same way, so no device
+ *                     value has to be read on the host), else PKV_ERR_CAPACITY.
+ *  prefix_lens        out int32[bs], or NULL when not wanted.
+ *  stream             hipStream_t.
+ * The caller guarantees that every sequence's slices lie inside the input
+ * arrays and that the total fits int32.
+ */
+int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
+                             const int32_t* extend_start_loc, const int32_t* extend_seq_lens,
+                             const int64_t* extend_kv_indices, int32_t bs,
+                             int64_t num_prefix_indices, int64_t num_extend_indices,
+                             int32_t* unified_kv_indptr, int64_t* unified_kv_indices,
+                             int64_t capacity, int32_t* prefix_lens, void* stream);
+
+/*
+ * Shapes and strides of one extend-attention call.  Strides are in
+ * ELEMENTS; the last dimension of every tensor is contiguous.
+ *
+ *  q_extend  [total_q_tokens, num_q_heads, lq]   strides (q_stride_tok, q_stride_head)
+ *  k_extend  [total_q_tokens, num_kv_heads, lq]  strides (ke_stride_tok, ke_stride_head)
+ *  v_extend  [total_q_tokens, num_kv_heads, lv]  strides (ve_stride_tok, ve_stride_head)
+ *  o         [total_q_tokens, num_q_heads, lv]   strides (o_stride_tok, o_stride_head)
+ *  k_pool    [pool_slots, num_kv_heads, lq]      strides (kp_stride_slot, kp_stride_head)
+ *  v_pool    [pool_slots, num_kv_heads, lv]      strides (vp_stride_slot, vp_stride_head)
+ *
+ * v_pool / v_extend may be views into k_pool / k_extend (the MLA layout on
+ * page "cpu_graph_runner.py", qkv_proj_with_rope: V is the first lv columns
+ * of the joint latent+rope K row).  Supported (lq, lv): (64,64), (128,128),
+ * (256,256), (192,128), (288,256), (576,512) for bf16; (64,64), (128,128)
+ * for fp32.  Strides must be multiples of 8 elements (bf16) or 4 (fp32) and
+ * base pointers 16-byte aligned.
+ */
+typedef struct {
+  int32_t dtype; /* PKV_BF16 or PKV_FP32: q, k/v extend, pools and o share it */
+  int32_t bs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads; /* must divide num_q_heads */
+  int32_t lq;           /* head dim of q and k */
+  int32_t lv;           /* head dim of v and o */
+  int64_t total_q_tokens;     /* qo_indptr[bs] */
+  int64_t num_prefix_indices; /* kv_indptr[bs] - kv_indptr[0] (length of kv_indices) */
+  int64_t pool_slots;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  int64_t ke_stride_tok, ke_stride_head;
+  int64_t ve_stride_tok, ve_stride_head;
+  int64_t kp_stride_slot, kp_stride_head;
+  int64_t vp_stride_slot, vp_stride_head;
+} pkv_attn_desc_t;
+
+/*
+ * Bytes of device workspace extend_attention_fwd needs for `desc` (a
+ * function of the sizes only).  Returns 0 when desc is invalid; then
+ * pkv_last_error() says why.
+ */
+size_t extend_attention_workspace_size(const pkv_attn_desc_t* desc);
+
+/*
+ * Extend attention forward.
+ * Page "extend_attention.py": _fwd_kernel_unified (causal mask, scale,
+ * soft-cap, online softmax, GQA head mapping) and extend_attention_fwd
+ * (default scale); page "flashinfer_backend.py": forward_extend and
+ * call_begin_forward (prefix read through kv_indptr / kv_indices, the new
+ * tokens' K/V rows addressed by qo_indptr).
+ *
+ * For sequence b (P_b = kv_indptr[b+1] - kv_indptr[b] prefix tokens,
+ * E_b = qo_indptr[b+1] - qo_indptr[b] new tokens), new token i in [0, E_b),
+ * query head h and its KV head g = h / (num_q_heads / num_kv_heads):
+ *   key j < P_b   : k_pool[kv_indices[kv_indptr[b] + j], g], v_pool likewise
+ *   key j >= P_b  : k_extend[qo_indptr[b] + j - P_b, g], v_extend likewise
+ *   visible keys  : j <= P_b + i
+ *   s_j = scale * <q[qo_indptr[b] + i, h], K_j>, scale = sm_scale, or
+ *         1/sqrt(lq) when sm_scale == 0;
+ *   if logit_cap > 0: s_j = logit_cap * tanh(s_j / logit_cap)
+ *   o[qo_indptr[b] + i, h] = sum_j softmax(s)_j V_j over the visible keys.
+ * The K/V of the new tokens are NOT written into the pool here.
+ *
+ * Arguments (device pointers unless noted):
+ *  q_extend, k_extend, v_extend, k_pool, v_pool: as in pkv_attn_desc_t.
+ *  o           out, as in pkv_attn_desc_t; rows of every new token are written.
+ *  qo_indptr   int32[bs+1], qo_indptr[0] == 0, non-decreasing, qo_indptr[bs]
+ *              == desc->total_q_tokens.
+ *  kv_indptr   int32[bs+1], non-decreasing, kv_indptr[bs] - kv_indptr[0] ==
+ *              desc->num_prefix_indices.
+ *  kv_indices  int64[num_prefix_indices], each in [0, pool_slots).
+ *  sm_scale, logit_cap: host floats (see above).
+ *  desc        host pointer.
+ *  workspace   device buffer of >= extend_attention_workspace_size(desc)
+ *              bytes, 256-byte aligned; contents need no initialisation and
+ *              are scratch after the call.  Calls that overlap in time must
+ *              use different workspaces.
+ *  stream      hipStream_t.
+ * The result does not depend on the order of sequences in the batch or on
+ * which pool slots hold the prefix; it is bitwise reproducible run to run
+ * on the same device.
+ */
+int extend_attention_fwd(const void* q_extend, const void* k_extend, const void* v_extend,
+                         void* o, const void* k_pool, const void* v_pool,
+                         const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int64_t* kv_indices, float sm_scale, float logit_cap,
+                         const pkv_attn_desc_t* desc, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Measurement hook (not needed for results).  pkv_profile_enable(1) clears
+ * the record and makes every later extend_attention_fwd call record a HIP
+ * event pair on its stream around its attention kernel; 0 stops recording.
+ * pkv_profile_read waits for the recorded events and returns the summed
+ * attention-kernel time in milliseconds and the number of calls.  The
+ * record is process-wide and holds at most 4096 calls.
+ */
+int pkv_profile_enable(int on);
+int pkv_profile_read(double* total_ms, int64_t* calls);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

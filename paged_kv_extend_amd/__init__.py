@@ -1,0 +1,222 @@
+"""Python binding of libpkv.so: paged-KV extend attention for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/pkv.h.  PyTorch supplies device
+memory and the current stream.  Importing works without a GPU; calling
+requires the built library (``python -m paged_kv_extend_amd._build``) and
+raises if it is missing -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_workspace_size",
+           "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "LIB_PATH", "PkvError"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_BF16 = 0
+PKV_FP32 = 1
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"pkv error {code}: {msg}")
+        self.code = code
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("dtype", "bs", "num_q_heads", "num_kv_heads", "lq", "lv")] + \
+               [(n, ctypes.c_int64) for n in (
+                   "total_q_tokens", "num_prefix_indices", "pool_slots",
+                   "q_stride_tok", "q_stride_head", "o_stride_tok", "o_stride_head",
+                   "ke_stride_tok", "ke_stride_head", "ve_stride_tok", "ve_stride_head",
+                   "kp_stride_slot", "kp_stride_head", "vp_stride_slot", "vp_stride_head")]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libpkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_extend_amd._build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.build_unified_kv_indices.argtypes = [P, P, P, P, P, i32, i64, i64, P, P, i64, P, P]
+    lib.build_unified_kv_indices.restype = ctypes.c_int
+    lib.extend_attention_workspace_size.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.extend_attention_workspace_size.restype = ctypes.c_size_t
+    lib.extend_attention_fwd.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
+                                         ctypes.POINTER(AttnDesc), P, ctypes.c_size_t, P]
+    lib.extend_attention_fwd.restype = ctypes.c_int
+    lib.pkv_profile_enable.argtypes = [ctypes.c_int]
+    lib.pkv_profile_enable.restype = ctypes.c_int
+    lib.pkv_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.pkv_profile_read.restype = ctypes.c_int
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def profile_enable(on: bool = True) -> None:
+    """Record HIP events around every later attention kernel (measurement only)."""
+    _check(library().pkv_profile_enable(1 if on else 0))
+
+
+def profile_read() -> Tuple[float, int]:
+    """(summed attention-kernel milliseconds, number of calls) since profile_enable(True)."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(library().pkv_profile_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def last_error() -> str:
+    return library().pkv_last_error().decode()
+
+
+def version() -> str:
+    return library().pkv_version().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise PkvError(rc, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _want(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def build_unified_kv_indices(prefix_kv_indptr: torch.Tensor, prefix_kv_indices: torch.Tensor,
+                             extend_start_loc: torch.Tensor, extend_seq_lens: torch.Tensor,
+                             extend_kv_indices: torch.Tensor, bs: int,
+                             out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Unified KV indices: (unified_kv_indptr int32[bs+1], unified_kv_indices int64[n_p+n_e],
+    prefix_lens int32[bs]).  Entries of unified_kv_indices past unified_kv_indptr[bs] are
+    left unwritten (as torch.empty leaves them)."""
+    for t, n, d in ((prefix_kv_indptr, "prefix_kv_indptr", torch.int32),
+                    (prefix_kv_indices, "prefix_kv_indices", torch.int64),
+                    (extend_start_loc, "extend_start_loc", torch.int32),
+                    (extend_seq_lens, "extend_seq_lens", torch.int32),
+                    (extend_kv_indices, "extend_kv_indices", torch.int64)):
+        _want(t, n, d)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    dev = prefix_kv_indptr.device
+    cap = prefix_kv_indices.numel() + extend_kv_indices.numel()
+    if out is None:
+        indptr = torch.empty(bs + 1, dtype=torch.int32, device=dev)
+        indices = torch.empty(cap, dtype=torch.int64, device=dev)
+        plens = torch.empty(bs, dtype=torch.int32, device=dev)
+    else:
+        indptr, indices, plens = out
+    rc = library().build_unified_kv_indices(
+        _ptr(prefix_kv_indptr), _ptr(prefix_kv_indices), _ptr(extend_start_loc), _ptr(extend_seq_lens),
+        _ptr(extend_kv_indices), int(bs), prefix_kv_indices.numel(), extend_kv_indices.numel(),
+        _ptr(indptr), _ptr(indices), indices.numel(), _ptr(plens) if plens is not None else None,
+        _stream(dev))
+    _check(rc)
+    return indptr, indices, plens
+
+
+def make_desc(q_extend, k_extend, v_extend, o, k_pool, v_pool, bs: int,
+              num_prefix_indices: int) -> AttnDesc:
+    if q_extend.dtype == torch.bfloat16:
+        dt = PKV_BF16
+    elif q_extend.dtype == torch.float32:
+        dt = PKV_FP32
+    else:
+        raise ValueError(f"unsupported dtype {q_extend.dtype}")
+    for t, n in ((q_extend, "q_extend"), (k_extend, "k_extend"), (v_extend, "v_extend"), (o, "o"),
+                 (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _want(t, n, q_extend.dtype)
+        if t.dim() != 3 or (t.numel() > 0 and t.stride(2) != 1):
+            raise ValueError(f"{n} must be 3-D with a contiguous last dimension")
+    def st(t):  # strides of an empty tensor carry no meaning; report contiguous ones
+        return (t.stride(0), t.stride(1)) if t.numel() > 0 else (t.shape[1] * t.shape[2], t.shape[2])
+
+    d = AttnDesc()
+    d.dtype = dt
+    d.bs = bs
+    d.num_q_heads, d.lq = q_extend.shape[1], q_extend.shape[2]
+    d.num_kv_heads, d.lv = k_pool.shape[1], v_pool.shape[2]
+    d.total_q_tokens = q_extend.shape[0]
+    d.num_prefix_indices = num_prefix_indices
+    d.pool_slots = k_pool.shape[0]
+    d.q_stride_tok, d.q_stride_head = st(q_extend)
+    d.o_stride_tok, d.o_stride_head = st(o)
+    d.ke_stride_tok, d.ke_stride_head = st(k_extend)
+    d.ve_stride_tok, d.ve_stride_head = st(v_extend)
+    d.kp_stride_slot, d.kp_stride_head = st(k_pool)
+    d.vp_stride_slot, d.vp_stride_head = st(v_pool)
+    return d
+
+
+def extend_attention_workspace_size(desc: AttnDesc) -> int:
+    n = library().extend_attention_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        raise PkvError(-1, last_error())
+    return int(n)
+
+
+_ws_cache = {}
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def extend_attention_fwd(q_extend: torch.Tensor, k_extend: torch.Tensor, v_extend: torch.Tensor,
+                         o: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                         qo_indptr: torch.Tensor, kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
+                         sm_scale: Optional[float] = None, logit_cap: float = 0.0,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Extend attention into ``o`` (see include/pkv.h for the exact semantics).
+
+    kv_indptr / kv_indices describe the cached prefix only; the new tokens'
+    K/V rows are addressed by qo_indptr.  sm_scale None or 0 means 1/sqrt(lq).
+    """
+    _want(qo_indptr, "qo_indptr", torch.int32)
+    _want(kv_indptr, "kv_indptr", torch.int32)
+    _want(kv_indices, "kv_indices", torch.int64)
+    bs = qo_indptr.numel() - 1
+    desc = make_desc(q_extend, k_extend, v_extend, o, k_pool, v_pool, bs, kv_indices.numel())
+    dev = q_extend.device
+    stream = _stream(dev)
+    nbytes = extend_attention_workspace_size(desc)
+    if workspace is None:
+        workspace = _workspace(dev, stream, nbytes)
+    rc = library().extend_attention_fwd(
+        _ptr(q_extend), _ptr(k_extend), _ptr(v_extend), _ptr(o), _ptr(k_pool), _ptr(v_pool),
+        _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+        float(sm_scale or 0.0), float(logit_cap), ctypes.byref(desc),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    _check(rc)
+    return o

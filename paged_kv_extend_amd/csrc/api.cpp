@@ -1,0 +1,319 @@
+// C ABI of libpkv.so: host-side argument checks, workspace sizing and the
+// stream-ordered launch sequence (plan -> attention -> merge).  Checks use
+// only host-visible sizes, so no call reads device memory or waits for the
+// device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return PKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int kMinChunkTiles = 8;           // never split an item below this many KV tiles
+constexpr size_t kPartialBytes = 64u << 20;  // budget for split partial states
+
+// Resident attention workgroups on the current device, cached per (device, variant).
+int resident_slots(int dtype, int lq, int lv) {
+  static std::mutex mu;
+  static std::unordered_map<long long, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const long long key = ((long long)dev << 32) | ((long long)dtype << 24) | ((long long)lq << 12) | lv;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int slots = cus * pkv::attention_blocks_per_cu(dtype, lq, lv);
+  cache[key] = slots;
+  return slots;
+}
+
+// Sizes derived from the descriptor; returns 0 and sets the error when invalid.
+int check_desc(const pkv_attn_desc_t* d, pkv::Tiling* t) {
+  if (!d) return fail(PKV_ERR_INVALID, "desc is NULL");
+  if (d->dtype != PKV_BF16 && d->dtype != PKV_FP32)
+    return fail(PKV_ERR_UNSUPPORTED, "dtype %d is not PKV_BF16 or PKV_FP32", d->dtype);
+  if (d->bs < 0) return fail(PKV_ERR_INVALID, "bs %d < 0", d->bs);
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID, "head counts must be positive (%d, %d)", d->num_q_heads, d->num_kv_heads);
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
+                d->num_kv_heads);
+  if (!pkv::attn_tiling(d->dtype, d->lq, d->lv, t))
+    return fail(PKV_ERR_UNSUPPORTED, "head dims (lq %d, lv %d) not supported for dtype %d", d->lq, d->lv,
+                d->dtype);
+  if (d->total_q_tokens < 0 || d->num_prefix_indices < 0 || d->pool_slots < 0)
+    return fail(PKV_ERR_INVALID, "negative size (total_q_tokens %lld, num_prefix_indices %lld, pool_slots %lld)",
+                (long long)d->total_q_tokens, (long long)d->num_prefix_indices, (long long)d->pool_slots);
+  const int group = d->num_q_heads / d->num_kv_heads;
+  if (d->total_q_tokens * (int64_t)group >= (1ll << 31) || d->num_prefix_indices >= (1ll << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "batch too large for 32-bit row indexing");
+  if (d->num_prefix_indices > 0 && d->pool_slots <= 0)
+    return fail(PKV_ERR_INVALID, "prefix indices given but pool_slots is %lld", (long long)d->pool_slots);
+  const int64_t vec = d->dtype == PKV_BF16 ? 8 : 4;
+  const int64_t strides[] = {d->q_stride_tok,   d->q_stride_head,  d->o_stride_tok,    d->o_stride_head,
+                             d->ke_stride_tok,  d->ke_stride_head, d->ve_stride_tok,   d->ve_stride_head,
+                             d->kp_stride_slot, d->kp_stride_head, d->vp_stride_slot,  d->vp_stride_head};
+  for (int64_t s : strides)
+    if (s < 0 || s % vec != 0)
+      return fail(PKV_ERR_UNSUPPORTED, "strides must be non-negative multiples of %lld elements", (long long)vec);
+  return PKV_OK;
+}
+
+pkv::PlanBounds plan_bounds(const pkv_attn_desc_t* d, const pkv::Tiling& t) {
+  pkv::PlanBounds pb;
+  const int64_t group = d->num_q_heads / d->num_kv_heads;
+  // sum_b ceil(E_b G / BM) <= T G / BM + bs
+  pb.max_items = (int64_t)d->num_kv_heads * (d->total_q_tokens * group / t.bm + d->bs + 1);
+  int64_t budget = (int64_t)(kPartialBytes / ((size_t)t.bm * (d->lv + 2) * sizeof(float)));
+  if (budget > 4096) budget = 4096;
+  if (budget < 16) budget = 16;
+  pb.part_budget = budget;
+  pb.max_merge = budget / 2;
+  pb.max_work = pb.max_items + budget;
+  return pb;
+}
+
+pkv::WsLayout ws_layout(const pkv_attn_desc_t* d, const pkv::Tiling& t, const pkv::PlanBounds& pb) {
+  pkv::WsLayout l;
+  size_t off = 0;
+  l.header = off;
+  off = align_up(off + sizeof(pkv::PlanHeader), 256);
+  l.work = off;
+  off = align_up(off + sizeof(pkv::WorkItem) * (size_t)pb.max_work, 256);
+  l.merge = off;
+  off = align_up(off + sizeof(pkv::MergeItem) * (size_t)(pb.max_merge > 0 ? pb.max_merge : 1), 256);
+  l.scratch = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)(d->bs + 1 + 7 * pb.max_items), 256);
+  l.part_ml = off;
+  off = align_up(off + sizeof(float) * 2 * (size_t)pb.part_budget * t.bm, 256);
+  l.part_acc = off;
+  off = align_up(off + sizeof(float) * (size_t)pb.part_budget * t.bm * d->lv, 256);
+  l.total = off;
+  return l;
+}
+
+// Event pairs around attention launches while profiling is enabled.
+struct Profile {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs;
+  size_t used = 0;
+};
+Profile& profile() {
+  static Profile p;
+  return p;
+}
+constexpr size_t kMaxProfiled = 4096;
+
+// Returns the event pair to record around this call's attention kernel, or nulls.
+std::pair<hipEvent_t, hipEvent_t> profile_slot() {
+  Profile& p = profile();
+  std::lock_guard<std::mutex> lk(p.mu);
+  if (!p.on || p.used >= kMaxProfiled) return {nullptr, nullptr};
+  if (p.used == p.pairs.size()) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess) return {nullptr, nullptr};
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return {nullptr, nullptr};
+    }
+    p.pairs.push_back({a, b});
+  }
+  return p.pairs[p.used++];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_profile_enable(int on) {
+  Profile& p = profile();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.on = on != 0;
+  if (p.on) p.used = 0;
+  return ok();
+}
+
+int pkv_profile_read(double* total_ms, int64_t* calls) {
+  if (!total_ms || !calls) return fail(PKV_ERR_INVALID, "NULL output");
+  Profile& p = profile();
+  std::lock_guard<std::mutex> lk(p.mu);
+  double t = 0.0;
+  for (size_t i = 0; i < p.used; ++i) {
+    if (hipEventSynchronize(p.pairs[i].second) != hipSuccess)
+      return fail(PKV_ERR_HIP, "event synchronize failed");
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, p.pairs[i].first, p.pairs[i].second) != hipSuccess)
+      return fail(PKV_ERR_HIP, "event elapsed time failed");
+    t += ms;
+  }
+  *total_ms = t;
+  *calls = (int64_t)p.used;
+  return ok();
+}
+
+const char* pkv_last_error(void) { return g_err; }
+
+const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+
+int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
+                             const int32_t* extend_start_loc, const int32_t* extend_seq_lens,
+                             const int64_t* extend_kv_indices, int32_t bs, int64_t num_prefix_indices,
+                             int64_t num_extend_indices, int32_t* unified_kv_indptr,
+                             int64_t* unified_kv_indices, int64_t capacity, int32_t* prefix_lens,
+                             void* stream) {
+  if (bs < 0) return fail(PKV_ERR_INVALID, "bs %d < 0", bs);
+  if (num_prefix_indices < 0 || num_extend_indices < 0 || capacity < 0)
+    return fail(PKV_ERR_INVALID, "negative length");
+  if (!unified_kv_indptr) return fail(PKV_ERR_INVALID, "unified_kv_indptr is NULL");
+  if (bs > 0 && (!prefix_kv_indptr || !extend_start_loc || !extend_seq_lens))
+    return fail(PKV_ERR_INVALID, "an input indptr/length array is NULL");
+  if ((num_prefix_indices > 0 && !prefix_kv_indices) || (num_extend_indices > 0 && !extend_kv_indices))
+    return fail(PKV_ERR_INVALID, "an input index array is NULL");
+  if (num_prefix_indices + num_extend_indices >= (1ll << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "more than 2^31 - 1 indices");
+  if (capacity < num_prefix_indices + num_extend_indices)
+    return fail(PKV_ERR_CAPACITY, "capacity %lld < %lld prefix + %lld extend indices", (long long)capacity,
+                (long long)num_prefix_indices, (long long)num_extend_indices);
+  if (capacity > 0 && !unified_kv_indices) return fail(PKV_ERR_INVALID, "unified_kv_indices is NULL");
+  hipError_t e = pkv::launch_index_build(prefix_kv_indptr, prefix_kv_indices, extend_start_loc, extend_seq_lens,
+                                         extend_kv_indices, bs, unified_kv_indptr, unified_kv_indices,
+                                         prefix_lens, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "index build launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t extend_attention_workspace_size(const pkv_attn_desc_t* desc) {
+  pkv::Tiling t;
+  if (check_desc(desc, &t) != PKV_OK) return 0;
+  g_err[0] = '\0';
+  return ws_layout(desc, t, plan_bounds(desc, t)).total;
+}
+
+int extend_attention_fwd(const void* q_extend, const void* k_extend, const void* v_extend, void* o,
+                         const void* k_pool, const void* v_pool, const int32_t* qo_indptr,
+                         const int32_t* kv_indptr, const int64_t* kv_indices, float sm_scale,
+                         float logit_cap, const pkv_attn_desc_t* desc, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  pkv::Tiling t;
+  int rc = check_desc(desc, &t);
+  if (rc != PKV_OK) return rc;
+  const pkv_attn_desc_t& d = *desc;
+  if (!std::isfinite(sm_scale) || std::isnan(logit_cap))
+    return fail(PKV_ERR_INVALID, "sm_scale must be finite and logit_cap not NaN");
+  if (d.bs == 0 || d.total_q_tokens == 0) return ok();  // no query rows: nothing to write
+  if (!qo_indptr || !kv_indptr) return fail(PKV_ERR_INVALID, "qo_indptr / kv_indptr is NULL");
+  if (!q_extend || !k_extend || !v_extend || !o)
+    return fail(PKV_ERR_INVALID, "q_extend / k_extend / v_extend / o is NULL");
+  if (d.num_prefix_indices > 0 && (!kv_indices || !k_pool || !v_pool))
+    return fail(PKV_ERR_INVALID, "kv_indices / k_pool / v_pool is NULL with a non-empty prefix");
+  const void* ptrs[] = {q_extend, k_extend, v_extend, o, k_pool, v_pool};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(PKV_ERR_UNSUPPORTED, "tensor base pointers must be 16-byte aligned");
+
+  const pkv::PlanBounds pb = plan_bounds(&d, t);
+  const pkv::WsLayout wl = ws_layout(&d, t, pb);
+  if (!workspace || workspace_bytes < wl.total)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                wl.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int group = d.num_q_heads / d.num_kv_heads;
+
+  pkv::PlanArgs pa;
+  pa.qo_indptr = qo_indptr;
+  pa.kv_indptr = kv_indptr;
+  pa.bs = d.bs;
+  pa.num_kv_heads = d.num_kv_heads;
+  pa.group = group;
+  pa.bm = t.bm;
+  pa.bn = t.bn;
+  pa.slots = resident_slots(d.dtype, d.lq, d.lv);
+  pa.min_chunk = kMinChunkTiles;
+  pa.max_items = pb.max_items;
+  pa.part_budget = pb.part_budget;
+  pa.max_merge = pb.max_merge;
+  pa.hdr = reinterpret_cast<pkv::PlanHeader*>(ws + wl.header);
+  pa.work = reinterpret_cast<pkv::WorkItem*>(ws + wl.work);
+  pa.merge = reinterpret_cast<pkv::MergeItem*>(ws + wl.merge);
+  pa.scratch = reinterpret_cast<int32_t*>(ws + wl.scratch);
+  hipError_t e = pkv::launch_plan(pa, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+
+  const double scale = sm_scale != 0.0f ? (double)sm_scale : 1.0 / sqrt((double)d.lq);
+  const double log2e = 1.4426950408889634;
+  pkv::AttnArgs a;
+  a.q = q_extend;
+  a.k_ext = k_extend;
+  a.v_ext = v_extend;
+  a.o = o;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.qo_indptr = qo_indptr;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.q_st = d.q_stride_tok;
+  a.q_sh = d.q_stride_head;
+  a.o_st = d.o_stride_tok;
+  a.o_sh = d.o_stride_head;
+  a.ke_st = d.ke_stride_tok;
+  a.ke_sh = d.ke_stride_head;
+  a.ve_st = d.ve_stride_tok;
+  a.ve_sh = d.ve_stride_head;
+  a.kp_ss = d.kp_stride_slot;
+  a.kp_sh = d.kp_stride_head;
+  a.vp_ss = d.vp_stride_slot;
+  a.vp_sh = d.vp_stride_head;
+  a.group = group;
+  a.use_cap = logit_cap > 0.0f ? 1 : 0;
+  a.scale_log2 = (float)(scale * log2e);
+  a.cap_in = logit_cap > 0.0f ? (float)(scale / logit_cap) : 0.0f;
+  a.cap_out = logit_cap > 0.0f ? (float)(logit_cap * log2e) : 0.0f;
+  a.hdr = pa.hdr;
+  a.work = pa.work;
+  a.merge = pa.merge;
+  a.part_acc = reinterpret_cast<float*>(ws + wl.part_acc);
+  a.part_ml = reinterpret_cast<float*>(ws + wl.part_ml);
+  const auto ev = profile_slot();
+  if (ev.first) (void)hipEventRecord(ev.first, s);
+  e = pkv::launch_attention(d.dtype, d.lq, d.lv, a, pb.max_work, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  if (ev.second) (void)hipEventRecord(ev.second, s);
+  e = pkv::launch_merge(d.dtype, d.lv, a, t.bm, pb.max_merge, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal declarations shared by the library's translation units.
+// Nothing here is part of the public ABI (include/pkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// One unit of attention work: packed query rows [t*BM, (t+1)*BM) of sequence
+// b and KV head g, over KV tiles [kt_begin, kt_end) of the concatenated
+// (prefix, new tokens) key sequence.  Packed row r is new token r / G, query
+// head g*G + r % G (token-major, so one KV tile serves all G heads of a token).
+// part < 0: the item covers all KV tiles and writes o directly; otherwise it is
+// one chunk of a split item and writes unnormalised partial state into
+// partial slot `part`.
+struct WorkItem {
+  int32_t b, g, t, kt_begin, kt_end, part, pad0, pad1;
+};
+
+// A split item whose chunks occupy partial slots [part_base, part_base + n).
+struct MergeItem {
+  int32_t b, g, t, part_base, n, pad0, pad1, pad2;
+};
+
+// Planner output header at the start of the workspace.
+struct PlanHeader {
+  int32_t num_work;
+  int32_t num_merge;
+  int32_t chunk_tiles;  // split threshold the planner settled on
+  int32_t total_tiles;  // KV tiles over all items before splitting
+  int32_t num_items;    // items before splitting
+  int32_t pad[59];
+};
+
+// Static tiling of one kernel instantiation.
+struct Tiling {
+  int bm;       // packed query rows per workgroup
+  int bn;       // keys per KV tile
+  int threads;  // workgroup size
+};
+
+// Upper bounds that size the workspace (functions of host-visible sizes only).
+struct PlanBounds {
+  int64_t max_items;    // items before splitting
+  int64_t max_work;     // items after splitting
+  int64_t part_budget;  // partial slots available for split chunks
+  int64_t max_merge;    // split items
+};
+
+// Workspace carve-up.
+struct WsLayout {
+  size_t header, work, merge, scratch, part_ml, part_acc, total;
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k_ext;
+  const void* v_ext;
+  void* o;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  const int64_t* kv_indices;
+  int64_t q_st, q_sh, o_st, o_sh, ke_st, ke_sh, ve_st, ve_sh, kp_ss, kp_sh, vp_ss, vp_sh;
+  int32_t group;     // query heads per KV head
+  int32_t use_cap;   // soft-cap enabled
+  float scale_log2;  // scale * log2(e): logits are kept in base-2 units
+  float cap_in;      // scale / cap
+  float cap_out;     // cap * log2(e)
+  const PlanHeader* hdr;
+  const WorkItem* work;
+  const MergeItem* merge;
+  float* part_acc;   // [part][bm][lv]
+  float* part_ml;    // [part][bm][2]: running max (base-2 units), sum of weights
+};
+
+struct PlanArgs {
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  int32_t bs, num_kv_heads, group, bm, bn;
+  int32_t slots;          // workgroups resident at once on the device
+  int32_t min_chunk;      // never split below this many KV tiles
+  int64_t max_items, part_budget, max_merge;
+  PlanHeader* hdr;
+  WorkItem* work;    // [max_work]
+  MergeItem* merge;  // [max_merge]
+  int32_t* scratch;  // [bs + 1 + 7 * max_items]
+};
+
+// Kernel variants: (dtype, lq, lv).  Returns false when unsupported.
+bool attn_tiling(int dtype, int lq, int lv, Tiling* t);
+hipError_t launch_attention(int dtype, int lq, int lv, const AttnArgs& a, int64_t grid,
+                            hipStream_t s);
+hipError_t launch_merge(int dtype, int lv, const AttnArgs& a, int bm, int64_t grid, hipStream_t s);
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_index_build(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
+                              const int32_t* extend_start_loc, const int32_t* extend_seq_lens,
+                              const int64_t* extend_kv_indices, int32_t bs,
+                              int32_t* unified_kv_indptr, int64_t* unified_kv_indices,
+                              int32_t* prefix_lens, hipStream_t s);
+// Workgroups of the attention kernel resident per CU (from the occupancy API).
+int attention_blocks_per_cu(int dtype, int lq, int lv);
+
+}  // namespace pkv

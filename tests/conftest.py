@@ -25,3 +25,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionstart(session):
+    # the HIP library is loaded from the tree; build it only when it is missing
+    lib = os.path.join(ROOT, "paged_kv_extend_amd", "libpkv.so")
+    if not os.path.exists(lib):
+        from paged_kv_extend_amd import _build
+        _build.build()

@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/pkv.h declares, sizes workspaces, and rejects bad
+arguments before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_extend_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert {"build_unified_kv_indices", "extend_attention_fwd", "extend_attention_workspace_size",
+            "pkv_last_error", "pkv_version"} <= set(names)
+    lib = pkv.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in pkv.version()
+
+
+def desc(**kw):
+    d = pkv.AttnDesc()
+    base = dict(dtype=0, bs=2, num_q_heads=32, num_kv_heads=8, lq=128, lv=128, total_q_tokens=100,
+                num_prefix_indices=50, pool_slots=1000, q_stride_tok=32 * 128, q_stride_head=128,
+                o_stride_tok=32 * 128, o_stride_head=128, ke_stride_tok=8 * 128, ke_stride_head=128,
+                ve_stride_tok=8 * 128, ve_stride_head=128, kp_stride_slot=8 * 128, kp_stride_head=128,
+                vp_stride_slot=8 * 128, vp_stride_head=128)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_workspace_size_valid_and_grows():
+    small = pkv.extend_attention_workspace_size(desc())
+    big = pkv.extend_attention_workspace_size(desc(total_q_tokens=100000, bs=64))
+    assert 0 < small < big
+    assert small % 256 == 0
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(num_q_heads=30), "multiple"),
+    (dict(lq=96, lv=96), "not supported"),
+    (dict(dtype=5), "dtype"),
+    (dict(bs=-1), "bs"),
+    (dict(q_stride_head=100), "stride"),
+    (dict(total_q_tokens=-3), "negative"),
+    (dict(dtype=1, lq=576, lv=512), "not supported"),
+])
+def test_workspace_size_rejects(kw, needle):
+    lib = pkv.library()
+    assert lib.extend_attention_workspace_size(ctypes.byref(desc(**kw))) == 0
+    assert needle in pkv.last_error()
+
+
+def call_fwd(d, ws_bytes=1 << 30, ptr=4096, ws=4096):
+    lib = pkv.library()
+    return lib.extend_attention_fwd(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 0.0, 0.0,
+                                    ctypes.byref(d) if d is not None else None, ws, ws_bytes, None)
+
+
+def test_fwd_argument_errors_without_device():
+    assert call_fwd(None) == pkv.PkvError(-1, "").code == -1
+    assert call_fwd(desc(lq=80, lv=80)) == -2
+    assert call_fwd(desc(num_kv_heads=7)) == -1
+    assert call_fwd(desc(), ws_bytes=16) == -3
+    assert "workspace" in pkv.last_error()
+    assert call_fwd(desc(), ptr=4100) == -2  # misaligned base pointer
+    assert call_fwd(desc(), ws=4096 + 16) == -3  # misaligned workspace
+    assert call_fwd(desc(bs=0)) == 0  # nothing to do
+    assert call_fwd(desc(total_q_tokens=0)) == 0
+    lib = pkv.library()
+    assert lib.extend_attention_fwd(4096, 4096, 4096, None, 4096, 4096, 4096, 4096, 4096, 0.0, 0.0,
+                                    ctypes.byref(desc()), 4096, 1 << 30, None) == -1
+    assert lib.extend_attention_fwd(4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096,
+                                    float("nan"), 0.0, ctypes.byref(desc()), 4096, 1 << 30, None) == -1
+
+
+def test_index_build_argument_errors_without_device():
+    lib = pkv.library()
+    p = 4096
+    assert lib.build_unified_kv_indices(p, p, p, p, p, 3, 10, 5, p, p, 14, p, None) == -4
+    assert "capacity" in pkv.last_error()
+    assert lib.build_unified_kv_indices(p, p, p, p, p, -1, 10, 5, p, p, 15, p, None) == -1
+    assert lib.build_unified_kv_indices(p, p, p, p, p, 3, 10, 5, None, p, 15, p, None) == -1
+    assert lib.build_unified_kv_indices(p, None, p, p, p, 3, 10, 5, p, p, 15, p, None) == -1

@@ -1,0 +1,127 @@
+"""Extend attention on the GPU against the CPU oracle.
+
+Full element-by-element comparison at sizes the oracle finishes in seconds
+(several tiles and ragged tails), sampled rows at the five workloads' full
+sizes in the launch configuration the benchmark uses, edge cases, and
+bitwise invariants (determinism, pool-slot permutation, batch order).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_extend_amd as pkv
+import workloads as wl
+from gpu_helpers import check, out_f64, run_gpu, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def parity_full(w, what):
+    say(f"parity {what}: bs={w.bs} T={w.total_q} P={w.num_prefix} dims={w.cfg.lq}/{w.cfg.lv} "
+        f"heads={w.cfg.hq}/{w.cfg.hkv} cap={w.logit_cap}")
+    dev = run_gpu(w)
+    want = oracle.extend_attention_workload(w)
+    check(out_f64(dev), want, w.cfg.dtype, what)
+    return dev
+
+
+# ---- reduced sizes, every output compared
+
+SMALL = {
+    "tiny_fp32": dict(),  # the tiny workload itself
+    "llama8b": dict(prefix_lens=[0, 300, 77, 1000, 5], extend_lens=[200, 1, 64, 33, 129]),
+    "long_prefix": dict(prefix_lens=[3000, 1500], extend_lens=[70, 19]),
+    "mla": dict(prefix_lens=[600, 1], extend_lens=[3, 20]),
+    "skewed_cap": dict(prefix_lens=[0, 900, 13, 2], extend_lens=[300, 5, 64, 1]),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_reduced(name):
+    w = wl.build(wl.CONFIGS[name], **{k: np.array(v) for k, v in SMALL[name].items()})
+    parity_full(w, f"{name}-reduced")
+
+
+EDGE = [
+    dict(name="e1-decode", dtype="bf16", prefix_lens=[500, 0, 31], extend_lens=[1, 1, 1], hq=8, hkv=2, lq=128, lv=128),
+    dict(name="p0-causal", dtype="bf16", prefix_lens=[0, 0], extend_lens=[257, 64], hq=4, hkv=4, lq=128, lv=128),
+    dict(name="empty-seq", dtype="bf16", prefix_lens=[10, 40, 0, 7], extend_lens=[5, 0, 0, 9], hq=4, hkv=1, lq=64, lv=64),
+    dict(name="cap1-d256", dtype="bf16", prefix_lens=[150, 3], extend_lens=[40, 70], hq=4, hkv=2, lq=256, lv=256, logit_cap=1.0),
+    dict(name="192x128", dtype="bf16", prefix_lens=[100, 33], extend_lens=[50, 7], hq=6, hkv=2, lq=192, lv=128),
+    dict(name="288x256", dtype="bf16", prefix_lens=[65, 0], extend_lens=[30, 41], hq=4, hkv=1, lq=288, lv=256),
+    dict(name="mqa-64", dtype="bf16", prefix_lens=[129, 64, 1], extend_lens=[63, 65, 128], hq=16, hkv=1, lq=64, lv=64),
+    dict(name="group7", dtype="bf16", prefix_lens=[200, 17], extend_lens=[37, 100], hq=28, hkv=4, lq=128, lv=128),
+    dict(name="fp32-128", dtype="fp32", prefix_lens=[40, 0, 100], extend_lens=[9, 50, 1], hq=4, hkv=2, lq=128, lv=128, sm_scale=0.05),
+    dict(name="neg-scale", dtype="bf16", prefix_lens=[20], extend_lens=[20], hq=2, hkv=1, lq=64, lv=64, sm_scale=-0.1),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c["name"] for c in EDGE])
+def test_parity_edge(case):
+    case = dict(case)
+    name = case.pop("name")
+    parity_full(wl.custom(**case), name)
+
+
+def test_long_prefix_single_sequence():
+    w = wl.custom(dtype="bf16", prefix_lens=[65536], extend_lens=[3], hq=8, hkv=1, lq=128, lv=128)
+    parity_full(w, "bs1-P65536")
+
+
+def test_empty_batch_is_noop():
+    w = wl.custom(dtype="bf16", prefix_lens=[5, 0], extend_lens=[0, 0], hq=4, hkv=2, lq=64, lv=64)
+    dev = wl.to_torch(w)
+    pkv.extend_attention_fwd(dev["q"], dev["k_ext"], dev["v_ext"], dev["o"], dev["k_pool"], dev["v_pool"],
+                             dev["qo_indptr"], dev["kv_indptr"], dev["kv_indices"])
+    torch.cuda.synchronize()
+    assert dev["o"].numel() == 0
+
+
+# ---- full sizes, sampled rows, same launch path as the benchmark
+
+@pytest.mark.parametrize("name", wl.CONFIG_ORDER)
+def test_parity_full_size_sampled(name):
+    w = wl.get(name)
+    rows = sample_rows(w)
+    say(f"full-size {name}: T={w.total_q} P={w.num_prefix}, {len(rows)} sampled rows")
+    dev = run_gpu(w)
+    got = dev["o"].float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite outputs"
+    check(got[rows], oracle.extend_attention_workload(w, rows=rows), w.cfg.dtype, f"{name}-sampled")
+
+
+# ---- bitwise invariants
+
+def test_deterministic_and_slot_permutation_invariant():
+    w = wl.build(wl.CONFIGS["llama8b"], prefix_lens=np.array([700, 5, 1200]), extend_lens=np.array([100, 300, 17]))
+    a = out_f64(run_gpu(w)).copy()
+    b = out_f64(run_gpu(w))
+    assert np.array_equal(a, b), "run-to-run results differ"
+    perm = np.random.default_rng(1).permutation(w.cfg.pool_slots)
+    k2 = np.empty_like(w.k_pool)
+    v2 = np.empty_like(w.v_pool)
+    k2[perm] = w.k_pool
+    v2[perm] = w.v_pool
+    w.k_pool, w.v_pool, w.kv_indices = k2, v2, perm[w.kv_indices]
+    c = out_f64(run_gpu(w))
+    assert np.array_equal(a, c), "pool-slot permutation changed the result"
+
+
+def test_batch_order_invariant():
+    w = wl.build(wl.CONFIGS["skewed_cap"], prefix_lens=np.array([0, 900, 13, 2, 40]),
+                 extend_lens=np.array([300, 5, 64, 1, 8]))
+    base = out_f64(run_gpu(w))
+    order = [3, 1, 4, 0, 2]
+    rows = np.concatenate([np.arange(w.qo_indptr[b], w.qo_indptr[b + 1]) for b in order])
+    e = w.extend_lens[order]
+    p = w.prefix_lens[order]
+    w2 = wl.Workload(w.cfg, p, e, np.concatenate([[0], np.cumsum(e)]).astype(np.int32),
+                     np.concatenate([[0], np.cumsum(p)]).astype(np.int32),
+                     np.concatenate([w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]] for b in order]),
+                     w.extend_kv_indices[rows], np.concatenate([[0], np.cumsum(e)[:-1]]).astype(np.int32),
+                     np.ascontiguousarray(w.q[rows]), np.ascontiguousarray(w.k_ext[rows]),
+                     np.ascontiguousarray(w.v_ext[rows]), w.k_pool, w.v_pool)
+    got = out_f64(run_gpu(w2))
+    assert np.array_equal(got, base[rows])

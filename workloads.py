@@ -289,3 +289,35 @@ def index_case(rng: np.random.Generator, bs: int, max_p: int = 300, max_e: int =
     return dict(prefix_kv_indptr=prefix_kv_indptr, prefix_kv_indices=prefix_kv_indices,
                 extend_start_loc=extend_start_loc, extend_seq_lens=extend_seq_lens,
                 extend_kv_indices=extend_kv_indices, bs=bs)
+
+
+def to_torch(w: Workload, device="cuda"):
+    """Device tensors of a workload (bf16 bit patterns become torch.bfloat16)."""
+    import torch
+
+    def t(x):
+        a = torch.from_numpy(np.ascontiguousarray(x))
+        if w.cfg.dtype == "bf16":
+            a = a.view(torch.bfloat16)
+        return a.to(device)
+
+    def i(x, dt):
+        return torch.from_numpy(np.ascontiguousarray(x).astype(dt)).to(device)
+
+    c = w.cfg
+    out = dict(q=t(w.q), k_ext=t(w.k_ext), k_pool=t(w.k_pool))
+    if c.v_aliases_k:
+        out["v_ext"] = out["k_ext"][..., :c.lv]
+        out["v_pool"] = out["k_pool"][..., :c.lv]
+    else:
+        out["v_ext"] = t(w.v_ext)
+        out["v_pool"] = t(w.v_pool)
+    out["qo_indptr"] = i(w.qo_indptr, np.int32)
+    out["kv_indptr"] = i(w.kv_indptr, np.int32)
+    out["kv_indices"] = i(w.kv_indices, np.int64)
+    out["extend_kv_indices"] = i(w.extend_kv_indices, np.int64)
+    out["extend_start_loc"] = i(w.extend_start_loc, np.int32)
+    out["extend_seq_lens"] = i(w.extend_lens, np.int32)
+    tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    out["o"] = torch.full((w.total_q, c.hq, c.lv), float("nan"), dtype=tdt, device=device)
+    return out
