@@ -107,6 +107,8 @@ pkv::WsLayout ws_layout(const pkv_attn_desc_t* d, const pkv::Tiling& t, const pk
   size_t off = 0;
   l.header = off;
   off = align_up(off + sizeof(pkv::PlanHeader), 256);
+  l.zero_row = off;
+  off = align_up(off + pkv::kZeroRowBytes, 256);
   l.work = off;
   off = align_up(off + sizeof(pkv::WorkItem) * (size_t)pb.max_work, 256);
   l.merge = off;
@@ -266,6 +268,7 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   pa.part_budget = pb.part_budget;
   pa.max_merge = pb.max_merge;
   pa.hdr = reinterpret_cast<pkv::PlanHeader*>(ws + wl.header);
+  pa.zero_row = ws + wl.zero_row;
   pa.work = reinterpret_cast<pkv::WorkItem*>(ws + wl.work);
   pa.merge = reinterpret_cast<pkv::MergeItem*>(ws + wl.merge);
   pa.scratch = reinterpret_cast<int32_t*>(ws + wl.scratch);
@@ -298,9 +301,11 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   a.vp_sh = d.vp_stride_head;
   a.group = group;
   a.use_cap = logit_cap > 0.0f ? 1 : 0;
-  a.scale_log2 = (float)(scale * log2e);
-  a.cap_in = logit_cap > 0.0f ? (float)(scale / logit_cap) : 0.0f;
+  a.neg_q = scale < 0.0 ? 1 : 0;
+  a.scale_log2 = (float)(fabs(scale) * log2e);
+  a.cap_in = logit_cap > 0.0f ? (float)(fabs(scale) / logit_cap) : 0.0f;
   a.cap_out = logit_cap > 0.0f ? (float)(logit_cap * log2e) : 0.0f;
+  a.zero_row = pa.zero_row;
   a.hdr = pa.hdr;
   a.work = pa.work;
   a.merge = pa.merge;

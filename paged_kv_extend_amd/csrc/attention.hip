@@ -12,22 +12,31 @@
 //
 // Design (MI355X):
 //  * One workgroup = 4 waves = 128 packed query rows (token-major packing of
-//    the G query heads that share a KV head), one KV tile of BN keys at a
-//    time staged in LDS and shared by all 128 rows.
+//    the G query heads that share a KV head), one tile of BN keys at a time
+//    staged in LDS and shared by all 128 rows.
+//  * Row gather: for every tile a table of BN row pointers (pool slot, new
+//    token row, or a zero row past the last key the tile's rows can see) is
+//    built in LDS one tile ahead, from index loads issued before the previous
+//    tile's math, so the slot lookups never stall the loads.  K and V rows are
+//    then fetched with 16-byte lane loads, 16 lanes per 256-byte row, into
+//    registers while the current tile is computed, and stored row-major.
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: K is the A operand read from
 //    LDS, Q^T the B operand held in registers.  In the result a lane owns one
 //    query row, so the row max and row sum of the online softmax are per-lane
 //    values plus one exchange between lanes l and l+32 (v_permlane32_swap).
 //  * O^T = V^T . P^T: the probabilities already sit in the B-operand layout
-//    (the MFMA contraction index is permuted consistently on both operands),
-//    V is stored transposed in LDS so each lane reads two 8-byte runs of
-//    keys.  The accumulator rescale by exp2(m_old - m_new) is a per-lane
-//    scalar multiply.
-//  * Keys are processed as one sequence (prefix then new tokens); tiles past
-//    the last visible key of a wave are skipped and only tiles crossing the
-//    causal diagonal pay for the mask.
+//    (the MFMA contraction index is permuted consistently on both operands);
+//    the V^T operand comes from the row-major V tile through gfx950's
+//    transposing LDS read (ds_read_b64_tr_b16), 4 consecutive keys per lane.
+//  * Probabilities are exp2(s * c - m) with the scale folded into one FMA; the
+//    reference max m is only raised (and the accumulator rescaled) when a row
+//    max exceeds it by more than 2^8, so most tiles skip the rescale.
+//  * Tiles past the last visible key of a wave are skipped and only tiles
+//    crossing the causal diagonal pay for the mask.
 //  * fp32 inputs use v_mfma_f32_32x32x2f32 with the same structure (no
 //    rounding of probabilities), so fp32 results carry fp32 products.
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -35,10 +44,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes, kept in registers
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;  // base-2 headroom before the reference max is raised
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -52,17 +63,9 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Logit in base-2 units: scale * s * log2(e), or cap * tanh(scale * s / cap) * log2(e).
-// tanh(y) = 1 - 2 / (e^{2y} + 1) saturates cleanly to +-1 for large |y|.
-template <bool CAP>
-__device__ __forceinline__ float logit2(float s, const AttnArgs& a) {
-  if constexpr (CAP) {
-    float e = fast_exp2(s * a.cap_in * (2.0f * kLog2e));
-    return a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
-  } else {
-    return s * a.scale_log2;
-  }
-}
+// global-memory (address space 1) views: loads through them become global_load
+template <class T>
+using gptr = const __attribute__((address_space(1))) T*;
 
 template <bool F32>
 struct Elem;
@@ -77,35 +80,24 @@ struct Elem<true> {
   static constexpr int kVec = 4;
 };
 
-// Row source for key j of sequence (prefix P, new tokens E): >= 0 pool slot,
-// -1 zero row (past the sequence), <= -2 encodes new-token row (q0 + j - P) as -(row + 2).
-__device__ __forceinline__ int64_t key_source(int j, int P, int E, int q0, int kvs,
-                                              const int64_t* __restrict__ kv_indices) {
-  if (j < P) return kv_indices[kvs + j];
-  if (j < P + E) return -2 - (int64_t)(q0 + j - P);
-  return -1;
-}
-
 template <bool F32, int LQ, int LV, int BN>
 struct Cfg {
-  static constexpr int NW = 4;
-  static constexpr int NT = NW * 64;
-  static constexpr int BM = NW * 32;
+  static constexpr int NT = 256;
+  static constexpr int BM = 128;
   static constexpr int VEC = Elem<F32>::kVec;
-  // LDS pitches in elements.  bf16: K row-major [BN][LQ+8] (16-byte reads,
-  // 8 consecutive rows hit 8 distinct 4-bank groups); V transposed
-  // [LV][BN+4] (8-byte reads, 16 consecutive rows hit distinct bank pairs).
-  // fp32: K [BN][LQ+1], V row-major [BN][LV+1].
+  // LDS pitches in elements.  bf16 K [BN][LQ+8]: 16-byte reads of 8
+  // consecutive rows land on 8 distinct 4-bank groups.  bf16 V [BN][LV+16]:
+  // a transposing read covers 4 rows x 32 bytes; a row pitch of 8 banks (mod
+  // 32) keeps the 4 rows on distinct banks.  fp32: one pad element per row.
   static constexpr int KROW = F32 ? LQ + 1 : LQ + 8;
-  static constexpr int VROW = F32 ? LV + 1 : BN + 4;
+  static constexpr int VROW = F32 ? LV + 1 : LV + 16;
   static constexpr int K_ELEMS = BN * KROW;
-  static constexpr int V_ELEMS = F32 ? BN * VROW : LV * VROW;
-  static constexpr int K_CHUNKS = BN * LQ / VEC;          // 16-byte chunks per K tile
-  static constexpr int K_PER_THREAD = (K_CHUNKS + NT - 1) / NT;
-  // bf16 V: blocks of 4 keys x 8 columns; fp32 V: 16-byte chunks like K
-  static constexpr int V_UNITS = F32 ? BN * LV / VEC : (BN / 4) * (LV / 8);
-  static constexpr int V_PER_THREAD = (V_UNITS + NT - 1) / NT;
-  static_assert(BN % 32 == 0 && LQ % 16 == 0 && LV % 32 == 0, "tile shape");
+  static constexpr int V_ELEMS = BN * VROW;
+  static constexpr int KC = BN * LQ / VEC;  // 16-byte chunks per tile
+  static constexpr int VC = BN * LV / VEC;
+  static constexpr int K_PER_THREAD = (KC + NT - 1) / NT;
+  static constexpr int V_PER_THREAD = (VC + NT - 1) / NT;
+  static_assert(BN % 32 == 0 && BN <= 64 && LQ % 16 == 0 && LV % 32 == 0, "tile shape");
 };
 
 template <bool F32, int LQ, int LV, int BN, bool CAP, int MINB>
@@ -118,6 +110,8 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   constexpr int NDB = LV / 32;  // 32-column blocks of the output
 
   __shared__ __attribute__((aligned(16))) T lds[C::K_ELEMS + C::V_ELEMS];
+  __shared__ gptr<T> kptr[2][BN];
+  __shared__ gptr<T> vptr[2][BN];
   T* __restrict__ Ks = lds;
   T* __restrict__ Vs = lds + C::K_ELEMS;
 
@@ -137,30 +131,36 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   const int tok = valid ? r / G : 0;
   const int head = g * G + (valid ? r % G : 0);
   const int lim = valid ? P + tok : -1;  // last visible key
-  // the wave's token range (rows are token-major)
+  // the wave's token range (rows are token-major) and the workgroup's last visible key
   const int rw0 = it.t * BM + wv * 32;
   const bool wave_live = rw0 < R;
   const int i_lo_w = wave_live ? rw0 / G : 0;
   const int i_hi_w = wave_live ? min(R - 1, rw0 + 31) / G : 0;
+  const int key_last = P + min(R - 1, it.t * BM + BM - 1) / G;
 
-  const T* __restrict__ qp = reinterpret_cast<const T*>(a.q);
-  const T* __restrict__ kpool = reinterpret_cast<const T*>(a.k_pool);
-  const T* __restrict__ vpool = reinterpret_cast<const T*>(a.v_pool);
-  const T* __restrict__ kext = reinterpret_cast<const T*>(a.k_ext);
-  const T* __restrict__ vext = reinterpret_cast<const T*>(a.v_ext);
+  const gptr<T> kpool = (gptr<T>)a.k_pool;
+  const gptr<T> vpool = (gptr<T>)a.v_pool;
+  const gptr<T> kext = (gptr<T>)a.k_ext;
+  const gptr<T> vext = (gptr<T>)a.v_ext;
+  const gptr<T> zrow = (gptr<T>)a.zero_row;
 
-  // ---- Q^T operand in registers
+  // ---- Q^T operand in registers (negated when the scale is negative)
   constexpr int NQ = F32 ? LQ / 2 : LQ / 16;
   using QT = typename std::conditional<F32, float, bf16x8>::type;
   QT qr[NQ];
   {
-    const T* qrow = qp + (int64_t)(q0 + tok) * a.q_st + (int64_t)head * a.q_sh;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + (int64_t)(q0 + tok) * a.q_st + (int64_t)head * a.q_sh;
+    const uint32_t flip = a.neg_q ? (F32 ? 0x80000000u : 0x80008000u) : 0u;
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) {
       if constexpr (F32) {
-        qr[ks] = valid ? qrow[2 * ks + hi] : 0.0f;
+        qr[ks] = valid ? __uint_as_float(__float_as_uint(qrow[2 * ks + hi]) ^ flip) : 0.0f;
       } else {
         uint4 v = valid ? *reinterpret_cast<const uint4*>(qrow + ks * 16 + hi * 8) : make_uint4(0, 0, 0, 0);
+        v.x ^= flip;
+        v.y ^= flip;
+        v.z ^= flip;
+        v.w ^= flip;
         qr[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
@@ -169,201 +169,216 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY;  // running max, base-2 units
+  float m_ref = -INFINITY;  // reference max of the exponentials, base-2 units
   float l_run = 0.0f;       // this lane's share of the running sum
 
-  // ---- global -> register staging of one KV tile
-  uint4 kreg[C::K_PER_THREAD];
-  uint4 vreg[C::V_PER_THREAD][F32 ? 1 : 4];
+  // ---- row pointer tables: thread t < BN owns key kt*BN + t
+  const int kt0 = it.kt_begin, kt1 = it.kt_end;
+  int64_t slot_next = 0;  // prefetched pool slot for the key this thread owns two tiles ahead
+  auto fetch_slot = [&](int kt) __attribute__((always_inline)) {
+    const int j = kt * BN + tid;
+    slot_next = (tid < BN && j < P && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
+  };
+  auto write_ptrs = [&](int kt) __attribute__((always_inline)) {
+    if (tid < BN) {
+      const int j = kt * BN + tid;
+      gptr<T> kp = zrow;
+      gptr<T> vp = zrow;
+      if (j <= key_last) {
+        if (j < P) {
+          kp = kpool + slot_next * a.kp_ss + (int64_t)g * a.kp_sh;
+          vp = vpool + slot_next * a.vp_ss + (int64_t)g * a.vp_sh;
+        } else {
+          const int64_t row = q0 + (j - P);
+          kp = kext + row * a.ke_st + (int64_t)g * a.ke_sh;
+          vp = vext + row * a.ve_st + (int64_t)g * a.ve_sh;
+        }
+      }
+      kptr[kt & 1][tid] = kp;
+      vptr[kt & 1][tid] = vp;
+    }
+  };
 
-  auto load_tile = [&](int kt) {
-    const int j0 = kt * BN;
+  // ---- global -> register staging of one tile
+  u32x4 kreg[C::K_PER_THREAD];
+  u32x4 vreg[C::V_PER_THREAD];
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
+    const int buf = kt & 1;
 #pragma unroll
     for (int u = 0; u < C::K_PER_THREAD; ++u) {
       const int c = tid + u * NT;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (C::K_CHUNKS % NT == 0 || c < C::K_CHUNKS) {
+      if (C::KC % NT == 0 || c < C::KC) {
         const int row = c / (LQ / VEC), col = (c % (LQ / VEC)) * VEC;
-        const int64_t src = key_source(j0 + row, P, E, q0, kvs, a.kv_indices);
-        if (src >= 0)
-          v = *reinterpret_cast<const uint4*>(kpool + src * a.kp_ss + (int64_t)g * a.kp_sh + col);
-        else if (src <= -2)
-          v = *reinterpret_cast<const uint4*>(kext + (-2 - src) * a.ke_st + (int64_t)g * a.ke_sh + col);
+        kreg[u] = *(gptr<u32x4>)(kptr[buf][row] + col);
       }
-      kreg[u] = v;
     }
 #pragma unroll
     for (int u = 0; u < C::V_PER_THREAD; ++u) {
       const int c = tid + u * NT;
-      if constexpr (F32) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (C::V_UNITS % NT == 0 || c < C::V_UNITS) {
-          const int row = c / (LV / VEC), col = (c % (LV / VEC)) * VEC;
-          const int64_t src = key_source(j0 + row, P, E, q0, kvs, a.kv_indices);
-          if (src >= 0)
-            v = *reinterpret_cast<const uint4*>(vpool + src * a.vp_ss + (int64_t)g * a.vp_sh + col);
-          else if (src <= -2)
-            v = *reinterpret_cast<const uint4*>(vext + (-2 - src) * a.ve_st + (int64_t)g * a.ve_sh + col);
-        }
-        vreg[u][0] = v;
-      } else {
-        const bool in = C::V_UNITS % NT == 0 || c < C::V_UNITS;
-        const int kq = c % (BN / 4), col = (c / (BN / 4)) * 8;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (in) {
-            const int64_t src = key_source(j0 + 4 * kq + rr, P, E, q0, kvs, a.kv_indices);
-            if (src >= 0)
-              v = *reinterpret_cast<const uint4*>(vpool + src * a.vp_ss + (int64_t)g * a.vp_sh + col);
-            else if (src <= -2)
-              v = *reinterpret_cast<const uint4*>(vext + (-2 - src) * a.ve_st + (int64_t)g * a.ve_sh + col);
-          }
-          vreg[u][rr] = v;
-        }
+      if (C::VC % NT == 0 || c < C::VC) {
+        const int row = c / (LV / VEC), col = (c % (LV / VEC)) * VEC;
+        vreg[u] = *(gptr<u32x4>)(vptr[buf][row] + col);
       }
     }
   };
-
-  auto store_tile = [&]() {
+  auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < C::K_PER_THREAD; ++u) {
       const int c = tid + u * NT;
-      if (C::K_CHUNKS % NT == 0 || c < C::K_CHUNKS) {
+      if (C::KC % NT == 0 || c < C::KC) {
         const int row = c / (LQ / VEC), col = (c % (LQ / VEC)) * VEC;
         if constexpr (F32) {
           float* dst = Ks + row * KROW + col;
-          dst[0] = __uint_as_float(kreg[u].x);
-          dst[1] = __uint_as_float(kreg[u].y);
-          dst[2] = __uint_as_float(kreg[u].z);
-          dst[3] = __uint_as_float(kreg[u].w);
+          dst[0] = __uint_as_float(kreg[u][0]);
+          dst[1] = __uint_as_float(kreg[u][1]);
+          dst[2] = __uint_as_float(kreg[u][2]);
+          dst[3] = __uint_as_float(kreg[u][3]);
         } else {
-          *reinterpret_cast<uint4*>(Ks + row * KROW + col) = kreg[u];
+          *reinterpret_cast<u32x4*>(Ks + row * KROW + col) = kreg[u];
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < C::V_PER_THREAD; ++u) {
       const int c = tid + u * NT;
-      if (C::V_UNITS % NT == 0 || c < C::V_UNITS) {
+      if (C::VC % NT == 0 || c < C::VC) {
+        const int row = c / (LV / VEC), col = (c % (LV / VEC)) * VEC;
         if constexpr (F32) {
-          const int row = c / (LV / VEC), col = (c % (LV / VEC)) * VEC;
           float* dst = Vs + row * VROW + col;
-          dst[0] = __uint_as_float(vreg[u][0].x);
-          dst[1] = __uint_as_float(vreg[u][0].y);
-          dst[2] = __uint_as_float(vreg[u][0].z);
-          dst[3] = __uint_as_float(vreg[u][0].w);
+          dst[0] = __uint_as_float(vreg[u][0]);
+          dst[1] = __uint_as_float(vreg[u][1]);
+          dst[2] = __uint_as_float(vreg[u][2]);
+          dst[3] = __uint_as_float(vreg[u][3]);
         } else {
-          // transpose 4 keys x 8 columns into 8 rows of V^T, 4 keys (8 bytes) each
-          const int kq = c % (BN / 4), col = (c / (BN / 4)) * 8;
-          const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vreg[u][0]);
-          const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vreg[u][1]);
-          const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vreg[u][2]);
-          const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vreg[u][3]);
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) {
-            // columns col+2*w2 (low halves) and col+2*w2+1 (high halves)
-            uint2 lo, hi2;
-            lo.x = __builtin_amdgcn_perm(r1[w2], r0[w2], 0x05040100u);
-            lo.y = __builtin_amdgcn_perm(r3[w2], r2[w2], 0x05040100u);
-            hi2.x = __builtin_amdgcn_perm(r1[w2], r0[w2], 0x07060302u);
-            hi2.y = __builtin_amdgcn_perm(r3[w2], r2[w2], 0x07060302u);
-            *reinterpret_cast<uint2*>(Vs + (col + 2 * w2) * VROW + 4 * kq) = lo;
-            *reinterpret_cast<uint2*>(Vs + (col + 2 * w2 + 1) * VROW + 4 * kq) = hi2;
-          }
+          *reinterpret_cast<u32x4*>(Vs + row * VROW + col) = vreg[u];
         }
       }
     }
   };
 
-  const int kt0 = it.kt_begin, kt1 = it.kt_end;
-  if (kt0 < kt1) load_tile(kt0);
+  // prologue: pointer tables for the first two tiles, then the first tile's loads
+  if (kt0 < kt1) {
+    fetch_slot(kt0);
+    write_ptrs(kt0);
+    if (kt0 + 1 < kt1) {
+      fetch_slot(kt0 + 1);
+      write_ptrs(kt0 + 1);
+    }
+    __syncthreads();
+    load_tile(kt0);
+  }
+
   for (int kt = kt0; kt < kt1; ++kt) {
-    __syncthreads();  // previous tile fully consumed
+    __syncthreads();  // previous tile consumed; pointer table of kt+1 published
     store_tile();
     __syncthreads();
     if (kt + 1 < kt1) load_tile(kt + 1);  // in flight while this tile is computed
+    if (kt + 2 < kt1) fetch_slot(kt + 2);
 
     const int j0 = kt * BN;
-    if (!wave_live || j0 > P + i_hi_w) continue;  // nothing visible for this wave
-    const bool need_mask = j0 + BN - 1 > P + i_lo_w;
+    if (wave_live && j0 <= P + i_hi_w) {
+      const bool need_mask = j0 + BN - 1 > P + i_lo_w;
 
-    // S^T = K Q^T for the tile's 32-key blocks
-    f32x16 s[NKB];
+      // S^T = K Q^T for the tile's 32-key blocks
+      f32x16 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      const T* krow = Ks + (kb * 32 + qi) * KROW;
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x16{};
+        const T* krow = Ks + (kb * 32 + qi) * KROW;
 #pragma unroll
-      for (int ks = 0; ks < NQ; ++ks) {
+        for (int ks = 0; ks < NQ; ++ks) {
+          if constexpr (F32) {
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + hi], qr[ks], s[kb], 0, 0, 0);
+          } else {
+            bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 16 + hi * 8));
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qr[ks], s[kb], 0, 0, 0);
+          }
+        }
+      }
+
+      // soft-cap (base-2 units), then mask the diagonal tiles, then the row max;
+      // without a cap the max is taken on raw dot products and scaled after
+      if constexpr (CAP) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const float e = fast_exp2(s[kb][rr] * (a.cap_in * 2.0f * kLog2e));
+            s[kb][rr] = a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
+          }
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
+            s[kb][rr] = j <= lim ? s[kb][rr] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+      mx = pair_max(mx);
+      if constexpr (!CAP) mx *= a.scale_log2;
+      // raise the reference max only when some row outgrows it by the slack
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      }
+      const float m_sub = m_ref == -INFINITY ? 0.0f : m_ref;
+
+      // P and O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
         if constexpr (F32) {
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + hi], qr[ks], s[kb], 0, 0, 0);
-        } else {
-          bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 16 + hi * 8));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qr[ks], s[kb], 0, 0, 0);
-        }
-      }
-    }
-
-    // logits (base 2), mask, row max
-    float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        float x = logit2<CAP>(s[kb][rr], a);
-        if (need_mask) {
-          const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
-          x = j <= lim ? x : -INFINITY;
-        }
-        s[kb][rr] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-
-    // P and O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      if constexpr (F32) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float p = fast_exp2(s[kb][rr] - m_use);
-          l_run += p;
-          const int key = kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * VROW + db * 32 + qi], p, acc[db], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 pb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = fast_exp2(s[kb][8 * half + e] - m_use);
+          for (int rr = 0; rr < 16; ++rr) {
+            const float p = CAP ? fast_exp2(s[kb][rr] - m_sub) : fast_exp2(fmaf(s[kb][rr], a.scale_log2, -m_sub));
             l_run += p;
-            pb[e] = (__bf16)p;
-          }
-          const int kcol = kb * 32 + 16 * half + 4 * hi;
+            const int key = kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const T* vrow = Vs + (db * 32 + qi) * VROW + kcol;
-            uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-            uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
-            bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[db], 0, 0, 0);
+            for (int db = 0; db < NDB; ++db)
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * VROW + db * 32 + qi], p, acc[db], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = s[kb][8 * half + e];
+              const float p = CAP ? fast_exp2(x - m_sub) : fast_exp2(fmaf(x, a.scale_log2, -m_sub));
+              l_run += p;
+              pb[e] = (__bf16)p;
+            }
+            // keys kb*32 + 16*half + 4*hi + {0..3} and {8..11}: lane (in its 16-lane
+            // group) j points at row key0 + j/4, columns cbase + 4*(j%4); it receives
+            // the 4 keys of column cbase + j.
+            const int key0 = kb * 32 + 16 * half + 4 * hi + ((lane & 15) >> 2);
+            const int cofs = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const T* v0 = Vs + key0 * VROW + db * 32 + cofs;
+              i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) i16x4*)(v0));
+              i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) i16x4*)(v0 + 8 * VROW));
+              bf16x8 va = __builtin_bit_cast(
+                  bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[db], 0, 0, 0);
+            }
           }
         }
       }
     }
+    if (kt + 2 < kt1) write_ptrs(kt + 2);  // its table slot was last read before this tile's barriers
   }
 
   // ---- epilogue
@@ -404,7 +419,7 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
             make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
       }
     }
-    if (hi == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_run, l_tot);
+    if (hi == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref, l_tot);
   }
 }
 
@@ -412,6 +427,7 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s acc_s 2^(m_s - M) / L
 // which is the log-sum-exp state merge (page "flashinfer_backend.py",
 // forward_extend, merge_state of the ragged and paged partial outputs).
+// One workgroup per split item; thread = (row, 4 columns).
 template <bool F32, int LV>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int bm) {
   using T = typename Elem<F32>::T;
@@ -431,8 +447,9 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int bm) {
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < mi.n; ++s) {
       const int64_t prow = (int64_t)(mi.part_base + s) * bm + row;
-      const float w = fast_exp2(a.part_ml[prow * 2] - M);
-      L += a.part_ml[prow * 2 + 1] * w;
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
+      const float w = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
+      L += ml.y * w;
       const float4 v = *reinterpret_cast<const float4*>(a.part_acc + prow * LV + d);
       o.x += v.x * w;
       o.y += v.y * w;
@@ -474,7 +491,7 @@ int occupancy_t() {
   return n > 0 ? n : 1;
 }
 
-// The supported (dtype, lq, lv) variants and their key-tile widths.
+// The supported (dtype, lq, lv) variants: key-tile width and workgroups per CU.
 #define PKV_VARIANTS(X)          \
   X(false, 64, 64, 64, 2)        \
   X(false, 128, 128, 64, 2)      \

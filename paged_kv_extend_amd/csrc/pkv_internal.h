@@ -34,6 +34,8 @@ struct PlanHeader {
   int32_t pad[59];
 };
 
+constexpr int kZeroRowBytes = 4096;  // >= 576 fp32 or bf16 elements
+
 // Static tiling of one kernel instantiation.
 struct Tiling {
   int bm;       // packed query rows per workgroup
@@ -51,7 +53,7 @@ struct PlanBounds {
 
 // Workspace carve-up.
 struct WsLayout {
-  size_t header, work, merge, scratch, part_ml, part_acc, total;
+  size_t header, zero_row, work, merge, scratch, part_ml, part_acc, total;
 };
 
 struct AttnArgs {
@@ -67,9 +69,11 @@ struct AttnArgs {
   int64_t q_st, q_sh, o_st, o_sh, ke_st, ke_sh, ve_st, ve_sh, kp_ss, kp_sh, vp_ss, vp_sh;
   int32_t group;     // query heads per KV head
   int32_t use_cap;   // soft-cap enabled
-  float scale_log2;  // scale * log2(e): logits are kept in base-2 units
-  float cap_in;      // scale / cap
+  int32_t neg_q;     // the scale is negative: q is negated (exact) and |scale| used
+  float scale_log2;  // |scale| * log2(e): logits are kept in base-2 units
+  float cap_in;      // |scale| / cap
   float cap_out;     // cap * log2(e)
+  const void* zero_row;  // >= max(lq, lv) zero elements, read for keys past a sequence
   const PlanHeader* hdr;
   const WorkItem* work;
   const MergeItem* merge;
@@ -85,6 +89,7 @@ struct PlanArgs {
   int32_t min_chunk;      // never split below this many KV tiles
   int64_t max_items, part_budget, max_merge;
   PlanHeader* hdr;
+  void* zero_row;    // zeroed by the planner: kZeroRowBytes bytes
   WorkItem* work;    // [max_work]
   MergeItem* merge;  // [max_merge]
   int32_t* scratch;  // [bs + 1 + 7 * max_items]

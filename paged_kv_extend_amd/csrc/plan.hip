@@ -3,11 +3,11 @@
 // Items are (sequence b, KV head g, packed-row tile t).  An item's cost is the
 // number of KV tiles it must visit: the prefix plus the new tokens up to the
 // last token in its rows (keys past the causal diagonal are never visited).
-// Items costing more than a chunk limit are split into near-equal KV ranges
-// whose partial softmax states are merged afterwards; the limit starts at
-// total / (2 * resident workgroups) so no chunk exceeds half an average
-// workgroup's share, and grows when the partial-state budget would overflow.
-// Chunks are then ordered heaviest first, so the hardware's in-order
+// An item costing more than one resident workgroup's average share (total
+// cost / resident workgroups) is split into near-equal KV ranges whose
+// partial softmax states are merged afterwards; the limit grows when the
+// partial-state budget would overflow.  Chunks are then ordered heaviest
+// first (a counting sort over 256 size classes), so the hardware's in-order
 // dispatch approximates longest-processing-time-first scheduling.
 //
 // The pages' own grids launch one program per (sequence, head, query block)
@@ -20,40 +20,38 @@ namespace pkv {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kBuckets = 4096;
+constexpr int kWaves = kThreads / 64;
+constexpr int kBuckets = 256;
+constexpr int kSeqLds = 8192;  // sequence offsets kept in LDS up to this batch size
 
 struct Shared {
-  int32_t scan[kThreads];
-  int64_t red[kThreads / 64];
+  int32_t wave_tot[kWaves];
+  int64_t red[kWaves];
   int32_t bucket[kBuckets];
+  int32_t seq_base[kSeqLds + 1];
 };
 
-// Exclusive scan of f(i), i in [0, n), written to out[i]; returns the total.
-// Each thread owns a contiguous run; one block scan of the run sums.
-template <class F>
-__device__ int64_t block_scan(int n, F f, int32_t* out, Shared& sh) {
-  const int tid = threadIdx.x;
-  const int per = (n + kThreads - 1) / kThreads;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int32_t sum = 0;
-  for (int i = lo; i < hi; ++i) sum += f(i);
-  sh.scan[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int32_t v = tid >= off ? sh.scan[tid - off] : 0;
-    __syncthreads();
-    sh.scan[tid] += v;
-    __syncthreads();
+// Exclusive block-wide scan of one int per thread; returns the block total.
+__device__ int32_t block_excl_scan(int32_t v, int32_t* total, Shared& sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(inc, off);
+    if (lane >= off) inc += u;
   }
-  int32_t run = sh.scan[tid] - sum;
-  const int64_t total = sh.scan[kThreads - 1];
-  for (int i = lo; i < hi; ++i) {
-    const int32_t v = f(i);
-    out[i] = run;
-    run += v;
+  if (lane == 63) sh.wave_tot[w] = inc;
+  __syncthreads();
+  int32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int32_t t = sh.wave_tot[i];
+    before += i < w ? t : 0;
+    all += t;
   }
   __syncthreads();
-  return total;
+  *total = all;
+  return before + inc - v;
 }
 
 __device__ int64_t block_sum(int64_t v, Shared& sh) {
@@ -61,7 +59,8 @@ __device__ int64_t block_sum(int64_t v, Shared& sh) {
   if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
   __syncthreads();
   int64_t t = 0;
-  for (int w = 0; w < kThreads / 64; ++w) t += sh.red[w];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += sh.red[w];
   __syncthreads();
   return t;
 }
@@ -72,22 +71,33 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
   __shared__ Shared sh;
   const int tid = threadIdx.x;
   const int G = a.group, BM = a.bm, BN = a.bn, H = a.num_kv_heads;
-  // scratch: seq_base[bs+1] | cost | chunk_base | part_base | merge_idx | b | g | t  (items)
-  int32_t* seq_base = a.scratch;
-  int32_t* cost_of = seq_base + a.bs + 1;
-  int32_t* chunk_base = cost_of + a.max_items;
-  int32_t* part_base = chunk_base + a.max_items;
+  // global scratch: seq_base[bs+1] | cost | part_base | merge_idx | b | g | t  (per item)
+  int32_t* seq_base_g = a.scratch;
+  int32_t* cost_of = seq_base_g + a.bs + 1;
+  int32_t* part_base = cost_of + a.max_items;
   int32_t* merge_idx = part_base + a.max_items;
   int32_t* item_b = merge_idx + a.max_items;
   int32_t* item_g = item_b + a.max_items;
   int32_t* item_t = item_g + a.max_items;
+  const bool seq_in_lds = a.bs <= kSeqLds;
+  int32_t* seq_base = seq_in_lds ? sh.seq_base : seq_base_g;
 
-  // 1. items per sequence: H * ceil(E_b * G / BM)
-  auto seq_items = [&](int b) {
-    const int E = a.qo_indptr[b + 1] - a.qo_indptr[b];
-    return H * ceil_div(E * G, BM);
-  };
-  const int n_items = (int)block_scan(a.bs, seq_items, seq_base, sh);
+  // zero row read for keys past a sequence
+  for (int i = tid; i < kZeroRowBytes / 16; i += kThreads)
+    reinterpret_cast<uint4*>(a.zero_row)[i] = make_uint4(0, 0, 0, 0);
+
+  // 1. items per sequence, H * ceil(E_b G / BM); exclusive scan in runs of kThreads
+  int32_t carry = 0;
+  for (int base = 0; base < a.bs; base += kThreads) {
+    const int b = base + tid;
+    int32_t v = 0;
+    if (b < a.bs) v = H * ceil_div((a.qo_indptr[b + 1] - a.qo_indptr[b]) * G, BM);
+    int32_t tot;
+    const int32_t ex = block_excl_scan(v, &tot, sh);
+    if (b < a.bs) seq_base[b] = carry + ex;
+    carry += tot;
+  }
+  const int n_items = carry;
   if (tid == 0) seq_base[a.bs] = n_items;
   __syncthreads();
 
@@ -103,20 +113,21 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     const int E = a.qo_indptr[b + 1] - a.qo_indptr[b];
     const int P = a.kv_indptr[b + 1] - a.kv_indptr[b];
     const int T = ceil_div(E * G, BM);
-    const int t = (n - seq_base[b]) % T;
+    const int local = n - seq_base[b];
+    const int t = local % T;
     const int row_hi = min((t + 1) * BM, E * G) - 1;
     const int cost = ceil_div(P + row_hi / G + 1, BN);
     cost_of[n] = cost;
     item_b[n] = b;
-    item_g[n] = (n - seq_base[b]) / T;
+    item_g[n] = local / T;
     item_t[n] = t;
     my_total += cost;
   }
   const int64_t total = block_sum(my_total, sh);
 
-  // 3. chunk limit: half an average share per resident workgroup, grown until
-  //    the split chunks fit the partial-state budget
-  int64_t chunk = (total + 2 * (int64_t)a.slots - 1) / (2 * (int64_t)a.slots);
+  // 3. chunk limit: one average share per resident workgroup, grown until the
+  //    split chunks fit the partial-state budget
+  int64_t chunk = (total + a.slots - 1) / a.slots;
   if (chunk < a.min_chunk) chunk = a.min_chunk;
   for (;;) {
     int64_t parts = 0;
@@ -128,46 +139,62 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     if (parts <= a.part_budget) break;
     chunk *= 2;
   }
-  auto nsplit = [&](int n) {
-    const int c = cost_of[n];
-    return c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
-  };
 
-  // 4. per-item offsets of partial slots and merge records
-  const int n_work = (int)block_scan(n_items, nsplit, chunk_base, sh);
-  block_scan(n_items, [&](int n) { int k = nsplit(n); return k > 1 ? k : 0; }, part_base, sh);
-  const int n_merge = (int)block_scan(n_items, [&](int n) { return nsplit(n) > 1 ? 1 : 0; }, merge_idx, sh);
+  // 4. partial-slot and merge-record offsets of split items (scan in runs)
+  int32_t pcarry = 0, mcarry = 0;
+  for (int base = 0; base < n_items; base += kThreads) {
+    const int n = base + tid;
+    int k = 1;
+    if (n < n_items) {
+      const int c = cost_of[n];
+      k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
+    }
+    int32_t ptot, mtot;
+    const int32_t pex = block_excl_scan(k > 1 ? k : 0, &ptot, sh);
+    const int32_t mex = block_excl_scan(k > 1 ? 1 : 0, &mtot, sh);
+    if (n < n_items) {
+      part_base[n] = pcarry + pex;
+      merge_idx[n] = mcarry + mex;
+    }
+    pcarry += ptot;
+    mcarry += mtot;
+  }
 
-  // 5. heaviest first: counting sort of chunks by size (descending); the order
-  //    among equal sizes only affects scheduling, never the results
+  // 5. heaviest first: counting sort of chunks over 256 size classes (descending)
   for (int i = tid; i < kBuckets; i += kThreads) sh.bucket[i] = 0;
   __syncthreads();
+  const int64_t cls_div = (chunk + kBuckets - 1) / kBuckets;  // chunk sizes are <= chunk
+  auto size_class = [&](int sz) { return (int)min<int64_t>(kBuckets - 1, (sz - 1) / cls_div); };
+  int32_t my_chunks = 0;
   for (int n = tid; n < n_items; n += kThreads) {
-    const int c = cost_of[n], k = nsplit(n);
+    const int c = cost_of[n];
+    const int k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
+    my_chunks += k;
     for (int s = 0; s < k; ++s) {
       const int sz = (int)((int64_t)c * (s + 1) / k - (int64_t)c * s / k);
-      atomicAdd(&sh.bucket[min(sz, kBuckets - 1)], 1);
+      atomicAdd(&sh.bucket[size_class(sz)], 1);
     }
   }
   __syncthreads();
-  if (tid == 0) {  // descending exclusive scan over bucket counts
-    int run = 0;
-    for (int i = kBuckets - 1; i >= 0; --i) {
-      const int v = sh.bucket[i];
-      sh.bucket[i] = run;
-      run += v;
-    }
+  {  // descending exclusive scan of the 256 class counts
+    const int cls = kBuckets - 1 - tid;
+    const int32_t v = tid < kBuckets ? sh.bucket[cls] : 0;
+    int32_t tot;
+    const int32_t ex = block_excl_scan(v, &tot, sh);
+    if (tid < kBuckets) sh.bucket[cls] = ex;
+    __syncthreads();
   }
-  __syncthreads();
   for (int n = tid; n < n_items; n += kThreads) {
-    const int c = cost_of[n], k = nsplit(n);
+    const int c = cost_of[n];
+    const int k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
+    const int b = item_b[n], ig = item_g[n], itt = item_t[n];
     for (int s = 0; s < k; ++s) {
       const int k0 = (int)((int64_t)c * s / k), k1 = (int)((int64_t)c * (s + 1) / k);
-      const int pos = atomicAdd(&sh.bucket[min(k1 - k0, kBuckets - 1)], 1);
+      const int pos = atomicAdd(&sh.bucket[size_class(k1 - k0)], 1);
       WorkItem w;
-      w.b = item_b[n];
-      w.g = item_g[n];
-      w.t = item_t[n];
+      w.b = b;
+      w.g = ig;
+      w.t = itt;
       w.kt_begin = k0;
       w.kt_end = k1;
       w.part = k > 1 ? part_base[n] + s : -1;
@@ -177,18 +204,19 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     }
     if (k > 1) {
       MergeItem m;
-      m.b = item_b[n];
-      m.g = item_g[n];
-      m.t = item_t[n];
+      m.b = b;
+      m.g = ig;
+      m.t = itt;
       m.part_base = part_base[n];
       m.n = k;
       m.pad0 = m.pad1 = m.pad2 = 0;
       a.merge[merge_idx[n]] = m;
     }
   }
+  const int64_t n_work = block_sum(my_chunks, sh);
   if (tid == 0) {
-    a.hdr->num_work = n_work;
-    a.hdr->num_merge = n_merge;
+    a.hdr->num_work = (int32_t)n_work;
+    a.hdr->num_merge = mcarry;
     a.hdr->chunk_tiles = (int32_t)chunk;
     a.hdr->total_tiles = (int32_t)total;
     a.hdr->num_items = n_items;
