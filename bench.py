@@ -95,7 +95,7 @@ def main():
     w = wl.get(args.workload)
     flops = w.causal_flops()
     algo_bytes = w.algorithmic_bytes()
-    copies = args.copies or max(1, int(np.ceil(512e6 / algo_bytes)))
+    copies = args.copies or max(1, min(16, int(np.ceil(512e6 / algo_bytes))))
     sets = [wl.to_torch(w, dev) for _ in range(copies)]
     for s in sets:
         s["uni"] = (torch.empty(w.bs + 1, dtype=torch.int32, device=dev),

@@ -4,7 +4,8 @@
 // _fwd_kernel_unified: logits are q.k times the scale, optionally soft-capped
 // (cap * tanh(s / cap)), masked so that new token i of a sequence with P
 // prefix tokens sees keys j <= P + i, and combined with an online softmax
-// whose probabilities are rounded to the value dtype before the P.V product.
+// whose probabilities are rounded to the value dtype before the P.V product
+// (here the row sum adds the same rounded probabilities).
 // The key sequence is the prefix, gathered from the token-granular pool
 // through kv_indices, followed by the sequence's own new tokens (page
 // "flashinfer_backend.py", forward_extend / call_begin_forward: prefix via
@@ -47,6 +48,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes, kept in registers
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // base-2 headroom before the reference max is raised
@@ -85,12 +87,14 @@ struct Cfg {
   static constexpr int NT = 256;
   static constexpr int BM = 128;
   static constexpr int VEC = Elem<F32>::kVec;
-  // LDS pitches in elements.  bf16 K [BN][LQ+8]: 16-byte reads of 8
-  // consecutive rows land on 8 distinct 4-bank groups.  bf16 V [BN][LV+16]:
-  // a transposing read covers 4 rows x 32 bytes; a row pitch of 8 banks (mod
-  // 32) keeps the 4 rows on distinct banks.  fp32: one pad element per row.
+  // LDS pitches in elements, chosen from measured bank-conflict counts on
+  // gfx950.  bf16 K [BN][LQ+8]: the 16-byte operand reads of 32 rows are
+  // conflict-free when the row pitch is 4 x (odd) dwords modulo 64.  bf16 V
+  // [BN][LV+32]: the transposing reads (4 rows x 32 bytes per 16 lanes, two
+  // such groups per half-wave) are conflict-free when the pitch is 16 dwords
+  // modulo 64.  fp32: one pad element per row.
   static constexpr int KROW = F32 ? LQ + 1 : LQ + 8;
-  static constexpr int VROW = F32 ? LV + 1 : LV + 16;
+  static constexpr int VROW = F32 ? LV + 1 : LV + 32;
   static constexpr int K_ELEMS = BN * KROW;
   static constexpr int V_ELEMS = BN * VROW;
   static constexpr int KC = BN * LQ / VEC;  // 16-byte chunks per tile
@@ -355,9 +359,14 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
             for (int e = 0; e < 8; ++e) {
               const float x = s[kb][8 * half + e];
               const float p = CAP ? fast_exp2(x - m_sub) : fast_exp2(fmaf(x, a.scale_log2, -m_sub));
-              l_run += p;
               pb[e] = (__bf16)p;
             }
+            // the row sum adds the same rounded weights that multiply V, two per dot2
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones, l_run, false);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones, l_run, false);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones, l_run, false);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones, l_run, false);
             // keys kb*32 + 16*half + 4*hi + {0..3} and {8..11}: lane (in its 16-lane
             // group) j points at row key0 + j/4, columns cbase + 4*(j%4); it receives
             // the 4 keys of column cbase + j.
