@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attention_traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -86,6 +88,16 @@ def main():
     import torch
     import paged_kv_extend_amd as pkv
     import workloads as wl
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 5}))
+        return 0
 
     if not os.path.exists(pkv.LIB_PATH):
         from paged_kv_extend_amd import _build

@@ -37,6 +37,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kMinChunkTiles = 8;           // never split an item below this many KV tiles
 constexpr size_t kPartialBytes = 64u << 20;  // budget for split partial states
+constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dealt round-robin
 
 // Resident attention workgroups on the current device, cached per (device, variant).
 int resident_slots(int dtype, int lq, int lv) {
@@ -51,7 +52,10 @@ int resident_slots(int dtype, int lq, int lv) {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  const int slots = cus * pkv::attention_blocks_per_cu(dtype, lq, lv);
+  pkv::Tiling t;
+  const int per_cu = pkv::dl_tiling(dtype, lq, lv, &t) ? pkv::dl_blocks_per_cu(lq, lv)
+                                                        : pkv::attention_blocks_per_cu(dtype, lq, lv);
+  const int slots = cus * per_cu;
   cache[key] = slots;
   return slots;
 }
@@ -67,7 +71,7 @@ int check_desc(const pkv_attn_desc_t* d, pkv::Tiling* t) {
   if (d->num_q_heads % d->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
                 d->num_kv_heads);
-  if (!pkv::attn_tiling(d->dtype, d->lq, d->lv, t))
+  if (!pkv::dl_tiling(d->dtype, d->lq, d->lv, t) && !pkv::attn_tiling(d->dtype, d->lq, d->lv, t))
     return fail(PKV_ERR_UNSUPPORTED, "head dims (lq %d, lv %d) not supported for dtype %d", d->lq, d->lv,
                 d->dtype);
   if (d->total_q_tokens < 0 || d->num_prefix_indices < 0 || d->pool_slots < 0)
@@ -98,7 +102,9 @@ pkv::PlanBounds plan_bounds(const pkv_attn_desc_t* d, const pkv::Tiling& t) {
   if (budget < 16) budget = 16;
   pb.part_budget = budget;
   pb.max_merge = budget / 2;
-  pb.max_work = pb.max_items + budget;
+  // chunks never exceed items + budget; placement may leave up to as many
+  // empty slots again when the XCD bins end up uneven in count
+  pb.max_work = 2 * (pb.max_items + budget) + 8;
   return pb;
 }
 
@@ -114,7 +120,7 @@ pkv::WsLayout ws_layout(const pkv_attn_desc_t* d, const pkv::Tiling& t, const pk
   l.merge = off;
   off = align_up(off + sizeof(pkv::MergeItem) * (size_t)(pb.max_merge > 0 ? pb.max_merge : 1), 256);
   l.scratch = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)(d->bs + 1 + 7 * pb.max_items), 256);
+  off = align_up(off + sizeof(int32_t) * (size_t)(d->bs + 1 + 8 * pb.max_items), 256);
   l.part_ml = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)pb.part_budget * t.bm, 256);
   l.part_acc = off;
@@ -264,6 +270,8 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   pa.bn = t.bn;
   pa.slots = resident_slots(d.dtype, d.lq, d.lv);
   pa.min_chunk = kMinChunkTiles;
+  pa.xcds = kXcds;
+  pa.max_work = pb.max_work;
   pa.max_items = pb.max_items;
   pa.part_budget = pb.part_budget;
   pa.max_merge = pb.max_merge;
@@ -313,7 +321,9 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   a.part_ml = reinterpret_cast<float*>(ws + wl.part_ml);
   const auto ev = profile_slot();
   if (ev.first) (void)hipEventRecord(ev.first, s);
-  e = pkv::launch_attention(d.dtype, d.lq, d.lv, a, pb.max_work, s);
+  pkv::Tiling td;
+  e = pkv::dl_tiling(d.dtype, d.lq, d.lv, &td) ? pkv::launch_dl(d.lq, d.lv, a, pb.max_work, s)
+                                               : pkv::launch_attention(d.dtype, d.lq, d.lv, a, pb.max_work, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   if (ev.second) (void)hipEventRecord(ev.second, s);
   e = pkv::launch_merge(d.dtype, d.lv, a, t.bm, pb.max_merge, s);

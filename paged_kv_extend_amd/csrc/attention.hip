@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
 
   if ((int)blockIdx.x >= a.hdr->num_work) return;
   const WorkItem it = a.work[blockIdx.x];
+  if (it.b < 0) return;  // empty placement slot
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qi = lane & 31, hi = lane >> 5;
   const int G = a.group;

@@ -14,7 +14,7 @@ namespace pkv {
 // head g*G + r % G (token-major, so one KV tile serves all G heads of a token).
 // part < 0: the item covers all KV tiles and writes o directly; otherwise it is
 // one chunk of a split item and writes unnormalised partial state into
-// partial slot `part`.
+// partial slot `part`.  b < 0 marks an empty slot.
 struct WorkItem {
   int32_t b, g, t, kt_begin, kt_end, part, pad0, pad1;
 };
@@ -31,7 +31,9 @@ struct PlanHeader {
   int32_t chunk_tiles;  // split threshold the planner settled on
   int32_t total_tiles;  // KV tiles over all items before splitting
   int32_t num_items;    // items before splitting
-  int32_t pad[59];
+  int32_t num_chunks;   // work items after splitting (num_work also counts empty slots)
+  int32_t xcds;         // XCD bins used for placement (1: plain heaviest-first)
+  int32_t pad[57];
 };
 
 constexpr int kZeroRowBytes = 4096;  // >= 576 fp32 or bf16 elements
@@ -87,12 +89,14 @@ struct PlanArgs {
   int32_t bs, num_kv_heads, group, bm, bn;
   int32_t slots;          // workgroups resident at once on the device
   int32_t min_chunk;      // never split below this many KV tiles
+  int32_t xcds;           // XCDs to spread work over (workgroup i runs on XCD i mod xcds)
   int64_t max_items, part_budget, max_merge;
+  int64_t max_work;       // grid size: slots available for work items
   PlanHeader* hdr;
   void* zero_row;    // zeroed by the planner: kZeroRowBytes bytes
   WorkItem* work;    // [max_work]
   MergeItem* merge;  // [max_merge]
-  int32_t* scratch;  // [bs + 1 + 7 * max_items]
+  int32_t* scratch;  // [bs + 1 + 8 * max_items]
 };
 
 // Kernel variants: (dtype, lq, lv).  Returns false when unsupported.
@@ -108,5 +112,9 @@ hipError_t launch_index_build(const int32_t* prefix_kv_indptr, const int64_t* pr
                               int32_t* prefix_lens, hipStream_t s);
 // Workgroups of the attention kernel resident per CU (from the occupancy API).
 int attention_blocks_per_cu(int dtype, int lq, int lv);
+// The direct-to-LDS kernel (bf16, head dims 64, 128, 256); preferred when it applies.
+bool dl_tiling(int dtype, int lq, int lv, Tiling* t);
+hipError_t launch_dl(int lq, int lv, const AttnArgs& a, int64_t grid, hipStream_t s);
+int dl_blocks_per_cu(int lq, int lv);
 
 }  // namespace pkv

@@ -6,9 +6,16 @@
 // An item costing more than one resident workgroup's average share (total
 // cost / resident workgroups) is split into near-equal KV ranges whose
 // partial softmax states are merged afterwards; the limit grows when the
-// partial-state budget would overflow.  Chunks are then ordered heaviest
-// first (a counting sort over 256 size classes), so the hardware's in-order
-// dispatch approximates longest-processing-time-first scheduling.
+// partial-state budget would overflow.
+//
+// Placement: workgroup i of a launch runs on XCD i mod 8, and each XCD has
+// its own L2.  The (b, g, t, chunk)-ordered cost sequence is cut into one
+// contiguous, equal-cost range per XCD (a chunk goes to the range holding its
+// midpoint), so the q-tiles of one (sequence, KV head) -- which read the same
+// prefix K/V -- share an L2 while every XCD gets the same work.  Within an
+// XCD chunks run heaviest first (counting sort over 256 size classes), which
+// with in-order dispatch approximates longest-processing-time-first; slot
+// rank*8 + xcd holds the XCD's rank-th chunk and unused slots hold empty items.
 //
 // The pages' own grids launch one program per (sequence, head, query block)
 // with every program visiting all keys (page "extend_attention.py",
@@ -22,12 +29,14 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBuckets = 256;
+constexpr int kMaxXcd = 8;
 constexpr int kSeqLds = 8192;  // sequence offsets kept in LDS up to this batch size
 
 struct Shared {
   int32_t wave_tot[kWaves];
   int64_t red[kWaves];
-  int32_t bucket[kBuckets];
+  int32_t bucket[kMaxXcd * kBuckets];
+  int32_t bin_count[kMaxXcd];
   int32_t seq_base[kSeqLds + 1];
 };
 
@@ -71,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
   __shared__ Shared sh;
   const int tid = threadIdx.x;
   const int G = a.group, BM = a.bm, BN = a.bn, H = a.num_kv_heads;
-  // global scratch: seq_base[bs+1] | cost | part_base | merge_idx | b | g | t  (per item)
+  // global scratch: seq_base[bs+1] | cost | part_base | merge_idx | b | g | t | cum  (per item)
   int32_t* seq_base_g = a.scratch;
   int32_t* cost_of = seq_base_g + a.bs + 1;
   int32_t* part_base = cost_of + a.max_items;
@@ -79,6 +88,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
   int32_t* item_b = merge_idx + a.max_items;
   int32_t* item_g = item_b + a.max_items;
   int32_t* item_t = item_g + a.max_items;
+  int32_t* cum_cost = item_t + a.max_items;  // exclusive running sum of item costs
   const bool seq_in_lds = a.bs <= kSeqLds;
   int32_t* seq_base = seq_in_lds ? sh.seq_base : seq_base_g;
 
@@ -140,48 +150,66 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     chunk *= 2;
   }
 
-  // 4. partial-slot and merge-record offsets of split items (scan in runs)
-  int32_t pcarry = 0, mcarry = 0;
+  // 4. partial-slot and merge-record offsets of split items, running cost (scans in runs)
+  int32_t pcarry = 0, mcarry = 0, ccarry = 0;
   for (int base = 0; base < n_items; base += kThreads) {
     const int n = base + tid;
-    int k = 1;
+    int k = 1, c = 0;
     if (n < n_items) {
-      const int c = cost_of[n];
+      c = cost_of[n];
       k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
     }
-    int32_t ptot, mtot;
+    int32_t ptot, mtot, ctot;
     const int32_t pex = block_excl_scan(k > 1 ? k : 0, &ptot, sh);
     const int32_t mex = block_excl_scan(k > 1 ? 1 : 0, &mtot, sh);
+    const int32_t cex = block_excl_scan(c, &ctot, sh);
     if (n < n_items) {
       part_base[n] = pcarry + pex;
       merge_idx[n] = mcarry + mex;
+      cum_cost[n] = ccarry + cex;
     }
     pcarry += ptot;
     mcarry += mtot;
+    ccarry += ctot;
   }
 
-  // 5. heaviest first: counting sort of chunks over 256 size classes (descending)
-  for (int i = tid; i < kBuckets; i += kThreads) sh.bucket[i] = 0;
-  __syncthreads();
+  // 5. XCD bin of every chunk (midpoint rule), then heaviest first inside a bin
   const int64_t cls_div = (chunk + kBuckets - 1) / kBuckets;  // chunk sizes are <= chunk
   auto size_class = [&](int sz) { return (int)min<int64_t>(kBuckets - 1, (sz - 1) / cls_div); };
+  int X = a.xcds < 1 ? 1 : (a.xcds > kMaxXcd ? kMaxXcd : a.xcds);
+  auto bin_of = [&](int n, int k0, int k1) {
+    const int64_t mid2 = 2 * (int64_t)cum_cost[n] + k0 + k1;  // twice the chunk midpoint
+    return (int)min<int64_t>(X - 1, mid2 * X / (2 * (total > 0 ? total : 1)));
+  };
   int32_t my_chunks = 0;
-  for (int n = tid; n < n_items; n += kThreads) {
-    const int c = cost_of[n];
-    const int k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
-    my_chunks += k;
-    for (int s = 0; s < k; ++s) {
-      const int sz = (int)((int64_t)c * (s + 1) / k - (int64_t)c * s / k);
-      atomicAdd(&sh.bucket[size_class(sz)], 1);
+  int max_count = 0;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    for (int i = tid; i < kMaxXcd * kBuckets; i += kThreads) sh.bucket[i] = 0;
+    __syncthreads();
+    my_chunks = 0;
+    for (int n = tid; n < n_items; n += kThreads) {
+      const int c = cost_of[n];
+      const int k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
+      my_chunks += k;
+      for (int s = 0; s < k; ++s) {
+        const int k0 = (int)((int64_t)c * s / k), k1 = (int)((int64_t)c * (s + 1) / k);
+        atomicAdd(&sh.bucket[bin_of(n, k0, k1) * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1);
+      }
     }
-  }
-  __syncthreads();
-  {  // descending exclusive scan of the 256 class counts
-    const int cls = kBuckets - 1 - tid;
-    const int32_t v = tid < kBuckets ? sh.bucket[cls] : 0;
-    int32_t tot;
-    const int32_t ex = block_excl_scan(v, &tot, sh);
-    if (tid < kBuckets) sh.bucket[cls] = ex;
+    __syncthreads();
+    // per-bin exclusive scans of the class counts (bins are 256 classes each)
+    for (int x = 0; x < X; ++x) {
+      const int32_t v = tid < kBuckets ? sh.bucket[x * kBuckets + tid] : 0;
+      int32_t tot;
+      const int32_t ex = block_excl_scan(v, &tot, sh);
+      if (tid < kBuckets) sh.bucket[x * kBuckets + tid] = ex;
+      if (tid == 0) sh.bin_count[x] = tot;
+      __syncthreads();
+    }
+    max_count = 0;
+    for (int x = 0; x < X; ++x) max_count = max(max_count, sh.bin_count[x]);
+    if ((int64_t)max_count * X <= a.max_work || X == 1) break;
+    X = 1;  // bins too uneven for the grid: plain heaviest-first order
     __syncthreads();
   }
   for (int n = tid; n < n_items; n += kThreads) {
@@ -190,7 +218,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     const int b = item_b[n], ig = item_g[n], itt = item_t[n];
     for (int s = 0; s < k; ++s) {
       const int k0 = (int)((int64_t)c * s / k), k1 = (int)((int64_t)c * (s + 1) / k);
-      const int pos = atomicAdd(&sh.bucket[size_class(k1 - k0)], 1);
+      const int x = bin_of(n, k0, k1);
+      const int rank = atomicAdd(&sh.bucket[x * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1);
       WorkItem w;
       w.b = b;
       w.g = ig;
@@ -200,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
       w.part = k > 1 ? part_base[n] + s : -1;
       w.pad0 = 0;
       w.pad1 = 0;
-      a.work[pos] = w;
+      a.work[rank * X + x] = w;
     }
     if (k > 1) {
       MergeItem m;
@@ -213,9 +242,22 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
       a.merge[merge_idx[n]] = m;
     }
   }
-  const int64_t n_work = block_sum(my_chunks, sh);
+  // unused slots of shorter bins hold empty items
+  for (int x = 0; x < X; ++x) {
+    for (int rank = sh.bin_count[x] + tid; rank < max_count; rank += kThreads) {
+      WorkItem w;
+      w.b = -1;
+      w.g = w.t = w.kt_begin = w.kt_end = 0;
+      w.part = -1;
+      w.pad0 = w.pad1 = 0;
+      a.work[rank * X + x] = w;
+    }
+  }
+  const int64_t n_chunks = block_sum(my_chunks, sh);
   if (tid == 0) {
-    a.hdr->num_work = (int32_t)n_work;
+    a.hdr->num_work = max_count * X;  // grid slots in use, empty items included
+    a.hdr->num_chunks = (int32_t)n_chunks;
+    a.hdr->xcds = X;
     a.hdr->num_merge = mcarry;
     a.hdr->chunk_tiles = (int32_t)chunk;
     a.hdr->total_tiles = (int32_t)total;
