@@ -116,6 +116,7 @@ def main():
         desc = pkv.make_desc(s["q"], s["k_ext"], s["v_ext"], s["o"], s["k_pool"], s["v_pool"], w.bs,
                              w.num_prefix)
         s["ws"] = torch.empty(pkv.extend_attention_workspace_size(desc), dtype=torch.uint8, device=dev)
+    kernel = pkv.extend_attention_kernel_name(desc)
 
     def step(i):
         s = sets[i % copies]
@@ -170,7 +171,7 @@ def main():
                    "causal_gflop": round(flops / 1e9, 3), "algorithmic_mb": round(algo_bytes / 1e6, 2),
                    "input_copies_rotated": copies, "wall_s_timed": round(wall, 3)},
         "mfma_frac_step": round(flops / (ms_per_step * 1e-3) / 1e12 / peak, 4),
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "ms_per_launch": round(ms_attn, 4),
                      "hbm_gbs_algorithmic": round(algo_bytes / (ms_attn * 1e-3) / 1e9, 1)},
@@ -185,7 +186,7 @@ def kernel_source_sha():
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("attention.hip", "plan.hip"):
+    for f in ("attention.hip", "attention_dl.hip", "plan.hip"):
         with open(os.path.join(ROOT, "paged_kv_extend_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -174,6 +174,13 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
                          void* stream);
 
 /*
+ * Name of the attention kernel symbol that serves `desc` ("attn_dl_kernel" or
+ * "attn_kernel", as profilers list it), or NULL when desc is invalid.  For
+ * matching profiler output; results do not depend on it.
+ */
+const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc);
+
+/*
  * Measurement hook (not needed for results).  pkv_profile_enable(1) clears
  * the record and makes every later extend_attention_fwd call record a HIP
  * event pair on its stream around its attention kernel; 0 stops recording.

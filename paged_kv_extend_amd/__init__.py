@@ -17,6 +17,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_workspace_size",
+           "extend_attention_kernel_name",
            "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "LIB_PATH", "PkvError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -63,6 +64,8 @@ def library() -> ctypes.CDLL:
     lib.pkv_profile_enable.restype = ctypes.c_int
     lib.pkv_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.pkv_profile_read.restype = ctypes.c_int
+    lib.extend_attention_kernel_name.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.extend_attention_kernel_name.restype = ctypes.c_char_p
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.restype = ctypes.c_char_p
     _lib = lib
@@ -179,6 +182,14 @@ def extend_attention_workspace_size(desc: AttnDesc) -> int:
     if n == 0:
         raise PkvError(-1, last_error())
     return int(n)
+
+
+def extend_attention_kernel_name(desc: AttnDesc) -> str:
+    """Symbol name of the attention kernel serving ``desc`` (for profiler output)."""
+    n = library().extend_attention_kernel_name(ctypes.byref(desc))
+    if n is None:
+        raise PkvError(-1, last_error())
+    return n.decode()
 
 
 _ws_cache = {}

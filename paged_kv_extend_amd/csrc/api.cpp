@@ -193,6 +193,12 @@ const char* pkv_last_error(void) { return g_err; }
 
 const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
 
+const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc) {
+  pkv::Tiling t;
+  if (check_desc(desc, &t) != PKV_OK) return nullptr;
+  return pkv::dl_tiling(desc->dtype, desc->lq, desc->lv, &t) ? "attn_dl_kernel" : "attn_kernel";
+}
+
 int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
                              const int32_t* extend_start_loc, const int32_t* extend_seq_lens,
                              const int64_t* extend_kv_indices, int32_t bs, int64_t num_prefix_indices,

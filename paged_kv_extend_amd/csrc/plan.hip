@@ -34,9 +34,11 @@ constexpr int kSeqLds = 8192;  // sequence offsets kept in LDS up to this batch 
 
 struct Shared {
   int32_t wave_tot[kWaves];
+  int32_t wave_tot3[kWaves][3];
   int64_t red[kWaves];
   int32_t bucket[kMaxXcd * kBuckets];
   int32_t bin_count[kMaxXcd];
+  int32_t bin_start[kMaxXcd];
   int32_t seq_base[kSeqLds + 1];
 };
 
@@ -61,6 +63,43 @@ __device__ int32_t block_excl_scan(int32_t v, int32_t* total, Shared& sh) {
   __syncthreads();
   *total = all;
   return before + inc - v;
+}
+
+// Exclusive block-wide scans of three ints per thread in one pass.
+__device__ int3 block_excl_scan3(int3 v, int3* total, Shared& sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int3 inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ux = __shfl_up(inc.x, off), uy = __shfl_up(inc.y, off), uz = __shfl_up(inc.z, off);
+    if (lane >= off) {
+      inc.x += ux;
+      inc.y += uy;
+      inc.z += uz;
+    }
+  }
+  if (lane == 63) {
+    sh.wave_tot3[w][0] = inc.x;
+    sh.wave_tot3[w][1] = inc.y;
+    sh.wave_tot3[w][2] = inc.z;
+  }
+  __syncthreads();
+  int3 before = make_int3(0, 0, 0), all = make_int3(0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int tx = sh.wave_tot3[i][0], ty = sh.wave_tot3[i][1], tz = sh.wave_tot3[i][2];
+    if (i < w) {
+      before.x += tx;
+      before.y += ty;
+      before.z += tz;
+    }
+    all.x += tx;
+    all.y += ty;
+    all.z += tz;
+  }
+  __syncthreads();
+  *total = all;
+  return make_int3(before.x + inc.x - v.x, before.y + inc.y - v.y, before.z + inc.z - v.z);
 }
 
 __device__ int64_t block_sum(int64_t v, Shared& sh) {
@@ -159,15 +198,14 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
       c = cost_of[n];
       k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
     }
-    int32_t ptot, mtot, ctot;
-    const int32_t pex = block_excl_scan(k > 1 ? k : 0, &ptot, sh);
-    const int32_t mex = block_excl_scan(k > 1 ? 1 : 0, &mtot, sh);
-    const int32_t cex = block_excl_scan(c, &ctot, sh);
+    int3 tot;
+    const int3 ex = block_excl_scan3(make_int3(k > 1 ? k : 0, k > 1 ? 1 : 0, c), &tot, sh);
     if (n < n_items) {
-      part_base[n] = pcarry + pex;
-      merge_idx[n] = mcarry + mex;
-      cum_cost[n] = ccarry + cex;
+      part_base[n] = pcarry + ex.x;
+      merge_idx[n] = mcarry + ex.y;
+      cum_cost[n] = ccarry + ex.z;
     }
+    const int32_t ptot = tot.x, mtot = tot.y, ctot = tot.z;
     pcarry += ptot;
     mcarry += mtot;
     ccarry += ctot;
@@ -197,13 +235,21 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
       }
     }
     __syncthreads();
-    // per-bin exclusive scans of the class counts (bins are 256 classes each)
-    for (int x = 0; x < X; ++x) {
-      const int32_t v = tid < kBuckets ? sh.bucket[x * kBuckets + tid] : 0;
+    // one exclusive scan over all (bin, class) counters, two per thread; a bin's
+    // ranks are offsets from its first counter's scan value
+    {
+      const int i0 = 2 * tid;
+      const int32_t v0 = i0 < X * kBuckets ? sh.bucket[i0] : 0;
+      const int32_t v1 = i0 + 1 < X * kBuckets ? sh.bucket[i0 + 1] : 0;
       int32_t tot;
-      const int32_t ex = block_excl_scan(v, &tot, sh);
-      if (tid < kBuckets) sh.bucket[x * kBuckets + tid] = ex;
-      if (tid == 0) sh.bin_count[x] = tot;
+      const int32_t ex = block_excl_scan(v0 + v1, &tot, sh);
+      if (i0 < X * kBuckets) sh.bucket[i0] = ex;
+      if (i0 + 1 < X * kBuckets) sh.bucket[i0 + 1] = ex + v0;
+      __syncthreads();
+      if (tid < X) {
+        sh.bin_start[tid] = sh.bucket[tid * kBuckets];
+        sh.bin_count[tid] = (tid + 1 < X ? sh.bucket[(tid + 1) * kBuckets] : tot) - sh.bucket[tid * kBuckets];
+      }
       __syncthreads();
     }
     max_count = 0;
@@ -219,7 +265,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     for (int s = 0; s < k; ++s) {
       const int k0 = (int)((int64_t)c * s / k), k1 = (int)((int64_t)c * (s + 1) / k);
       const int x = bin_of(n, k0, k1);
-      const int rank = atomicAdd(&sh.bucket[x * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1);
+      const int rank = atomicAdd(&sh.bucket[x * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1) -
+                       sh.bin_start[x];
       WorkItem w;
       w.b = b;
       w.g = ig;

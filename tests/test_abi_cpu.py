@@ -29,6 +29,18 @@ def test_exports_every_declared_function():
     assert "gfx950" in pkv.version()
 
 
+def test_kernel_name_per_variant():
+    assert pkv.extend_attention_kernel_name(desc()) == "attn_dl_kernel"
+    assert pkv.extend_attention_kernel_name(desc(lq=576, lv=512, num_kv_heads=1, q_stride_head=576,
+                                                 q_stride_tok=32 * 576, ke_stride_tok=576, ke_stride_head=576,
+                                                 kp_stride_slot=576, kp_stride_head=576, o_stride_tok=32 * 512,
+                                                 o_stride_head=512, ve_stride_tok=576, ve_stride_head=576,
+                                                 vp_stride_slot=576, vp_stride_head=576)) == "attn_kernel"
+    assert pkv.extend_attention_kernel_name(desc(dtype=1, lq=64, lv=64)) == "attn_kernel"
+    with pytest.raises(pkv.PkvError):
+        pkv.extend_attention_kernel_name(desc(lq=80, lv=80))
+
+
 def desc(**kw):
     d = pkv.AttnDesc()
     base = dict(dtype=0, bs=2, num_q_heads=32, num_kv_heads=8, lq=128, lv=128, total_q_tokens=100,
