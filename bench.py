@@ -116,7 +116,7 @@ def main():
         desc = pkv.make_desc(s["q"], s["k_ext"], s["v_ext"], s["o"], s["k_pool"], s["v_pool"], w.bs,
                              w.num_prefix)
         s["ws"] = torch.empty(pkv.extend_attention_workspace_size(desc), dtype=torch.uint8, device=dev)
-    kernel = pkv.extend_attention_kernel_name(desc)
+    kernel = pkv.extend_attention_kernel_name(desc, s["k_ext"], s["v_ext"], s["k_pool"], s["v_pool"])
 
     def step(i):
         s = sets[i % copies]

@@ -174,11 +174,14 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
                          void* stream);
 
 /*
- * Name of the attention kernel symbol that serves `desc` ("attn_dl_kernel" or
- * "attn_kernel", as profilers list it), or NULL when desc is invalid.  For
- * matching profiler output; results do not depend on it.
+ * Name of the attention kernel symbol that serves a call with `desc` and these
+ * K/V base pointers ("attn_dl_kernel" or "attn_kernel", as profilers list it),
+ * or NULL when desc is invalid.  The pointers are only compared (V inside K
+ * selects a variant), never dereferenced.  For matching profiler output;
+ * results do not depend on it.
  */
-const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc);
+const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc, const void* k_extend, const void* v_extend,
+                                         const void* k_pool, const void* v_pool);
 
 /*
  * Measurement hook (not needed for results).  pkv_profile_enable(1) clears

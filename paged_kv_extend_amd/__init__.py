@@ -64,7 +64,7 @@ def library() -> ctypes.CDLL:
     lib.pkv_profile_enable.restype = ctypes.c_int
     lib.pkv_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.pkv_profile_read.restype = ctypes.c_int
-    lib.extend_attention_kernel_name.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.extend_attention_kernel_name.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P]
     lib.extend_attention_kernel_name.restype = ctypes.c_char_p
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.restype = ctypes.c_char_p
@@ -184,9 +184,12 @@ def extend_attention_workspace_size(desc: AttnDesc) -> int:
     return int(n)
 
 
-def extend_attention_kernel_name(desc: AttnDesc) -> str:
-    """Symbol name of the attention kernel serving ``desc`` (for profiler output)."""
-    n = library().extend_attention_kernel_name(ctypes.byref(desc))
+def extend_attention_kernel_name(desc: AttnDesc, k_extend=None, v_extend=None, k_pool=None,
+                                 v_pool=None) -> str:
+    """Symbol name of the attention kernel serving ``desc`` with these K/V tensors
+    (for profiler output; V sharing K's storage selects a variant)."""
+    n = library().extend_attention_kernel_name(ctypes.byref(desc), _ptr(k_extend), _ptr(v_extend), _ptr(k_pool),
+                                               _ptr(v_pool))
     if n is None:
         raise PkvError(-1, last_error())
     return n.decode()

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <unordered_map>
 #include <vector>
@@ -39,13 +40,23 @@ constexpr int kMinChunkTiles = 8;           // never split an item below this ma
 constexpr size_t kPartialBytes = 64u << 20;  // budget for split partial states
 constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dealt round-robin
 
+// V is the first lv columns of K (same base pointers and strides), as in the
+// MLA layout: the direct-load kernel then reads V out of the K tile.
+bool v_inside_k(const pkv_attn_desc_t& d, const void* k_extend, const void* v_extend, const void* k_pool,
+                const void* v_pool) {
+  return d.lv <= d.lq && k_extend == v_extend && k_pool == v_pool && d.ke_stride_tok == d.ve_stride_tok &&
+         d.ke_stride_head == d.ve_stride_head && d.kp_stride_slot == d.vp_stride_slot &&
+         d.kp_stride_head == d.vp_stride_head;
+}
+
 // Resident attention workgroups on the current device, cached per (device, variant).
-int resident_slots(int dtype, int lq, int lv) {
+int resident_slots(int dtype, int lq, int lv, bool v_in_k) {
   static std::mutex mu;
   static std::unordered_map<long long, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  const long long key = ((long long)dev << 32) | ((long long)dtype << 24) | ((long long)lq << 12) | lv;
+  const long long key = ((long long)dev << 33) | ((long long)v_in_k << 32) | ((long long)dtype << 24) |
+                        ((long long)lq << 12) | lv;
   std::lock_guard<std::mutex> lk(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
@@ -53,11 +64,16 @@ int resident_slots(int dtype, int lq, int lv) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   pkv::Tiling t;
-  const int per_cu = pkv::dl_tiling(dtype, lq, lv, &t) ? pkv::dl_blocks_per_cu(lq, lv)
-                                                        : pkv::attention_blocks_per_cu(dtype, lq, lv);
+  const int per_cu = pkv::dl_tiling(dtype, lq, lv, v_in_k, &t) ? pkv::dl_blocks_per_cu(lq, lv, v_in_k)
+                                                                : pkv::attention_blocks_per_cu(dtype, lq, lv);
   const int slots = cus * per_cu;
   cache[key] = slots;
   return slots;
+}
+
+// Row and key tiling of the kernel serving (dtype, lq, lv) with or without V inside K.
+bool tiling_for(const pkv_attn_desc_t& d, bool v_in_k, pkv::Tiling* t) {
+  return pkv::dl_tiling(d.dtype, d.lq, d.lv, v_in_k, t) || pkv::attn_tiling(d.dtype, d.lq, d.lv, t);
 }
 
 // Sizes derived from the descriptor; returns 0 and sets the error when invalid.
@@ -71,7 +87,9 @@ int check_desc(const pkv_attn_desc_t* d, pkv::Tiling* t) {
   if (d->num_q_heads % d->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
                 d->num_kv_heads);
-  if (!pkv::dl_tiling(d->dtype, d->lq, d->lv, t) && !pkv::attn_tiling(d->dtype, d->lq, d->lv, t))
+  // every head-dim pair that a V-inside-K variant serves has a general
+  // variant too, so the general tiling decides what is supported
+  if (!tiling_for(*d, false, t))
     return fail(PKV_ERR_UNSUPPORTED, "head dims (lq %d, lv %d) not supported for dtype %d", d->lq, d->lv,
                 d->dtype);
   if (d->total_q_tokens < 0 || d->num_prefix_indices < 0 || d->pool_slots < 0)
@@ -193,10 +211,12 @@ const char* pkv_last_error(void) { return g_err; }
 
 const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
 
-const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc) {
+const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc, const void* k_extend, const void* v_extend,
+                                         const void* k_pool, const void* v_pool) {
   pkv::Tiling t;
   if (check_desc(desc, &t) != PKV_OK) return nullptr;
-  return pkv::dl_tiling(desc->dtype, desc->lq, desc->lv, &t) ? "attn_dl_kernel" : "attn_kernel";
+  const bool vk = v_inside_k(*desc, k_extend, v_extend, k_pool, v_pool);
+  return pkv::dl_tiling(desc->dtype, desc->lq, desc->lv, vk, &t) ? "attn_dl_kernel" : "attn_kernel";
 }
 
 int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
@@ -230,7 +250,12 @@ size_t extend_attention_workspace_size(const pkv_attn_desc_t* desc) {
   pkv::Tiling t;
   if (check_desc(desc, &t) != PKV_OK) return 0;
   g_err[0] = '\0';
-  return ws_layout(desc, t, plan_bounds(desc, t)).total;
+  // the kernel, and with it the row tiling, may depend on whether V lies
+  // inside K, which only the call shows: size for both
+  size_t total = ws_layout(desc, t, plan_bounds(desc, t)).total;
+  pkv::Tiling tv;
+  if (tiling_for(*desc, true, &tv)) total = std::max(total, ws_layout(desc, tv, plan_bounds(desc, tv)).total);
+  return total;
 }
 
 int extend_attention_fwd(const void* q_extend, const void* k_extend, const void* v_extend, void* o,
@@ -254,6 +279,8 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(PKV_ERR_UNSUPPORTED, "tensor base pointers must be 16-byte aligned");
 
+  const bool vk = v_inside_k(d, k_extend, v_extend, k_pool, v_pool);
+  if (vk) tiling_for(d, true, &t);  // the tiling of the kernel that serves this call
   const pkv::PlanBounds pb = plan_bounds(&d, t);
   const pkv::WsLayout wl = ws_layout(&d, t, pb);
   if (!workspace || workspace_bytes < wl.total)
@@ -274,7 +301,7 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   pa.group = group;
   pa.bm = t.bm;
   pa.bn = t.bn;
-  pa.slots = resident_slots(d.dtype, d.lq, d.lv);
+  pa.slots = resident_slots(d.dtype, d.lq, d.lv, vk);
   pa.min_chunk = kMinChunkTiles;
   pa.xcds = kXcds;
   pa.max_work = pb.max_work;
@@ -328,8 +355,8 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   const auto ev = profile_slot();
   if (ev.first) (void)hipEventRecord(ev.first, s);
   pkv::Tiling td;
-  e = pkv::dl_tiling(d.dtype, d.lq, d.lv, &td) ? pkv::launch_dl(d.lq, d.lv, a, pb.max_work, s)
-                                               : pkv::launch_attention(d.dtype, d.lq, d.lv, a, pb.max_work, s);
+  e = pkv::dl_tiling(d.dtype, d.lq, d.lv, vk, &td) ? pkv::launch_dl(d.lq, d.lv, vk, a, pb.max_work, s)
+                                                   : pkv::launch_attention(d.dtype, d.lq, d.lv, a, pb.max_work, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   if (ev.second) (void)hipEventRecord(ev.second, s);
   e = pkv::launch_merge(d.dtype, d.lv, a, t.bm, pb.max_merge, s);

@@ -1,5 +1,6 @@
-// Extend-attention kernel for bf16 head dims 64, 128 and 256 on gfx950 with
-// K/V tiles loaded straight from global memory into LDS.
+// Extend-attention kernel for bf16 head dims 64, 128, 256 and the 576/512
+// latent+rope layout on gfx950, with K/V tiles loaded straight from global
+// memory into LDS.
 //
 // Same computation as attention.hip (page "extend_attention.py",
 // _fwd_kernel_unified: scale, optional soft-cap, mask j <= P + i, online
@@ -19,6 +20,9 @@
 //    MFMA operand reads of K and the transposing reads of V stay free of bank
 //    conflicts.
 //  * Waits on the loads are explicit vmcnt counts before a bare s_barrier.
+//  * When V is the first Lv columns of K (the MLA layout on page
+//    "cpu_graph_runner.py", qkv_proj_with_rope: v = k.narrow(-1, 0, lv)), only
+//    the K tile is loaded and the V^T operand is read from it.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -29,6 +33,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <class T>
 using gptr = const __attribute__((address_space(1))) T*;
@@ -50,67 +55,116 @@ __device__ __forceinline__ float pair_sum(float v) {
 
 // s_waitcnt vmcnt(0) lgkmcnt(0) (gfx9 encoding: vmcnt [3:0],[15:14]; expcnt [6:4]; lgkmcnt [11:8])
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0x7 << 4); }
+// s_waitcnt lgkmcnt(0) only: LDS traffic done, global loads may stay in flight
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int LQ, int LV, int BN>
+template <int LQ, int LV, int BN, bool VK>
 struct DlCfg {
-  static constexpr int NW = 4;
+  // Waves per row group.  When one wave cannot hold both its Q^T operand
+  // (LQ / 4 registers) and its O^T accumulator (LV / 2 registers), two waves
+  // share a row group: each holds half of the Q dims and half of the O
+  // columns, and the two halves of S^T are summed through LDS.  Half h owns
+  // chunks 4h..4h+3 of every 8-chunk group of a row (Q/K dims) and the
+  // 32-column output blocks 2m + h, so that inside a swizzle group its
+  // operand addresses differ from one per-lane base by constants only.
+  static constexpr int SPLIT = LQ / 4 + LV / 2 > 320 ? 2 : 1;
+  // 32-row groups per workgroup.  Split: 2, i.e. 4 waves and one wave per
+  // SIMD, which leaves each wave the whole 512-entry register file (its Q^T
+  // and O^T halves alone take ~200 entries).
+  static constexpr int RG = SPLIT > 1 ? 2 : 4;
+  static constexpr int NW = RG * SPLIT;
   static constexpr int NT = NW * 64;
-  static constexpr int BM = NW * 32;
-  static constexpr int CK = LQ / 8;  // 16-byte chunks per row
+  static constexpr int BM = RG * 32;
+  static constexpr int QD = LQ / SPLIT;  // Q dims per wave
+  static constexpr int VD = LV / SPLIT;  // O columns per wave
+  static constexpr int CK = LQ / 8;      // 16-byte chunks per K row
   static constexpr int CV = LV / 8;
+  static constexpr bool WIDE = CK == 72;  // 576-element rows: swizzle inside 8-chunk groups
   // rows sharing one 256-byte window of the 64 LDS banks
   static constexpr int RPK = CK >= 16 ? 1 : 16 / CK;
   static constexpr int RPV = CV >= 16 ? 1 : 16 / CV;
   static constexpr int SWK = CK >= 16 ? 16 : CK;     // distinct K swizzles
   static constexpr int SWV = CV >= 16 ? 4 : CV / 4;  // distinct V swizzles (multiples of 4 chunks)
   static constexpr int K_BYTES = BN * LQ * 2;
-  static constexpr int V_BYTES = BN * LV * 2;
+  static constexpr int V_BYTES = VK ? 0 : BN * LV * 2;
+  static constexpr int V_PITCH = VK ? LQ * 2 : LV * 2;  // bytes between V rows in LDS
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
-  static constexpr int K_LOADS = K_BYTES / 1024 / NW;  // 1 KB load instructions per wave per tile
-  static constexpr int V_LOADS = V_BYTES / 1024 / NW;
-  static_assert(CK == 8 || CK == 16 || CK == 32, "lq");
-  static_assert(CV == 8 || CV == 16 || CV == 32, "lv");
-  static_assert(K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0, "whole loads per wave");
+  static constexpr int K_CHUNKS = K_BYTES / 1024;  // 1 KB load instructions per tile
+  static constexpr int V_CHUNKS = V_BYTES / 1024;
+  static constexpr int K_LOADS = (K_CHUNKS + NW - 1) / NW;  // per wave (the last round may be partial)
+  static constexpr int V_LOADS = (V_CHUNKS + NW - 1) / NW;
+  static constexpr int XCH_BYTES = SPLIT > 1 ? NW * BN * 32 * 4 : 0;  // S^T halves exchanged
+  static_assert(CK == 8 || CK == 16 || CK == 32 || CK == 72, "lq");
+  static_assert(VK ? LV <= LQ : (CV == 8 || CV == 16 || CV == 32), "lv");
+  static_assert(!WIDE || VK, "576-wide rows only with V inside K");
+  static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "whole 1 KB loads");
+  static_assert(QD % 16 == 0 && VD % 32 == 0, "split");
+  static_assert(SPLIT == 1 || WIDE, "the split interleaves halves inside 8-chunk swizzle groups");
   static_assert(BN % 32 == 0 && BN <= 64, "key tile");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r.  K: the 32 rows read at
 // one logical chunk by an MFMA operand load spread over all 16 bank groups.
 // V: the 4 rows x 4 chunks of one transposing read spread over all 16 groups.
+// 576-wide rows (72 chunks, pitch = 8 groups mod 16): the XOR stays inside
+// each group of 8 chunks, g(s) = 4 (s & 1) + (s >> 1) over s = (r / 2) % 8,
+// which satisfies both read patterns on the one tile that holds K and V.
+__device__ __forceinline__ int wide_xor(int r) {
+  const int s = (r >> 1) & 7;
+  return ((s & 1) << 2) | (s >> 1);
+}
 template <class C>
-__device__ __forceinline__ int swz_k(int r, int c) { return c ^ ((r / C::RPK) % C::SWK); }
+__device__ __forceinline__ int swz_k(int r, int c) {
+  if constexpr (C::WIDE) {
+    return (c & ~7) | ((c & 7) ^ wide_xor(r));
+  } else {
+    return c ^ ((r / C::RPK) % C::SWK);
+  }
+}
 template <class C>
-__device__ __forceinline__ int swz_v(int r, int c) { return c ^ (4 * ((r / C::RPV) % C::SWV)); }
+__device__ __forceinline__ int swz_v(int r, int c) {
+  if constexpr (C::WIDE) {
+    return swz_k<C>(r, c);
+  } else {
+    return c ^ (4 * ((r / C::RPV) % C::SWV));
+  }
+}
 
-template <int LQ, int LV, int BN, bool CAP, int MINB>
-__global__ __launch_bounds__(256, MINB) void attn_dl_kernel(AttnArgs a) {
-  using C = DlCfg<LQ, LV, BN>;
+template <int LQ, int LV, int BN, bool VK, bool CAP, int MINB>
+__global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK>::NT), MINB) void attn_dl_kernel(AttnArgs a) {
+  using C = DlCfg<LQ, LV, BN, VK>;
   using T = uint16_t;
-  constexpr int NT = C::NT, BM = C::BM;
+  constexpr int BM = C::BM;
   constexpr int NKB = BN / 32;
-  constexpr int NQ = LQ / 16;
-  constexpr int NDB = LV / 32;
+  constexpr int NQ = C::QD / 16;
+  constexpr int NDB = C::VD / 32;
 
-  __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE_BYTES + C::XCH_BYTES];
   __shared__ gptr<T> kptr[2][BN];
   __shared__ gptr<T> vptr[2][BN];
-  (void)NT;
 
   if ((int)blockIdx.x >= a.hdr->num_work) return;
   const WorkItem it = a.work[blockIdx.x];
   if (it.b < 0) return;  // empty placement slot
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int rg = wv % C::RG, half = wv / C::RG;  // row group; which half of Q dims / O columns
   const int qi = lane & 31, hi = lane >> 5;
+  // first 16-byte chunk of contraction step ks (its lanes hi = 0, 1 take ch, ch + 1)
+  auto qk_chunk = [&](int ks) __attribute__((always_inline)) {
+    return C::SPLIT > 1 ? 8 * (ks >> 1) + 4 * half + 2 * (ks & 1) : 2 * ks;
+  };
+  // 32-column output block of this wave's block db
+  auto o_block = [&](int db) __attribute__((always_inline)) { return C::SPLIT > 1 ? 2 * db + half : db; };
   const int G = a.group;
   const int b = it.b, g = it.g;
   const int q0 = a.qo_indptr[b], E = a.qo_indptr[b + 1] - q0;
   const int kvs = a.kv_indptr[b], P = a.kv_indptr[b + 1] - kvs;
   const int R = E * G;
 
-  const int r = it.t * BM + wv * 32 + qi;
+  const int r = it.t * BM + rg * 32 + qi;
   const bool valid = r < R;
   const int lim = valid ? P + r / G : -1;  // last visible key of this lane's row
-  const int rw0 = it.t * BM + wv * 32;
+  const int rw0 = it.t * BM + rg * 32;
   const bool wave_live = rw0 < R;
   const int i_lo_w = wave_live ? rw0 / G : 0;
   const int i_hi_w = wave_live ? min(R - 1, rw0 + 31) / G : 0;
@@ -131,7 +185,8 @@ __global__ __launch_bounds__(256, MINB) void attn_dl_kernel(AttnArgs a) {
                    (int64_t)(g * G + (valid ? r % G : 0)) * a.q_sh;
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) {
-      const u32x4 v = valid ? *(gptr<u32x4>)(qrow + ks * 16 + hi * 8) : u32x4{0u, 0u, 0u, 0u};
+      const int ch = qk_chunk(ks) + hi;
+      const u32x4 v = valid ? *(gptr<u32x4>)(qrow + ch * 8) : u32x4{0u, 0u, 0u, 0u};
       qr[ks] = __builtin_bit_cast(bf16x8, v ^ flip);
     }
   }
@@ -168,7 +223,9 @@ __global__ __launch_bounds__(256, MINB) void attn_dl_kernel(AttnArgs a) {
     char* stage = lds + (kt & 1) * C::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < C::K_LOADS; ++i) {
-      const int base = (i * C::NW + wv) * 1024;
+      const int li = i * C::NW + wv;
+      if (C::K_CHUNKS % C::NW != 0 && li >= C::K_CHUNKS) break;  // wave-uniform
+      const int base = li * 1024;
       const int off = base + lane * 16;
       const int row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
       __builtin_amdgcn_global_load_lds((gptr<void>)(kptr[kt & 1][row] + swz_k<C>(row, p) * 8),
@@ -176,13 +233,32 @@ __global__ __launch_bounds__(256, MINB) void attn_dl_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < C::V_LOADS; ++i) {
-      const int base = (i * C::NW + wv) * 1024;
+      const int li = i * C::NW + wv;
+      if (C::V_CHUNKS % C::NW != 0 && li >= C::V_CHUNKS) break;
+      const int base = li * 1024;
       const int off = base + lane * 16;
       const int row = off / (LV * 2), p = (off % (LV * 2)) / 16;
       __builtin_amdgcn_global_load_lds((gptr<void>)(vptr[kt & 1][row] + swz_v<C>(row, p) * 8),
                                        (lptr<void>)(stage + C::K_BYTES + base), 16, 0, 0);
     }
   };
+
+  // wide rows: per-lane byte offsets of the operand reads inside a stage.
+  // K: row qi, chunk 4 half + 2 m + hi of a group (m = ks & 1).  V^T: rows
+  // key0 + 8 x, chunk 4 half + cofs / 8 of a group; all other rows and
+  // groups the wave reads add multiples of 32 rows, 16 rows or 128 bytes,
+  // which keep the swizzle.
+  int k_lane[2] = {0, 0}, v_lane[2] = {0, 0};
+  if constexpr (C::WIDE) {
+    const int key0 = 4 * hi + ((lane & 15) >> 2);
+    const int cofs = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      k_lane[m] = qi * LQ * 2 + ((4 * half + 2 * m + hi) ^ wide_xor(qi)) * 16;
+      const int vr = key0 + 8 * m;
+      v_lane[m] = vr * C::V_PITCH + ((4 * half + cofs / 8) ^ wide_xor(vr)) * 16 + (cofs % 8) * 2;
+    }
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -208,25 +284,69 @@ __global__ __launch_bounds__(256, MINB) void attn_dl_kernel(AttnArgs a) {
     if (kt + 1 < kt1) issue_tile(kt + 1);
 
     const int j0 = kt * BN;
-    if (wave_live && j0 <= P + i_hi_w) {
-      const bool need_mask = j0 + BN - 1 > P + i_lo_w;
-      const char* Ks = lds + (kt & 1) * C::STAGE_BYTES;
-      const char* Vs = Ks + C::K_BYTES;
+    const bool act = wave_live && j0 <= P + i_hi_w;  // same for both waves of a row group
+    const char* Ks = lds + (kt & 1) * C::STAGE_BYTES;
+    const char* Vs = VK ? Ks : Ks + C::K_BYTES;
 
-      // S^T = K Q^T
-      f32x16 s[NKB];
+    // S^T = K Q^T (this wave's Q dims)
+    f32x16 s[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    if (act) {
 #pragma unroll
       for (int ks = 0; ks < NQ; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const int row = kb * 32 + qi;
-          const bf16x8 kv = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(Ks + row * LQ * 2 + swz_k<C>(row, 2 * ks + hi) * 16));
+          const char* ka;
+          if constexpr (C::WIDE) {
+            // rows kb*32 + qi share qi's swizzle; the group offset is a constant
+            ka = Ks + k_lane[ks & 1] + kb * 32 * LQ * 2 + (ks >> 1) * 128;
+          } else {
+            const int row = kb * 32 + qi;
+            ka = Ks + row * LQ * 2 + swz_k<C>(row, qk_chunk(ks) + hi) * 16;
+          }
+          const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ka));
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qr[ks], s[kb], 0, 0, 0);
         }
       }
+    }
+    if constexpr (C::SPLIT > 1) {
+      // the two halves of S^T meet in LDS; a + b == b + a, so both waves of
+      // the pair hold the same S^T bit for bit and take the same softmax
+      // decisions.  The buffer is free again at the next tile's barrier,
+      // which every wave reaches only after its reads have returned.
+      f32x4* xw = reinterpret_cast<f32x4*>(lds + 2 * C::STAGE_BYTES) + wv * (NKB * 4 * 64);
+      const f32x4* xr =
+          reinterpret_cast<const f32x4*>(lds + 2 * C::STAGE_BYTES) + ((wv + C::RG) % C::NW) * (NKB * 4 * 64);
+      if (act) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            xw[(kb * 4 + q4) * 64 + lane] =
+                f32x4{s[kb][4 * q4], s[kb][4 * q4 + 1], s[kb][4 * q4 + 2], s[kb][4 * q4 + 3]};
+      }
+      wait_lds();
+      __builtin_amdgcn_s_barrier();
+      if (act) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          f32x16 o;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v = xr[(kb * 4 + q4) * 64 + lane];
+            o[4 * q4] = v[0];
+            o[4 * q4 + 1] = v[1];
+            o[4 * q4 + 2] = v[2];
+            o[4 * q4 + 3] = v[3];
+          }
+          s[kb] += o;
+        }
+      }
+    }
+
+    if (act) {
+      const bool need_mask = j0 + BN - 1 > P + i_lo_w;
 
       // soft-cap (base-2 units), mask of the diagonal tiles, row max
       if constexpr (CAP) {
@@ -271,11 +391,11 @@ __global__ __launch_bounds__(256, MINB) void attn_dl_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int hf = 0; hf < 2; ++hf) {
           bf16x8 pb;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float x = s[kb][8 * half + e];
+            const float x = s[kb][8 * hf + e];
             const float p = CAP ? fast_exp2(x - m_sub) : fast_exp2(fmaf(x, a.scale_log2, -m_sub));
             pb[e] = (__bf16)p;
           }
@@ -283,12 +403,19 @@ __global__ __launch_bounds__(256, MINB) void attn_dl_kernel(AttnArgs a) {
           l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones, l_run, false);
           l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones, l_run, false);
           l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones, l_run, false);
-          const int r0 = kb * 32 + 16 * half + key0, r1 = r0 + 8;
+          const int r0 = kb * 32 + 16 * hf + key0, r1 = r0 + 8;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const int col = db * 32 + cofs;
-            const char* a0 = Vs + r0 * LV * 2 + swz_v<C>(r0, col / 8) * 16 + (col % 8) * 2;
-            const char* a1 = Vs + r1 * LV * 2 + swz_v<C>(r1, col / 8) * 16 + (col % 8) * 2;
+            const char *a0, *a1;
+            if constexpr (C::WIDE) {
+              const int cst = (kb * 32 + 16 * hf) * C::V_PITCH + db * 128;
+              a0 = Vs + v_lane[0] + cst;
+              a1 = Vs + v_lane[1] + cst;
+            } else {
+              const int col = o_block(db) * 32 + cofs;
+              a0 = Vs + r0 * C::V_PITCH + swz_v<C>(r0, col / 8) * 16 + (col % 8) * 2;
+              a1 = Vs + r1 * C::V_PITCH + swz_v<C>(r1, col / 8) * 16 + (col % 8) * 2;
+            }
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr<i16x4>)(a0));
             const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr<i16x4>)(a1));
             const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -311,7 +438,7 @@ __global__ __launch_bounds__(256, MINB) void attn_dl_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hi;
+        const int d = o_block(db) * 32 + 8 * g4 + 4 * hi;
         bf16x4 ov;
         ov[0] = (__bf16)(acc[db][4 * g4] * inv);
         ov[1] = (__bf16)(acc[db][4 * g4 + 1] * inv);
@@ -321,73 +448,77 @@ __global__ __launch_bounds__(256, MINB) void attn_dl_kernel(AttnArgs a) {
       }
     }
   } else {
-    const int64_t prow = (int64_t)it.part * BM + wv * 32 + qi;
+    const int64_t prow = (int64_t)it.part * BM + rg * 32 + qi;
     float* pa = a.part_acc + prow * LV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hi;
+        const int d = o_block(db) * 32 + 8 * g4 + 4 * hi;
         *reinterpret_cast<float4*>(pa + d) =
             make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
       }
     }
-    if (hi == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref, l_tot);
+    if (hi == 0 && half == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref, l_tot);
   }
 }
 
-template <int LQ, int LV, int BN, int MINB>
+template <int LQ, int LV, int BN, bool VK, int MINB>
 hipError_t launch_dl_t(const AttnArgs& a, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (a.use_cap)
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, true, MINB>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, true, MINB>), dim3((unsigned)grid),
+                       dim3(DlCfg<LQ, LV, BN, VK>::NT), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, false, MINB>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, false, MINB>), dim3((unsigned)grid),
+                       dim3(DlCfg<LQ, LV, BN, VK>::NT), 0, s, a);
   return hipGetLastError();
 }
 
-template <int LQ, int LV, int BN, int MINB>
+template <int LQ, int LV, int BN, bool VK, int MINB>
 int dl_occupancy_t() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, false, MINB>), 256, 0) != hipSuccess)
+          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, VK, false, MINB>), DlCfg<LQ, LV, BN, VK>::NT,
+          0) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
 }
 
-// bf16 (lq, lv) pairs served here: key-tile width and workgroups per CU
-#define PKV_DL_VARIANTS(X) \
-  X(64, 64, 64, 2)         \
-  X(128, 128, 64, 2)       \
-  X(256, 256, 32, 1)
+// bf16 variants served here: (lq, lv, key tile, V inside K, workgroups per CU)
+#define PKV_DL_VARIANTS(X)      \
+  X(64, 64, 64, false, 2)       \
+  X(128, 128, 64, false, 2)     \
+  X(256, 256, 32, false, 1)     \
+  X(576, 512, 32, true, 1)
 
 }  // namespace
 
-bool dl_tiling(int dtype, int lq, int lv, Tiling* t) {
+bool dl_tiling(int dtype, int lq, int lv, bool v_in_k, Tiling* t) {
   if (dtype != 0) return false;
-#define PKV_DT(Q, V, N, M)           \
-  if (lq == Q && lv == V) {          \
-    t->bm = DlCfg<Q, V, N>::BM;      \
-    t->bn = N;                       \
-    t->threads = 256;                \
-    return true;                     \
+#define PKV_DT(Q, V, N, VK, M)                          \
+  if (lq == Q && lv == V && (!VK || v_in_k)) {          \
+    t->bm = DlCfg<Q, V, N, VK>::BM;                     \
+    t->bn = N;                                          \
+    t->threads = DlCfg<Q, V, N, VK>::NT;                \
+    return true;                                        \
   }
   PKV_DL_VARIANTS(PKV_DT)
 #undef PKV_DT
   return false;
 }
 
-hipError_t launch_dl(int lq, int lv, const AttnArgs& a, int64_t grid, hipStream_t s) {
-#define PKV_DLL(Q, V, N, M) \
-  if (lq == Q && lv == V) return launch_dl_t<Q, V, N, M>(a, grid, s);
+hipError_t launch_dl(int lq, int lv, bool v_in_k, const AttnArgs& a, int64_t grid, hipStream_t s) {
+#define PKV_DLL(Q, V, N, VK, M) \
+  if (lq == Q && lv == V && (!VK || v_in_k)) return launch_dl_t<Q, V, N, VK, M>(a, grid, s);
   PKV_DL_VARIANTS(PKV_DLL)
 #undef PKV_DLL
   return hipErrorInvalidValue;
 }
 
-int dl_blocks_per_cu(int lq, int lv) {
-#define PKV_DLO(Q, V, N, M) \
-  if (lq == Q && lv == V) return dl_occupancy_t<Q, V, N, M>();
+int dl_blocks_per_cu(int lq, int lv, bool v_in_k) {
+#define PKV_DLO(Q, V, N, VK, M) \
+  if (lq == Q && lv == V && (!VK || v_in_k)) return dl_occupancy_t<Q, V, N, VK, M>();
   PKV_DL_VARIANTS(PKV_DLO)
 #undef PKV_DLO
   return 1;

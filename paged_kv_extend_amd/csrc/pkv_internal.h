@@ -112,9 +112,10 @@ hipError_t launch_index_build(const int32_t* prefix_kv_indptr, const int64_t* pr
                               int32_t* prefix_lens, hipStream_t s);
 // Workgroups of the attention kernel resident per CU (from the occupancy API).
 int attention_blocks_per_cu(int dtype, int lq, int lv);
-// The direct-to-LDS kernel (bf16, head dims 64, 128, 256); preferred when it applies.
-bool dl_tiling(int dtype, int lq, int lv, Tiling* t);
-hipError_t launch_dl(int lq, int lv, const AttnArgs& a, int64_t grid, hipStream_t s);
-int dl_blocks_per_cu(int lq, int lv);
+// The direct-to-LDS kernel (bf16, head dims 64, 128, 256, and 576/512 when V is
+// the first lv columns of K); preferred when it applies.
+bool dl_tiling(int dtype, int lq, int lv, bool v_in_k, Tiling* t);
+hipError_t launch_dl(int lq, int lv, bool v_in_k, const AttnArgs& a, int64_t grid, hipStream_t s);
+int dl_blocks_per_cu(int lq, int lv, bool v_in_k);
 
 }  // namespace pkv

@@ -29,16 +29,22 @@ def test_exports_every_declared_function():
     assert "gfx950" in pkv.version()
 
 
+def kernel_name(d, k_ext=4096, v_ext=8192, k_pool=12288, v_pool=16384):
+    lib = pkv.library()
+    n = lib.extend_attention_kernel_name(ctypes.byref(d), k_ext, v_ext, k_pool, v_pool)
+    return None if n is None else n.decode()
+
+
 def test_kernel_name_per_variant():
-    assert pkv.extend_attention_kernel_name(desc()) == "attn_dl_kernel"
-    assert pkv.extend_attention_kernel_name(desc(lq=576, lv=512, num_kv_heads=1, q_stride_head=576,
-                                                 q_stride_tok=32 * 576, ke_stride_tok=576, ke_stride_head=576,
-                                                 kp_stride_slot=576, kp_stride_head=576, o_stride_tok=32 * 512,
-                                                 o_stride_head=512, ve_stride_tok=576, ve_stride_head=576,
-                                                 vp_stride_slot=576, vp_stride_head=576)) == "attn_kernel"
-    assert pkv.extend_attention_kernel_name(desc(dtype=1, lq=64, lv=64)) == "attn_kernel"
-    with pytest.raises(pkv.PkvError):
-        pkv.extend_attention_kernel_name(desc(lq=80, lv=80))
+    assert kernel_name(desc()) == "attn_dl_kernel"
+    mla = desc(lq=576, lv=512, num_kv_heads=1, q_stride_head=576, q_stride_tok=32 * 576, ke_stride_tok=576,
+               ke_stride_head=576, kp_stride_slot=576, kp_stride_head=576, o_stride_tok=32 * 512,
+               o_stride_head=512, ve_stride_tok=576, ve_stride_head=576, vp_stride_slot=576, vp_stride_head=576)
+    # V stored apart from K: the register-staged kernel; V inside K: the direct-load kernel
+    assert kernel_name(mla) == "attn_kernel"
+    assert kernel_name(mla, 4096, 4096, 12288, 12288) == "attn_dl_kernel"
+    assert kernel_name(desc(dtype=1, lq=64, lv=64)) == "attn_kernel"
+    assert kernel_name(desc(lq=80, lv=80)) is None
 
 
 def desc(**kw):

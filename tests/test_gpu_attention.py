@@ -55,6 +55,14 @@ EDGE = [
     dict(name="group7", dtype="bf16", prefix_lens=[200, 17], extend_lens=[37, 100], hq=28, hkv=4, lq=128, lv=128),
     dict(name="fp32-128", dtype="fp32", prefix_lens=[40, 0, 100], extend_lens=[9, 50, 1], hq=4, hkv=2, lq=128, lv=128, sm_scale=0.05),
     dict(name="neg-scale", dtype="bf16", prefix_lens=[20], extend_lens=[20], hq=2, hkv=1, lq=64, lv=64, sm_scale=-0.1),
+    # 576/512 with V the first 512 columns of K (split-wave kernel): ragged
+    # groups of 3 rows, soft-cap, negative scale, and V stored apart from K
+    dict(name="mla-g3-cap", dtype="bf16", prefix_lens=[70, 0, 200], extend_lens=[33, 65, 2], hq=3, hkv=1, lq=576,
+         lv=512, v_aliases_k=True, std=0.5, logit_cap=30.0),
+    dict(name="mla-g16-neg", dtype="bf16", prefix_lens=[45, 130], extend_lens=[19, 8], hq=16, hkv=1, lq=576, lv=512,
+         v_aliases_k=True, std=0.5, sm_scale=-0.06),
+    dict(name="mla-v-apart", dtype="bf16", prefix_lens=[33, 0], extend_lens=[10, 40], hq=8, hkv=1, lq=576, lv=512,
+         std=0.5),
 ]
 
 
@@ -68,6 +76,18 @@ def test_parity_edge(case):
 def test_long_prefix_single_sequence():
     w = wl.custom(dtype="bf16", prefix_lens=[65536], extend_lens=[3], hq=8, hkv=1, lq=128, lv=128)
     parity_full(w, "bs1-P65536")
+
+
+def test_long_prefix_split_mla():
+    # key ranges split into partials and merged, 64-row tiles of the split-wave kernel
+    w = wl.custom(dtype="bf16", prefix_lens=[24000], extend_lens=[2], hq=16, hkv=1, lq=576, lv=512,
+                  v_aliases_k=True, std=0.5)
+    dev = wl.to_torch(w)
+    desc = pkv.make_desc(dev["q"], dev["k_ext"], dev["v_ext"], dev["o"], dev["k_pool"], dev["v_pool"], w.bs,
+                         w.num_prefix)
+    assert pkv.extend_attention_kernel_name(desc, dev["k_ext"], dev["v_ext"], dev["k_pool"],
+                                            dev["v_pool"]) == "attn_dl_kernel"
+    parity_full(w, "mla-bs1-P24000")
 
 
 def test_empty_batch_is_noop():
