@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = enough to exceed 512 MiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel", default="auto", help="attention kernel preference: auto, r64, dl, attn")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attention_traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -103,6 +104,7 @@ def main():
         from paged_kv_extend_amd import _build
         _build.build()
     torch.cuda.init()
+    pkv.extend_attention_prefer_kernel(args.kernel)
     dev = torch.device("cuda", 0)
     w = wl.get(args.workload)
     flops = w.causal_flops()

@@ -174,8 +174,23 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
                          void* stream);
 
 /*
+ * Process-wide kernel preference for later extend_attention_fwd calls, for
+ * tests and benchmarks: "auto" (the default: the fastest measured kernel that
+ * serves the shape), "r64" (64 query rows per wave; bf16, lq == lv == 128), "dl"
+ * (direct global-to-LDS loads; bf16, head dims 64, 128, 256, and 576/512
+ * with V inside K), "attn" (register-staged; every supported shape).  A
+ * preferred kernel that does not serve a call's shape is passed over for the
+ * automatic choice.  Results of every kernel meet the same accuracy bounds;
+ * workspaces sized by extend_attention_workspace_size fit any choice.
+ * Returns PKV_OK, or PKV_ERR_INVALID for an unknown name.  Not synchronised
+ * with calls in flight on other host threads.
+ */
+int extend_attention_prefer_kernel(const char* name);
+
+/*
  * Name of the attention kernel symbol that serves a call with `desc` and these
- * K/V base pointers ("attn_dl_kernel" or "attn_kernel", as profilers list it),
+ * K/V base pointers ("attn_r64_kernel", "attn_dl_kernel" or "attn_kernel", as
+ * profilers list it),
  * or NULL when desc is invalid.  The pointers are only compared (V inside K
  * selects a variant), never dereferenced.  For matching profiler output;
  * results do not depend on it.

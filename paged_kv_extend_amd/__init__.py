@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_workspace_size",
-           "extend_attention_kernel_name",
+           "extend_attention_kernel_name", "extend_attention_prefer_kernel",
            "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "LIB_PATH", "PkvError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -66,6 +66,8 @@ def library() -> ctypes.CDLL:
     lib.pkv_profile_read.restype = ctypes.c_int
     lib.extend_attention_kernel_name.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P]
     lib.extend_attention_kernel_name.restype = ctypes.c_char_p
+    lib.extend_attention_prefer_kernel.argtypes = [ctypes.c_char_p]
+    lib.extend_attention_prefer_kernel.restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.restype = ctypes.c_char_p
     _lib = lib
@@ -193,6 +195,11 @@ def extend_attention_kernel_name(desc: AttnDesc, k_extend=None, v_extend=None, k
     if n is None:
         raise PkvError(-1, last_error())
     return n.decode()
+
+
+def extend_attention_prefer_kernel(name: str) -> None:
+    """Process-wide kernel preference: "auto", "r64", "dl" or "attn" (tests, benchmarks)."""
+    _check(library().extend_attention_prefer_kernel(name.encode()))
 
 
 _ws_cache = {}

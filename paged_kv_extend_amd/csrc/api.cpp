@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <unordered_map>
 #include <vector>
@@ -49,23 +50,62 @@ bool v_inside_k(const pkv_attn_desc_t& d, const void* k_extend, const void* v_ex
          d.kp_stride_head == d.vp_stride_head;
 }
 
+// The attention kernel that serves (dtype, lq, lv), with V inside K or not,
+// and its row / key tiling.  Automatic order: direct loads, 64 rows per wave,
+// register-staged.
+enum class Kernel { kNone, kR64, kDl, kAttn };
+
+std::atomic<int> g_prefer{0};  // Kernel preferred by extend_attention_prefer_kernel, 0 = automatic
+
+// Tiling of kernel k for the shape, or false when k does not serve it.
+bool kernel_tiling(Kernel k, int dtype, int lq, int lv, bool v_in_k, pkv::Tiling* t) {
+  switch (k) {
+    case Kernel::kR64: return pkv::r64_tiling(dtype, lq, lv, t);
+    case Kernel::kDl: return pkv::dl_tiling(dtype, lq, lv, v_in_k, t);
+    case Kernel::kAttn: return pkv::attn_tiling(dtype, lq, lv, t);
+    default: return false;
+  }
+}
+
+Kernel pick_kernel(int dtype, int lq, int lv, bool v_in_k, pkv::Tiling* t) {
+  const Kernel pref = static_cast<Kernel>(g_prefer.load(std::memory_order_relaxed));
+  if (pref != Kernel::kNone && kernel_tiling(pref, dtype, lq, lv, v_in_k, t)) return pref;
+  for (Kernel k : {Kernel::kDl, Kernel::kR64, Kernel::kAttn})
+    if (kernel_tiling(k, dtype, lq, lv, v_in_k, t)) return k;
+  return Kernel::kNone;
+}
+
+const char* kernel_symbol(Kernel k) {
+  switch (k) {
+    case Kernel::kR64: return "attn_r64_kernel";
+    case Kernel::kDl: return "attn_dl_kernel";
+    case Kernel::kAttn: return "attn_kernel";
+    default: return nullptr;
+  }
+}
+
 // Resident attention workgroups on the current device, cached per (device, variant).
 int resident_slots(int dtype, int lq, int lv, bool v_in_k) {
   static std::mutex mu;
   static std::unordered_map<long long, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  const long long key = ((long long)dev << 33) | ((long long)v_in_k << 32) | ((long long)dtype << 24) |
-                        ((long long)lq << 12) | lv;
+  pkv::Tiling t;
+  const Kernel k = pick_kernel(dtype, lq, lv, v_in_k, &t);
+  const long long key = ((long long)dev << 36) | ((long long)k << 33) | ((long long)v_in_k << 32) |
+                        ((long long)dtype << 24) | ((long long)lq << 12) | lv;
   std::lock_guard<std::mutex> lk(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  pkv::Tiling t;
-  const int per_cu = pkv::dl_tiling(dtype, lq, lv, v_in_k, &t) ? pkv::dl_blocks_per_cu(lq, lv, v_in_k)
-                                                                : pkv::attention_blocks_per_cu(dtype, lq, lv);
+  int per_cu = 1;
+  switch (k) {
+    case Kernel::kR64: per_cu = pkv::r64_blocks_per_cu(lq); break;
+    case Kernel::kDl: per_cu = pkv::dl_blocks_per_cu(lq, lv, v_in_k); break;
+    default: per_cu = pkv::attention_blocks_per_cu(dtype, lq, lv); break;
+  }
   const int slots = cus * per_cu;
   cache[key] = slots;
   return slots;
@@ -73,7 +113,7 @@ int resident_slots(int dtype, int lq, int lv, bool v_in_k) {
 
 // Row and key tiling of the kernel serving (dtype, lq, lv) with or without V inside K.
 bool tiling_for(const pkv_attn_desc_t& d, bool v_in_k, pkv::Tiling* t) {
-  return pkv::dl_tiling(d.dtype, d.lq, d.lv, v_in_k, t) || pkv::attn_tiling(d.dtype, d.lq, d.lv, t);
+  return pick_kernel(d.dtype, d.lq, d.lv, v_in_k, t) != Kernel::kNone;
 }
 
 // Sizes derived from the descriptor; returns 0 and sets the error when invalid.
@@ -216,7 +256,7 @@ const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc, const void
   pkv::Tiling t;
   if (check_desc(desc, &t) != PKV_OK) return nullptr;
   const bool vk = v_inside_k(*desc, k_extend, v_extend, k_pool, v_pool);
-  return pkv::dl_tiling(desc->dtype, desc->lq, desc->lv, vk, &t) ? "attn_dl_kernel" : "attn_kernel";
+  return kernel_symbol(pick_kernel(desc->dtype, desc->lq, desc->lv, vk, &t));
 }
 
 int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
@@ -246,15 +286,34 @@ int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* pre
   return ok();
 }
 
+int extend_attention_prefer_kernel(const char* name) {
+  if (!name) return fail(PKV_ERR_INVALID, "kernel name is NULL");
+  static const struct {
+    const char* name;
+    Kernel k;
+  } names[] = {{"auto", Kernel::kNone}, {"r64", Kernel::kR64}, {"dl", Kernel::kDl}, {"attn", Kernel::kAttn}};
+  for (const auto& n : names)
+    if (strcmp(name, n.name) == 0) {
+      g_prefer.store(static_cast<int>(n.k), std::memory_order_relaxed);
+      return ok();
+    }
+  return fail(PKV_ERR_INVALID, "unknown kernel \"%s\" (auto, r64, dl, attn)", name);
+}
+
 size_t extend_attention_workspace_size(const pkv_attn_desc_t* desc) {
   pkv::Tiling t;
   if (check_desc(desc, &t) != PKV_OK) return 0;
   g_err[0] = '\0';
-  // the kernel, and with it the row tiling, may depend on whether V lies
-  // inside K, which only the call shows: size for both
-  size_t total = ws_layout(desc, t, plan_bounds(desc, t)).total;
-  pkv::Tiling tv;
-  if (tiling_for(*desc, true, &tv)) total = std::max(total, ws_layout(desc, tv, plan_bounds(desc, tv)).total);
+  // the kernel, and with it the row tiling, depends on whether V lies inside
+  // K (which only the call shows) and on the kernel preference: size for
+  // every kernel that could serve the shape
+  size_t total = 0;
+  for (Kernel k : {Kernel::kR64, Kernel::kDl, Kernel::kAttn})
+    for (bool vk : {false, true}) {
+      pkv::Tiling tk;
+      if (kernel_tiling(k, desc->dtype, desc->lq, desc->lv, vk, &tk))
+        total = std::max(total, ws_layout(desc, tk, plan_bounds(desc, tk)).total);
+    }
   return total;
 }
 
@@ -355,8 +414,11 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   const auto ev = profile_slot();
   if (ev.first) (void)hipEventRecord(ev.first, s);
   pkv::Tiling td;
-  e = pkv::dl_tiling(d.dtype, d.lq, d.lv, vk, &td) ? pkv::launch_dl(d.lq, d.lv, vk, a, pb.max_work, s)
-                                                   : pkv::launch_attention(d.dtype, d.lq, d.lv, a, pb.max_work, s);
+  switch (pick_kernel(d.dtype, d.lq, d.lv, vk, &td)) {
+    case Kernel::kR64: e = pkv::launch_r64(d.lq, a, pb.max_work, s); break;
+    case Kernel::kDl: e = pkv::launch_dl(d.lq, d.lv, vk, a, pb.max_work, s); break;
+    default: e = pkv::launch_attention(d.dtype, d.lq, d.lv, a, pb.max_work, s); break;
+  }
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   if (ev.second) (void)hipEventRecord(ev.second, s);
   e = pkv::launch_merge(d.dtype, d.lv, a, t.bm, pb.max_merge, s);

@@ -23,40 +23,11 @@
 //  * When V is the first Lv columns of K (the MLA layout on page
 //    "cpu_graph_runner.py", qkv_proj_with_rope: v = k.narrow(-1, 0, lv)), only
 //    the K tile is loaded and the V^T operand is read from it.
+#include "device_common.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-template <class T>
-using gptr = const __attribute__((address_space(1))) T*;
-template <class T>
-using lptr = __attribute__((address_space(3))) T*;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float pair_max(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// s_waitcnt vmcnt(0) lgkmcnt(0) (gfx9 encoding: vmcnt [3:0],[15:14]; expcnt [6:4]; lgkmcnt [11:8])
-__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0x7 << 4); }
-// s_waitcnt lgkmcnt(0) only: LDS traffic done, global loads may stay in flight
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int LQ, int LV, int BN, bool VK>
 struct DlCfg {
@@ -146,7 +117,8 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK>::NT), MINB) void attn_dl_ker
   if ((int)blockIdx.x >= a.hdr->num_work) return;
   const WorkItem it = a.work[blockIdx.x];
   if (it.b < 0) return;  // empty placement slot
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
   const int rg = wv % C::RG, half = wv / C::RG;  // row group; which half of Q dims / O columns
   const int qi = lane & 31, hi = lane >> 5;
   // first 16-byte chunk of contraction step ks (its lanes hi = 0, 1 take ch, ch + 1)
@@ -220,26 +192,37 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK>::NT), MINB) void attn_dl_ker
   // ---- direct loads of tile kt into stage kt & 1: wave w covers bytes
   //      [(i * NW + w) * 1024, +1024) of the K and V regions
   auto issue_tile = [&](int kt) __attribute__((always_inline)) {
-    char* stage = lds + (kt & 1) * C::STAGE_BYTES;
+    const uint32_t stage = lds_addr(lds + (kt & 1) * C::STAGE_BYTES);
+    // all row pointers first: each load is a compiler memory barrier
+    gptr<T> ksrc[C::K_LOADS];
+    gptr<T> vsrc[C::V_LOADS > 0 ? C::V_LOADS : 1];
 #pragma unroll
     for (int i = 0; i < C::K_LOADS; ++i) {
       const int li = i * C::NW + wv;
       if (C::K_CHUNKS % C::NW != 0 && li >= C::K_CHUNKS) break;  // wave-uniform
-      const int base = li * 1024;
-      const int off = base + lane * 16;
+      const int off = li * 1024 + lane * 16;
       const int row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
-      __builtin_amdgcn_global_load_lds((gptr<void>)(kptr[kt & 1][row] + swz_k<C>(row, p) * 8),
-                                       (lptr<void>)(stage + base), 16, 0, 0);
+      ksrc[i] = kptr[kt & 1][row] + swz_k<C>(row, p) * 8;
     }
 #pragma unroll
     for (int i = 0; i < C::V_LOADS; ++i) {
       const int li = i * C::NW + wv;
       if (C::V_CHUNKS % C::NW != 0 && li >= C::V_CHUNKS) break;
-      const int base = li * 1024;
-      const int off = base + lane * 16;
+      const int off = li * 1024 + lane * 16;
       const int row = off / (LV * 2), p = (off % (LV * 2)) / 16;
-      __builtin_amdgcn_global_load_lds((gptr<void>)(vptr[kt & 1][row] + swz_v<C>(row, p) * 8),
-                                       (lptr<void>)(stage + C::K_BYTES + base), 16, 0, 0);
+      vsrc[i] = vptr[kt & 1][row] + swz_v<C>(row, p) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < C::K_LOADS; ++i) {
+      const int li = i * C::NW + wv;
+      if (C::K_CHUNKS % C::NW != 0 && li >= C::K_CHUNKS) break;
+      load_lds_16((gptr<void>)ksrc[i], stage + li * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < C::V_LOADS; ++i) {
+      const int li = i * C::NW + wv;
+      if (C::V_CHUNKS % C::NW != 0 && li >= C::V_CHUNKS) break;
+      load_lds_16((gptr<void>)vsrc[i], stage + C::K_BYTES + li * 1024);
     }
   };
 
@@ -279,7 +262,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK>::NT), MINB) void attn_dl_ker
     // only tile kt's loads are outstanding here (the index load of the wave
     // that builds tables was waited for when its table was written)
     wait_all_mem();
-    __builtin_amdgcn_s_barrier();  // tile kt visible; stage and table of kt+1 free/visible
+    barrier_fence();  // tile kt visible; stage and table of kt+1 free/visible
     if (wv == 0 && kt + 2 < kt1) fetch_slot(kt + 2);  // before the tile loads: waiting for it never waits for them
     if (kt + 1 < kt1) issue_tile(kt + 1);
 
@@ -327,7 +310,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK>::NT), MINB) void attn_dl_ker
                 f32x4{s[kb][4 * q4], s[kb][4 * q4 + 1], s[kb][4 * q4 + 2], s[kb][4 * q4 + 3]};
       }
       wait_lds();
-      __builtin_amdgcn_s_barrier();
+      barrier_fence();
       if (act) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {

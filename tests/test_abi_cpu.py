@@ -37,6 +37,7 @@ def kernel_name(d, k_ext=4096, v_ext=8192, k_pool=12288, v_pool=16384):
 
 def test_kernel_name_per_variant():
     assert kernel_name(desc()) == "attn_dl_kernel"
+    assert kernel_name(desc(lq=64, lv=64)) == "attn_dl_kernel"
     mla = desc(lq=576, lv=512, num_kv_heads=1, q_stride_head=576, q_stride_tok=32 * 576, ke_stride_tok=576,
                ke_stride_head=576, kp_stride_slot=576, kp_stride_head=576, o_stride_tok=32 * 512,
                o_stride_head=512, ve_stride_tok=576, ve_stride_head=576, vp_stride_slot=576, vp_stride_head=576)
@@ -45,6 +46,35 @@ def test_kernel_name_per_variant():
     assert kernel_name(mla, 4096, 4096, 12288, 12288) == "attn_dl_kernel"
     assert kernel_name(desc(dtype=1, lq=64, lv=64)) == "attn_kernel"
     assert kernel_name(desc(lq=80, lv=80)) is None
+
+
+def test_kernel_preference():
+    try:
+        pkv.extend_attention_prefer_kernel("r64")
+        assert kernel_name(desc()) == "attn_r64_kernel"
+        pkv.extend_attention_prefer_kernel("attn")
+        assert kernel_name(desc()) == "attn_kernel"
+        # a preferred kernel that does not serve the shape is passed over
+        pkv.extend_attention_prefer_kernel("r64")
+        assert kernel_name(desc(lq=64, lv=64)) == "attn_dl_kernel"
+        with pytest.raises(pkv.PkvError):
+            pkv.extend_attention_prefer_kernel("fastest")
+    finally:
+        pkv.extend_attention_prefer_kernel("auto")
+    assert kernel_name(desc()) == "attn_dl_kernel"
+
+
+def test_workspace_covers_every_kernel():
+    lib = pkv.library()
+    d = desc()
+    sizes = []
+    try:
+        for k in ("auto", "r64", "dl", "attn"):
+            pkv.extend_attention_prefer_kernel(k)
+            sizes.append(lib.extend_attention_workspace_size(ctypes.byref(d)))
+    finally:
+        pkv.extend_attention_prefer_kernel("auto")
+    assert len(set(sizes)) == 1 and sizes[0] > 0
 
 
 def desc(**kw):
