@@ -15,11 +15,14 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          # no packed fp32 instructions from the compiler
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per-source additions: the 64-row kernel keeps its S tiles in ordinary vector
+# registers for the softmax, so its MFMA results are taken in VGPR form
+SOURCE_FLAGS = {"attention_r64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = ["hipcc", *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", out]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

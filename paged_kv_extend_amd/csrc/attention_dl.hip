@@ -12,14 +12,19 @@
 // What differs from attention.hip is the tile movement:
 //  * global_load_lds (16 bytes per lane) writes each K/V row chunk directly
 //    into LDS: no staging registers, no LDS store instructions, and one barrier
-//    per tile instead of two.  Two LDS stages: tile t+1 streams in while tile t
-//    is computed.
+//    per tile instead of two.
+//  * NS LDS stages: tile t+NS-1 is requested while tile t is computed, deep
+//    enough to cover the latency of a gather from the pool under load.  The
+//    row slots (kv_indices) of later tiles come into LDS the same way, so the
+//    only memory traffic in the loop is these loads, every trip has the same
+//    number of them, and the wait at the top of a trip is a fixed vmcnt.
 //  * The load places lane L's 16 bytes at base + 16 L, so rows cannot be
 //    padded; instead the 16-byte chunk index is XOR-swizzled per row (applied
 //    when choosing each lane's global address, undone on reads): the
 //    MFMA operand reads of K and the transposing reads of V stay free of bank
 //    conflicts.
-//  * Waits on the loads are explicit vmcnt counts before a bare s_barrier.
+//  * Head dim 128 runs 256 rows (8 waves, two per SIMD) per workgroup, so one
+//    K/V tile in LDS serves twice the rows of a 128-row workgroup.
 //  * When V is the first Lv columns of K (the MLA layout on page
 //    "cpu_graph_runner.py", qkv_proj_with_rope: v = k.narrow(-1, 0, lv)), only
 //    the K tile is loaded and the V^T operand is read from it.
@@ -29,7 +34,7 @@
 namespace pkv {
 namespace {
 
-template <int LQ, int LV, int BN, bool VK>
+template <int LQ, int LV, int BN, bool VK, int RG_, int NS_>
 struct DlCfg {
   // Waves per row group.  When one wave cannot hold both its Q^T operand
   // (LQ / 4 registers) and its O^T accumulator (LV / 2 registers), two waves
@@ -39,10 +44,12 @@ struct DlCfg {
   // 32-column output blocks 2m + h, so that inside a swizzle group its
   // operand addresses differ from one per-lane base by constants only.
   static constexpr int SPLIT = LQ / 4 + LV / 2 > 320 ? 2 : 1;
-  // 32-row groups per workgroup.  Split: 2, i.e. 4 waves and one wave per
-  // SIMD, which leaves each wave the whole 512-entry register file (its Q^T
-  // and O^T halves alone take ~200 entries).
-  static constexpr int RG = SPLIT > 1 ? 2 : 4;
+  // 32-row groups per workgroup (the split variant uses 2, i.e. 4 waves and
+  // one wave per SIMD, which leaves each wave the whole 512-entry register
+  // file: its Q^T and O^T halves alone take ~200 entries)
+  static constexpr int RG = RG_;
+  // LDS stages: tile kt+NS-1 is requested while tile kt is computed
+  static constexpr int NS = NS_;
   static constexpr int NW = RG * SPLIT;
   static constexpr int NT = NW * 64;
   static constexpr int BM = RG * 32;
@@ -62,13 +69,20 @@ struct DlCfg {
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
   static constexpr int K_CHUNKS = K_BYTES / 1024;  // 1 KB load instructions per tile
   static constexpr int V_CHUNKS = V_BYTES / 1024;
-  static constexpr int K_LOADS = (K_CHUNKS + NW - 1) / NW;  // per wave (the last round may be partial)
-  static constexpr int V_LOADS = (V_CHUNKS + NW - 1) / NW;
+  static constexpr int K_LOADS = K_CHUNKS / NW;  // per wave
+  static constexpr int V_LOADS = V_CHUNKS / NW;
+  static constexpr int L = K_LOADS + V_LOADS;     // tile loads per wave per tile
+  static constexpr int I = BN * 8 / 256;          // row-slot loads (64 lanes x 4 bytes) per tile, wave 0
+  // waits at the top of an iteration (see the loop): outstanding loads allowed
+  static constexpr int W_OTHER = (NS - 2) * L;
+  static constexpr int W_WAVE0 = (NS - 2) * (I + L) < 2 * L + I ? (NS - 2) * (I + L) : 2 * L + I;
   static constexpr int XCH_BYTES = SPLIT > 1 ? NW * BN * 32 * 4 : 0;  // S^T halves exchanged
   static_assert(CK == 8 || CK == 16 || CK == 32 || CK == 72, "lq");
   static_assert(VK ? LV <= LQ : (CV == 8 || CV == 16 || CV == 32), "lv");
   static_assert(!WIDE || VK, "576-wide rows only with V inside K");
-  static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "whole 1 KB loads");
+  static_assert(K_CHUNKS % NW == 0 && V_CHUNKS % NW == 0, "the same whole 1 KB loads in every wave");
+  static_assert(NS >= 3 && W_WAVE0 < 64 && W_OTHER < 64, "pipeline depth");
+  static_assert(RG == 2 || SPLIT == 1, "split variant: two row groups");
   static_assert(QD % 16 == 0 && VD % 32 == 0, "split");
   static_assert(SPLIT == 1 || WIDE, "the split interleaves halves inside 8-chunk swizzle groups");
   static_assert(BN % 32 == 0 && BN <= 64, "key tile");
@@ -101,18 +115,19 @@ __device__ __forceinline__ int swz_v(int r, int c) {
   }
 }
 
-template <int LQ, int LV, int BN, bool VK, bool CAP, int MINB>
-__global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK>::NT), MINB) void attn_dl_kernel(AttnArgs a) {
-  using C = DlCfg<LQ, LV, BN, VK>;
+template <int LQ, int LV, int BN, bool VK, int RG, int NS, bool CAP, int MINB>
+__global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void attn_dl_kernel(AttnArgs a) {
+  using C = DlCfg<LQ, LV, BN, VK, RG, NS>;
   using T = uint16_t;
   constexpr int BM = C::BM;
   constexpr int NKB = BN / 32;
   constexpr int NQ = C::QD / 16;
   constexpr int NDB = C::VD / 32;
 
-  __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE_BYTES + C::XCH_BYTES];
-  __shared__ gptr<T> kptr[2][BN];
-  __shared__ gptr<T> vptr[2][BN];
+  __shared__ __attribute__((aligned(1024))) char lds[NS * C::STAGE_BYTES + C::XCH_BYTES];
+  __shared__ gptr<T> kptr[NS][BN];  // row pointer tables, slot kt % NS
+  __shared__ gptr<T> vptr[NS][BN];
+  __shared__ __attribute__((aligned(16))) int64_t slots[4][BN];  // row slots of later tiles, slot kt & 3
 
   if ((int)blockIdx.x >= a.hdr->num_work) return;
   const WorkItem it = a.work[blockIdx.x];
@@ -163,67 +178,76 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK>::NT), MINB) void attn_dl_ker
     }
   }
 
-  // ---- row pointer tables (two slots); lane j < BN of the owning wave owns key kt*BN + j
-  int64_t slot_next = 0;
-  auto fetch_slot = [&](int kt) __attribute__((always_inline)) {
+  // ---- row pointer tables (two slots), built by wave 0; lane j < BN owns key kt*BN + j.
+  //      Strides and per-head bases are read once into scalar registers.
+  const int64_t kp_ss = uniform64(a.kp_ss), vp_ss = uniform64(a.vp_ss);
+  const int64_t ke_st = uniform64(a.ke_st), ve_st = uniform64(a.ve_st);
+  const gptr<T> kpool_g = kpool + (int64_t)g * uniform64(a.kp_sh);
+  const gptr<T> vpool_g = vpool + (int64_t)g * uniform64(a.vp_sh);
+  const gptr<T> kext_g = kext + (int64_t)g * uniform64(a.ke_sh);
+  const gptr<T> vext_g = vext + (int64_t)g * uniform64(a.ve_sh);
+  // pointers of key kt*BN + lane (lane < BN) for the table of tile kt
+  auto key_ptrs = [&](int kt, int64_t slot, gptr<T>& kp, gptr<T>& vp) __attribute__((always_inline)) {
     const int j = kt * BN + lane;
-    slot_next = (lane < BN && j < P && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
-  };
-  auto write_ptrs = [&](int kt) __attribute__((always_inline)) {
-    if (lane < BN) {
-      const int j = kt * BN + lane;
-      gptr<T> kp = zrow;
-      gptr<T> vp = zrow;
-      if (j <= key_last) {
-        if (j < P) {
-          kp = kpool + slot_next * a.kp_ss + (int64_t)g * a.kp_sh;
-          vp = vpool + slot_next * a.vp_ss + (int64_t)g * a.vp_sh;
-        } else {
-          const int64_t row = q0 + (j - P);
-          kp = kext + row * a.ke_st + (int64_t)g * a.ke_sh;
-          vp = vext + row * a.ve_st + (int64_t)g * a.ve_sh;
-        }
+    kp = zrow;
+    vp = zrow;
+    if (j <= key_last) {
+      if (j < P) {
+        kp = kpool_g + slot * kp_ss;
+        vp = vpool_g + slot * vp_ss;
+      } else {
+        const int64_t row = q0 + (j - P);
+        kp = kext_g + row * ke_st;
+        vp = vext_g + row * ve_st;
       }
-      kptr[kt & 1][lane] = kp;
-      vptr[kt & 1][lane] = vp;
+    }
+  };
+  // table of tile kt from the row slots already in LDS (wave 0)
+  auto write_table = [&](int kt) __attribute__((always_inline)) {
+    if (lane < BN) {
+      gptr<T> kp, vp;
+      key_ptrs(kt, slots[kt & 3][lane], kp, vp);
+      kptr[kt % NS][lane] = kp;
+      vptr[kt % NS][lane] = vp;
+    }
+  };
+  // row slots of tile kt into LDS (wave 0): I loads of 64 lanes x 4 bytes;
+  // keys outside the prefix or past the last visible key read the zero row
+  auto issue_slots = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::I; ++i) {
+      const int o = i * 256 + lane * 4;  // byte offset in the tile's slot block
+      const int j = kt * BN + o / 8;
+      gptr<char> src = (gptr<char>)zrow;
+      if (j < P && j <= key_last) src = (gptr<char>)a.kv_indices + (int64_t)(kvs + j) * 8 + (o & 4);
+      load_lds_4((gptr<void>)src, lds_addr(&slots[kt & 3][0]) + i * 256);
     }
   };
 
-  // ---- direct loads of tile kt into stage kt & 1: wave w covers bytes
+  // ---- direct loads of tile kt into stage kt % NS: wave w covers bytes
   //      [(i * NW + w) * 1024, +1024) of the K and V regions
   auto issue_tile = [&](int kt) __attribute__((always_inline)) {
-    const uint32_t stage = lds_addr(lds + (kt & 1) * C::STAGE_BYTES);
+    const uint32_t stage = lds_addr(lds + (kt % NS) * C::STAGE_BYTES);
     // all row pointers first: each load is a compiler memory barrier
     gptr<T> ksrc[C::K_LOADS];
     gptr<T> vsrc[C::V_LOADS > 0 ? C::V_LOADS : 1];
 #pragma unroll
     for (int i = 0; i < C::K_LOADS; ++i) {
-      const int li = i * C::NW + wv;
-      if (C::K_CHUNKS % C::NW != 0 && li >= C::K_CHUNKS) break;  // wave-uniform
-      const int off = li * 1024 + lane * 16;
+      const int off = (i * C::NW + wv) * 1024 + lane * 16;
       const int row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
-      ksrc[i] = kptr[kt & 1][row] + swz_k<C>(row, p) * 8;
+      ksrc[i] = kptr[kt % NS][row] + swz_k<C>(row, p) * 8;
     }
 #pragma unroll
     for (int i = 0; i < C::V_LOADS; ++i) {
-      const int li = i * C::NW + wv;
-      if (C::V_CHUNKS % C::NW != 0 && li >= C::V_CHUNKS) break;
-      const int off = li * 1024 + lane * 16;
+      const int off = (i * C::NW + wv) * 1024 + lane * 16;
       const int row = off / (LV * 2), p = (off % (LV * 2)) / 16;
-      vsrc[i] = vptr[kt & 1][row] + swz_v<C>(row, p) * 8;
+      vsrc[i] = vptr[kt % NS][row] + swz_v<C>(row, p) * 8;
     }
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int li = i * C::NW + wv;
-      if (C::K_CHUNKS % C::NW != 0 && li >= C::K_CHUNKS) break;
-      load_lds_16((gptr<void>)ksrc[i], stage + li * 1024);
-    }
+    for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ksrc[i], stage + (i * C::NW + wv) * 1024);
 #pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i) {
-      const int li = i * C::NW + wv;
-      if (C::V_CHUNKS % C::NW != 0 && li >= C::V_CHUNKS) break;
-      load_lds_16((gptr<void>)vsrc[i], stage + C::K_BYTES + li * 1024);
-    }
+    for (int i = 0; i < C::V_LOADS; ++i)
+      load_lds_16((gptr<void>)vsrc[i], stage + C::K_BYTES + (i * C::NW + wv) * 1024);
   };
 
   // wide rows: per-lane byte offsets of the operand reads inside a stage.
@@ -249,167 +273,232 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK>::NT), MINB) void attn_dl_ker
   float m_ref = -INFINITY;  // reference max of the exponentials, base-2 units
   float l_run = 0.0f;       // this lane's share of the running sum
 
+  // Pipeline.  Iteration kt computes tile kt while tiles kt+1 .. kt+NS-2 are
+  // in flight; after its barrier it requests the row slots of tile kt+NS+1
+  // (wave 0) and then tile kt+NS-1.  Tiles and slots past the end of the
+  // range are requested too (zero rows, unused), so every wave has the same
+  // number of loads in flight on every trip and the waits are fixed counts.
   if (kt0 < kt1) {
-    if (wv < 2 && kt0 + wv < kt1) {  // tables of the first two tiles, one wave each
-      fetch_slot(kt0 + wv);
-      write_ptrs(kt0 + wv);
+    // tables of the first NS-1 tiles straight from global memory
+    for (int v = wv; v < NS - 1; v += C::NW) {
+      if (lane < BN) {
+        const int j = (kt0 + v) * BN + lane;
+        const int64_t slot = (j < P && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
+        gptr<T> kp, vp;
+        key_ptrs(kt0 + v, slot, kp, vp);
+        kptr[(kt0 + v) % NS][lane] = kp;
+        vptr[(kt0 + v) % NS][lane] = vp;
+      }
     }
     __syncthreads();
-    issue_tile(kt0);
+    // the groups that iterations kt0-NS+1 .. kt0-1 would have issued
+#pragma unroll
+    for (int v = 0; v < NS - 1; ++v) {
+      if (wv == 0) issue_slots(kt0 + v + 2);
+      issue_tile(kt0 + v);
+    }
   }
 
-  for (int kt = kt0; kt < kt1; ++kt) {
-    // only tile kt's loads are outstanding here (the index load of the wave
-    // that builds tables was waited for when its table was written)
-    wait_all_mem();
-    barrier_fence();  // tile kt visible; stage and table of kt+1 free/visible
-    if (wv == 0 && kt + 2 < kt1) fetch_slot(kt + 2);  // before the tile loads: waiting for it never waits for them
-    if (kt + 1 < kt1) issue_tile(kt + 1);
+  // ---- tile math
+  auto active = [&](int kt) __attribute__((always_inline)) { return wave_live && kt * BN <= P + i_hi_w; };
 
-    const int j0 = kt * BN;
-    const bool act = wave_live && j0 <= P + i_hi_w;  // same for both waves of a row group
-    const char* Ks = lds + (kt & 1) * C::STAGE_BYTES;
-    const char* Vs = VK ? Ks : Ks + C::K_BYTES;
-
-    // S^T = K Q^T (this wave's Q dims)
-    f32x16 s[NKB];
+  // S^T = K Q^T over this wave's Q dims
+  auto qk = [&](int kt, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
+    const char* Ks = lds + (kt % NS) * C::STAGE_BYTES;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-    if (act) {
 #pragma unroll
-      for (int ks = 0; ks < NQ; ++ks) {
+    for (int ks = 0; ks < NQ; ++ks) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const char* ka;
-          if constexpr (C::WIDE) {
-            // rows kb*32 + qi share qi's swizzle; the group offset is a constant
-            ka = Ks + k_lane[ks & 1] + kb * 32 * LQ * 2 + (ks >> 1) * 128;
-          } else {
-            const int row = kb * 32 + qi;
-            ka = Ks + row * LQ * 2 + swz_k<C>(row, qk_chunk(ks) + hi) * 16;
-          }
-          const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ka));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qr[ks], s[kb], 0, 0, 0);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const char* ka;
+        if constexpr (C::WIDE) {
+          // rows kb*32 + qi share qi's swizzle; the group offset is a constant
+          ka = Ks + k_lane[ks & 1] + kb * 32 * LQ * 2 + (ks >> 1) * 128;
+        } else {
+          const int row = kb * 32 + qi;
+          ka = Ks + row * LQ * 2 + swz_k<C>(row, qk_chunk(ks) + hi) * 16;
         }
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ka));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qr[ks], s[kb], 0, 0, 0);
       }
     }
-    if constexpr (C::SPLIT > 1) {
-      // the two halves of S^T meet in LDS; a + b == b + a, so both waves of
-      // the pair hold the same S^T bit for bit and take the same softmax
-      // decisions.  The buffer is free again at the next tile's barrier,
-      // which every wave reaches only after its reads have returned.
-      f32x4* xw = reinterpret_cast<f32x4*>(lds + 2 * C::STAGE_BYTES) + wv * (NKB * 4 * 64);
-      const f32x4* xr =
-          reinterpret_cast<const f32x4*>(lds + 2 * C::STAGE_BYTES) + ((wv + C::RG) % C::NW) * (NKB * 4 * 64);
-      if (act) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            xw[(kb * 4 + q4) * 64 + lane] =
-                f32x4{s[kb][4 * q4], s[kb][4 * q4 + 1], s[kb][4 * q4 + 2], s[kb][4 * q4 + 3]};
-      }
-      wait_lds();
-      barrier_fence();
-      if (act) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          f32x16 o;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 v = xr[(kb * 4 + q4) * 64 + lane];
-            o[4 * q4] = v[0];
-            o[4 * q4 + 1] = v[1];
-            o[4 * q4 + 2] = v[2];
-            o[4 * q4 + 3] = v[3];
-          }
-          s[kb] += o;
-        }
-      }
-    }
+  };
 
+  // split waves: the two halves of S^T meet in LDS; a + b == b + a, so both
+  // waves of the pair hold the same S^T bit for bit and take the same
+  // softmax decisions.  Contains a barrier: every wave calls it.  The buffer
+  // is free again at the next tile's barrier, which every wave reaches only
+  // after its reads have returned.
+  auto exchange = [&](bool act, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
+    f32x4* xw = reinterpret_cast<f32x4*>(lds + NS * C::STAGE_BYTES) + wv * (NKB * 4 * 64);
+    const f32x4* xr =
+        reinterpret_cast<const f32x4*>(lds + NS * C::STAGE_BYTES) + ((wv + C::RG) % C::NW) * (NKB * 4 * 64);
     if (act) {
-      const bool need_mask = j0 + BN - 1 > P + i_lo_w;
-
-      // soft-cap (base-2 units), mask of the diagonal tiles, row max
-      if constexpr (CAP) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const float e = fast_exp2(s[kb][rr] * (a.cap_in * 2.0f * kLog2e));
-            s[kb][rr] = a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
-          }
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
-            s[kb][rr] = j <= lim ? s[kb][rr] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
-      mx = pair_max(mx);
-      if constexpr (!CAP) mx *= a.scale_log2;
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack)) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-      }
-      const float m_sub = m_ref == -INFINITY ? 0.0f : m_ref;
-
-      // P (bf16, summed with dot2) and O^T += V^T P^T
-      const int key0 = 4 * hi + ((lane & 15) >> 2);
-      const int cofs = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        for (int q4 = 0; q4 < 4; ++q4)
+          xw[(kb * 4 + q4) * 64 + lane] = f32x4{s[kb][4 * q4], s[kb][4 * q4 + 1], s[kb][4 * q4 + 2], s[kb][4 * q4 + 3]};
+    }
+    wait_lds();
+    barrier_fence();
+    if (act) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        f32x16 o;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          bf16x8 pb;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = xr[(kb * 4 + q4) * 64 + lane];
+          o[4 * q4] = v[0];
+          o[4 * q4 + 1] = v[1];
+          o[4 * q4 + 2] = v[2];
+          o[4 * q4 + 3] = v[3];
+        }
+        s[kb] += o;
+      }
+    }
+  };
+
+  // softmax head: soft-cap (base-2 units), mask of the diagonal tiles, row
+  // max and lazy rescale; returns the value subtracted in the exponent
+  auto softmax_head = [&](int kt, f32x16 (&s)[NKB]) __attribute__((always_inline)) -> float {
+    const int j0 = kt * BN;
+    const bool need_mask = j0 + BN - 1 > P + i_lo_w;
+    if constexpr (CAP) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = s[kb][8 * hf + e];
-            const float p = CAP ? fast_exp2(x - m_sub) : fast_exp2(fmaf(x, a.scale_log2, -m_sub));
-            pb[e] = (__bf16)p;
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const float e = fast_exp2(s[kb][rr] * (a.cap_in * 2.0f * kLog2e));
+          s[kb][rr] = a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
+        }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
+          s[kb][rr] = j <= lim ? s[kb][rr] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+    mx = pair_max(mx);
+    if constexpr (!CAP) mx *= a.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    return m_ref == -INFINITY ? 0.0f : m_ref;
+  };
+  // P = exp2(s - m) rounded to bf16 in B-operand layout and its row sum
+  // (bf16 dot2 with ones); no branches
+  auto softmax_exp = [&](const f32x16 (&s)[NKB], float m_sub, bf16x8 (&pb)[NKB][2]) __attribute__((always_inline)) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        bf16x8 q;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = s[kb][8 * hf + e];
+          const float p = CAP ? fast_exp2(x - m_sub) : fast_exp2(fmaf(x, a.scale_log2, -m_sub));
+          q[e] = (__bf16)p;
+        }
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 0, 1), ones, l_run, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 2, 3), ones, l_run, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 4, 5), ones, l_run, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 6, 7), ones, l_run, false);
+        pb[kb][hf] = q;
+      }
+    }
+  };
+  auto softmax = [&](int kt, f32x16 (&s)[NKB], bf16x8 (&pb)[NKB][2]) __attribute__((always_inline)) {
+    softmax_exp(s, softmax_head(kt, s), pb);
+  };
+
+  // O^T += V^T P^T, the V^T operand through transposing LDS reads
+  const int key0 = 4 * hi + ((lane & 15) >> 2);
+  const int cofs = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto pv = [&](int kt, const bf16x8 (&pb)[NKB][2]) __attribute__((always_inline)) {
+    const char* Ks = lds + (kt % NS) * C::STAGE_BYTES;
+    const char* Vs = VK ? Ks : Ks + C::K_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r0 = kb * 32 + 16 * hf + key0, r1 = r0 + 8;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const char *a0, *a1;
+          if constexpr (C::WIDE) {
+            const int cst = (kb * 32 + 16 * hf) * C::V_PITCH + db * 128;
+            a0 = Vs + v_lane[0] + cst;
+            a1 = Vs + v_lane[1] + cst;
+          } else {
+            const int col = o_block(db) * 32 + cofs;
+            a0 = Vs + r0 * C::V_PITCH + swz_v<C>(r0, col / 8) * 16 + (col % 8) * 2;
+            a1 = Vs + r1 * C::V_PITCH + swz_v<C>(r1, col / 8) * 16 + (col % 8) * 2;
           }
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones, l_run, false);
-          const int r0 = kb * 32 + 16 * hf + key0, r1 = r0 + 8;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const char *a0, *a1;
-            if constexpr (C::WIDE) {
-              const int cst = (kb * 32 + 16 * hf) * C::V_PITCH + db * 128;
-              a0 = Vs + v_lane[0] + cst;
-              a1 = Vs + v_lane[1] + cst;
-            } else {
-              const int col = o_block(db) * 32 + cofs;
-              a0 = Vs + r0 * C::V_PITCH + swz_v<C>(r0, col / 8) * 16 + (col % 8) * 2;
-              a1 = Vs + r1 * C::V_PITCH + swz_v<C>(r1, col / 8) * 16 + (col % 8) * 2;
-            }
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr<i16x4>)(a0));
-            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr<i16x4>)(a1));
-            const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[db], 0, 0, 0);
-          }
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr<i16x4>)(a0));
+          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr<i16x4>)(a1));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][hf], acc[db], 0, 0, 0);
         }
       }
     }
-    // table of kt+2 into the slot of kt (last read when tile kt was issued)
-    if (wv == 0 && kt + 2 < kt1) write_ptrs(kt + 2);
+  };
+
+  // Top of iteration kt.  Tile kt was requested NS-1 groups ago and the row
+  // slots of tile kt+NS-1 two groups ago (first in that group): wait until at
+  // most the later loads are outstanding.  Wave 0 then writes table kt+NS-1
+  // (its slot held table kt-1, issued long ago) before the barrier that
+  // publishes it and tile kt.
+  auto tile_top = [&](int kt) __attribute__((always_inline)) {
+    if (wv == 0) {
+      wait_vm<C::W_WAVE0>();
+      write_table(kt + NS - 1);
+      wait_lds();
+    } else {
+      wait_vm<C::W_OTHER>();
+    }
+    barrier_fence();
+  };
+  // the group of iteration kt: row slots of tile kt+NS+1 (wave 0) and tile
+  // kt+NS-1 into stage (kt-1) % NS, which tile kt-1 no longer needs
+  auto issue_group = [&](int kt) __attribute__((always_inline)) {
+    if (wv == 0) issue_slots(kt + NS + 1);
+    issue_tile(kt + NS - 1);
+  };
+
+  for (int kt = kt0; kt < kt1; ++kt) {
+    tile_top(kt);
+    issue_group(kt);
+    const bool act = active(kt);
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    if (act) qk(kt, s);
+    if constexpr (C::SPLIT > 1) exchange(act, s);
+    if (act) {
+      bf16x8 pb[NKB][2];
+      softmax(kt, s, pb);
+      pv(kt, pb);
+    }
   }
+
+  // the requests past the end may still be writing LDS
+  wait_all_mem();
 
   // ---- epilogue
   const float l_tot = pair_sum(l_run);
@@ -446,44 +535,46 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK>::NT), MINB) void attn_dl_ker
   }
 }
 
-template <int LQ, int LV, int BN, bool VK, int MINB>
+template <int LQ, int LV, int BN, bool VK, int RG, int NS, int MINB>
 hipError_t launch_dl_t(const AttnArgs& a, int64_t grid, hipStream_t s) {
+  using C = DlCfg<LQ, LV, BN, VK, RG, NS>;
   if (grid <= 0) return hipSuccess;
   if (a.use_cap)
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, true, MINB>), dim3((unsigned)grid),
-                       dim3(DlCfg<LQ, LV, BN, VK>::NT), 0, s, a);
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, NS, true, MINB>), dim3((unsigned)grid), dim3(C::NT), 0,
+                       s, a);
   else
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, false, MINB>), dim3((unsigned)grid),
-                       dim3(DlCfg<LQ, LV, BN, VK>::NT), 0, s, a);
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, NS, false, MINB>), dim3((unsigned)grid), dim3(C::NT), 0,
+                       s, a);
   return hipGetLastError();
 }
 
-template <int LQ, int LV, int BN, bool VK, int MINB>
+template <int LQ, int LV, int BN, bool VK, int RG, int NS, int MINB>
 int dl_occupancy_t() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, VK, false, MINB>), DlCfg<LQ, LV, BN, VK>::NT,
-          0) != hipSuccess)
+          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, VK, RG, NS, false, MINB>),
+          DlCfg<LQ, LV, BN, VK, RG, NS>::NT, 0) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
 }
 
-// bf16 variants served here: (lq, lv, key tile, V inside K, workgroups per CU)
-#define PKV_DL_VARIANTS(X)      \
-  X(64, 64, 64, false, 2)       \
-  X(128, 128, 64, false, 2)     \
-  X(256, 256, 32, false, 1)     \
-  X(576, 512, 32, true, 1)
+// bf16 variants served here: (lq, lv, key tile, V inside K, 32-row groups,
+// LDS stages, workgroups per CU)
+#define PKV_DL_VARIANTS(X)            \
+  X(64, 64, 64, false, 4, 4, 2)       \
+  X(128, 128, 64, false, 8, 4, 1)     \
+  X(256, 256, 32, false, 4, 4, 1)     \
+  X(576, 512, 32, true, 2, 3, 1)
 
 }  // namespace
 
 bool dl_tiling(int dtype, int lq, int lv, bool v_in_k, Tiling* t) {
   if (dtype != 0) return false;
-#define PKV_DT(Q, V, N, VK, M)                          \
+#define PKV_DT(Q, V, N, VK, RG, NS, M)                  \
   if (lq == Q && lv == V && (!VK || v_in_k)) {          \
-    t->bm = DlCfg<Q, V, N, VK>::BM;                     \
+    t->bm = DlCfg<Q, V, N, VK, RG, NS>::BM;             \
     t->bn = N;                                          \
-    t->threads = DlCfg<Q, V, N, VK>::NT;                \
+    t->threads = DlCfg<Q, V, N, VK, RG, NS>::NT;        \
     return true;                                        \
   }
   PKV_DL_VARIANTS(PKV_DT)
@@ -492,16 +583,16 @@ bool dl_tiling(int dtype, int lq, int lv, bool v_in_k, Tiling* t) {
 }
 
 hipError_t launch_dl(int lq, int lv, bool v_in_k, const AttnArgs& a, int64_t grid, hipStream_t s) {
-#define PKV_DLL(Q, V, N, VK, M) \
-  if (lq == Q && lv == V && (!VK || v_in_k)) return launch_dl_t<Q, V, N, VK, M>(a, grid, s);
+#define PKV_DLL(Q, V, N, VK, RG, NS, M) \
+  if (lq == Q && lv == V && (!VK || v_in_k)) return launch_dl_t<Q, V, N, VK, RG, NS, M>(a, grid, s);
   PKV_DL_VARIANTS(PKV_DLL)
 #undef PKV_DLL
   return hipErrorInvalidValue;
 }
 
 int dl_blocks_per_cu(int lq, int lv, bool v_in_k) {
-#define PKV_DLO(Q, V, N, VK, M) \
-  if (lq == Q && lv == V && (!VK || v_in_k)) return dl_occupancy_t<Q, V, N, VK, M>();
+#define PKV_DLO(Q, V, N, VK, RG, NS, M) \
+  if (lq == Q && lv == V && (!VK || v_in_k)) return dl_occupancy_t<Q, V, N, VK, RG, NS, M>();
   PKV_DL_VARIANTS(PKV_DLO)
 #undef PKV_DLO
   return 1;

@@ -168,12 +168,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   auto active = [&](int kt) __attribute__((always_inline)) { return wave_live && kt * BN <= P + i_hi_w; };
+  auto needs_mask = [&](int kt) __attribute__((always_inline)) { return kt * BN + BN - 1 > P + i_lo_w; };
 
-  // S^T = K Q^T for tile kt, both row blocks; the tile's K operands are all
-  // requested before the first product
-  auto qk = [&](int kt, f32x16 (&s)[RS][NKB]) __attribute__((always_inline)) {
+  typedef f32x16 STile[RS][NKB];  // S^T of one key tile, both row blocks
+  typedef bf16x8 PTile[NKB][2][RS];  // probabilities in B-operand layout
+
+  // K operands of tile kt, all requested together
+  auto read_k = [&](int kt, bf16x8 (&kv)[NQ][NKB]) __attribute__((always_inline)) {
     const char* Ks = lds + (kt & 1) * TB;
-    bf16x8 kv[NQ][NKB];
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks)
 #pragma unroll
@@ -182,6 +184,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         kv[ks][kb] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(Ks + row * D * 2 + swz_k(row, 2 * ks + hi) * 16));
       }
+  };
+  // S^T = K Q^T
+  auto qk_mfma = [&](const bf16x8 (&kv)[NQ][NKB], STile& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
@@ -193,6 +198,45 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs)
           s[rs][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks][kb], qr[rs][ks], s[rs][kb], 0, 0, 0);
+  };
+  // soft-cap, in base-2 units: cap * tanh(s * scale / cap) * log2(e)
+  auto cap_tile = [&](STile& s) __attribute__((always_inline)) {
+    if constexpr (CAP) {
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const float e = fast_exp2(s[rs][kb][rr] * (a.cap_in * 2.0f * kLog2e));
+            s[rs][kb][rr] = a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
+          }
+    }
+  };
+  // keys past a row's last visible key to -inf (tiles crossing the diagonal)
+  auto mask_tile = [&](int kt, STile& s) __attribute__((always_inline)) {
+    const int j0 = kt * BN;
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
+          s[rs][kb][rr] = j <= lim[rs] ? s[rs][kb][rr] : -INFINITY;
+        }
+  };
+  // row max over the tile (both lanes of a row)
+  auto row_max = [&](const STile& s, float (&mx)[RS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) m = fmaxf(m, s[rs][kb][rr]);
+      mx[rs] = pair_max(m);
+    }
   };
 
   f32x16 acc[RS][NDB];
@@ -207,41 +251,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     l_run[rs] = 0.0f;       // this lane's share of the running sum
   }
 
-  // softmax of S(kt) and O^T += V^T P^T
-  auto softmax_pv = [&](int kt, f32x16 (&s)[RS][NKB]) __attribute__((always_inline)) {
-    const int j0 = kt * BN;
-    const bool need_mask = j0 + BN - 1 > P + i_lo_w;
-    const char* Vs = lds + (2 + (kt & 1)) * TB;
-    float m_sub[RS];
+  // raise the reference max of a row block where the tile's row max exceeds
+  // it by more than the slack (rescaling O and the running sum); returns the
+  // value subtracted in the exponent
+  auto rescale = [&](const float (&mx)[RS], float (&m_sub)[RS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
-      if constexpr (CAP) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const float e = fast_exp2(s[rs][kb][rr] * (a.cap_in * 2.0f * kLog2e));
-            s[rs][kb][rr] = a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
-          }
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
-            s[rs][kb][rr] = j <= lim[rs] ? s[rs][kb][rr] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[rs][kb][rr]);
-      mx = pair_max(mx);
-      if constexpr (!CAP) mx *= a.scale_log2;
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref[rs] + kRescaleSlack)) {
-        const float m_new = fmaxf(m_ref[rs], mx);
+      const float m = CAP ? mx[rs] : mx[rs] * a.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(m > m_ref[rs] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_ref[rs], m);
         const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_ref[rs] - m_new);
         m_ref[rs] = m_new;
         l_run[rs] *= alpha;
@@ -250,47 +268,157 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
       m_sub[rs] = m_ref[rs] == -INFINITY ? 0.0f : m_ref[rs];
     }
-
-    const int key0 = 4 * hi + ((lane & 15) >> 2);
-    const int cofs = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  };
+  // probabilities rounded to bf16, and their sum (bf16 dot2 with ones)
+  auto probs = [&](const STile& s, const float (&m_sub)[RS], PTile& pb) __attribute__((always_inline)) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        bf16x8 pb[RS];
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs) {
+          bf16x8 q;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float x = s[rs][kb][8 * hf + e];
             const float p = CAP ? fast_exp2(x - m_sub[rs]) : fast_exp2(fmaf(x, a.scale_log2, -m_sub[rs]));
-            pb[rs][e] = (__bf16)p;
+            q[e] = (__bf16)p;
           }
-          bf16x8 q = pb[rs];
           l_run[rs] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 0, 1), ones, l_run[rs], false);
           l_run[rs] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 2, 3), ones, l_run[rs], false);
           l_run[rs] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 4, 5), ones, l_run[rs], false);
           l_run[rs] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(q, q, 6, 7), ones, l_run[rs], false);
+          pb[kb][hf][rs] = q;
         }
-        const int r0 = kb * 32 + 16 * hf + key0, r1 = r0 + 8;
+  };
+  // V^T operands of tile kt (transposing LDS reads, 4 keys per lane)
+  const int key0 = 4 * hi + ((lane & 15) >> 2);
+  const int cofs = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto read_v = [&](int kt, bf16x8 (&va)[NKB][2][NDB]) __attribute__((always_inline)) {
+    const char* Vs = lds + (2 + (kt & 1)) * TB;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
+          const int r0 = kb * 32 + 16 * hf + key0, r1 = r0 + 8;
           const int col = db * 32 + cofs;
           const char* a0 = Vs + r0 * D * 2 + swz_v(r0, col / 8) * 16 + (col % 8) * 2;
           const char* a1 = Vs + r1 * D * 2 + swz_v(r1, col / 8) * 16 + (col % 8) * 2;
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr<i16x4>)(a0));
           const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr<i16x4>)(a1));
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          va[kb][hf][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+  };
+  // O^T += V^T P^T
+  auto pv_mfma = [&](const bf16x8 (&va)[NKB][2][NDB], const PTile& pb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int rs = 0; rs < RS; ++rs)
-            acc[rs][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[rs], acc[rs][db], 0, 0, 0);
-        }
-      }
-    }
+            acc[rs][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][hf][db], pb[kb][hf][rs], acc[rs][db], 0, 0, 0);
   };
 
-  f32x16 s_cur[RS][NKB];
+  // One iteration: tile kt's softmax and P V, with tile kt+1's S = K Q^T
+  // issued alongside.  On entry sc holds S(kt) (soft-capped) and mc its
+  // unmasked row max; on exit sn and mn hold the same for kt+1.
+  constexpr int kQkMfma = NQ * NKB * RS, kPvMfma = NKB * 2 * NDB * RS;
+  auto step = [&](int kt, STile& sc, STile& sn, float (&mc)[RS], float (&mn)[RS]) __attribute__((always_inline)) {
+    // outstanding: V(kt), K(kt+1).  After the barrier both are visible, K
+    // stage kt & 1 (read by the S(kt) products) and V stage (kt+1) & 1 (read
+    // by the P(kt-1) V products) are free, and so is table slot (kt+3) & 3.
+    wait_all_mem();
+    barrier_fence();
+    if (wv == 0 && kt + 3 < kt1) fetch_slot(kt + 3);
+    if (kt + 2 < kt1) issue_k(kt + 2);
+    if (kt + 1 < kt1) issue_v(kt + 1);
+    // Tiles a wave computes are a prefix of [kt0, kt1) (causal), so when
+    // tile kt is active the products for kt+1 are made even when kt+1 is not:
+    // they then read a stale but complete K stage and are never used.  One
+    // code path keeps the register assignment the same on every trip.
+    if (active(kt)) {
+      float m_sub[RS];
+      if (needs_mask(kt)) {
+        mask_tile(kt, sc);
+        row_max(sc, mc);
+      }
+      rescale(mc, m_sub);
+      // Block A: the products of S(kt+1) with the probabilities of S(kt).
+      // Unit u issues one MFMA and then two probabilities (FMA, exp, bf16
+      // pack, dot2 into the row sum), which run on the VALU while the matrix
+      // core works; sched_barrier keeps the order as written.
+      bf16x8 kv[NQ][NKB];
+      PTile pb;
+      read_k(kt + 1, kv);
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sn[rs][kb] = f32x16{};
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      static_assert(kQkMfma * 2 == NKB * 2 * RS * 8, "two probabilities per product");
+#pragma unroll
+      for (int u = 0; u < kQkMfma; ++u) {
+        {
+          const int ks = u / (NKB * RS), kb = (u / RS) % NKB, rs = u % RS;
+          sn[rs][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks][kb], qr[rs][ks], sn[rs][kb], 0, 0, 0);
+        }
+        {
+          const int g = u / 4, e = 2 * (u % 4);  // probabilities e, e+1 of group g = (kb, hf, rs)
+          const int kb = g / (2 * RS), hf = (g / RS) % 2, rs = g % RS;
+          const float x0 = sc[rs][kb][8 * hf + e], x1 = sc[rs][kb][8 * hf + e + 1];
+          const float p0 = CAP ? fast_exp2(x0 - m_sub[rs]) : fast_exp2(fmaf(x0, a.scale_log2, -m_sub[rs]));
+          const float p1 = CAP ? fast_exp2(x1 - m_sub[rs]) : fast_exp2(fmaf(x1, a.scale_log2, -m_sub[rs]));
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          l_run[rs] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run[rs], false);
+          pb[kb][hf][rs][e] = pp[0];
+          pb[kb][hf][rs][e + 1] = pp[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Block B: P(kt) V(kt) with the soft-cap and row max of S(kt+1).
+      bf16x8 va[NKB][2][NDB];
+      read_v(kt, va);
+      float mrun[RS];
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) mrun[rs] = -INFINITY;
+      constexpr int kVals = RS * NKB * 16;  // S values of a lane, capped and max-reduced
+      constexpr int kPer = (kVals + kPvMfma - 1) / kPvMfma;
+#pragma unroll
+      for (int u = 0; u < kPvMfma; ++u) {
+        {
+          const int kb = u / (2 * NDB * RS), hf = (u / (NDB * RS)) % 2, db = (u / RS) % NDB, rs = u % RS;
+          acc[rs][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][hf][db], pb[kb][hf][rs], acc[rs][db], 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          const int v = u * kPer + k;
+          if (v < kVals) {
+            const int rs = v / (NKB * 16), kb = (v / 16) % NKB, rr = v % 16;
+            float x = sn[rs][kb][rr];
+            if constexpr (CAP) {
+              const float e = fast_exp2(x * (a.cap_in * 2.0f * kLog2e));
+              x = a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
+              sn[rs][kb][rr] = x;
+            }
+            mrun[rs] = fmaxf(mrun[rs], x);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) mn[rs] = pair_max(mrun[rs]);
+    }
+    if (wv == 0 && kt + 3 < kt1) write_ptrs(kt + 3);
+  };
+
+  STile s_a, s_b;
+  float m_a[RS], m_b[RS];
   if (kt0 < kt1) {
     // tables of the first three tiles
     if (wv == 0) {
@@ -314,28 +442,21 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       wait_vm<C::LOADS>();
     }
     barrier_fence();
-    if (active(kt0)) qk(kt0, s_cur);
+    if (active(kt0)) {
+      bf16x8 kv[NQ][NKB];
+      read_k(kt0, kv);
+      qk_mfma(kv, s_a);
+      cap_tile(s_a);
+      row_max(s_a, m_a);
+    }
   }
-
-  for (int kt = kt0; kt < kt1; ++kt) {
-    // outstanding: V(kt), K(kt+1).  After the barrier both are visible, K
-    // stage kt & 1 (read by the S(kt) products) and V stage (kt+1) & 1 (read
-    // by the P(kt-1) V products) are free, and so is table slot (kt+3) & 3.
-    wait_all_mem();
-    barrier_fence();
-    if (wv == 0 && kt + 3 < kt1) fetch_slot(kt + 3);
-    if (kt + 2 < kt1) issue_k(kt + 2);
-    if (kt + 1 < kt1) issue_v(kt + 1);
-
-    f32x16 s_next[RS][NKB];
-    if (kt + 1 < kt1 && active(kt + 1)) qk(kt + 1, s_next);
-    if (active(kt)) softmax_pv(kt, s_cur);
-#pragma unroll
-    for (int rs = 0; rs < RS; ++rs)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s_cur[rs][kb] = s_next[rs][kb];
-    if (wv == 0 && kt + 3 < kt1) write_ptrs(kt + 3);
+  // two tiles per trip so that the S tiles swap roles without copies
+  int kt = kt0;
+  for (; kt + 1 < kt1; kt += 2) {
+    step(kt, s_a, s_b, m_a, m_b);
+    step(kt + 1, s_b, s_a, m_b, m_a);
   }
+  if (kt < kt1) step(kt, s_a, s_b, m_a, m_b);
 
   // ---- epilogue
 #pragma unroll

@@ -61,10 +61,46 @@ __device__ __forceinline__ void barrier_fence() {
 // transposing LDS read, serialising the next tile's loads with this tile's
 // math.  Kernels wait for these loads themselves (vmcnt) before the barrier
 // that publishes a tile, and must not read the destination before that.
+// M0 is saved and restored around the load (the compiler reserves it), with
+// one wait state between each write of M0 and the load.
 __device__ __forceinline__ void load_lds_16(gptr<void> src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+
+// 4 bytes per active lane from global memory into LDS at lds_base + 4 * lane
+// (global_load_lds_dword); same conventions as load_lds_16.
+__device__ __forceinline__ void load_lds_4(gptr<void> src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lptr<const void>)p; }
+
+// A wave-uniform 64-bit value pinned to scalar registers (the compiler cannot
+// turn its later uses back into memory loads).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 }  // namespace pkv
