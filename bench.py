@@ -188,7 +188,7 @@ def kernel_source_sha():
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("attention.hip", "attention_dl.hip", "plan.hip"):
+    for f in ("device_common.h", "attention.hip", "attention_dl.hip", "attention_r64.hip", "plan.hip"):
         with open(os.path.join(ROOT, "paged_kv_extend_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
