@@ -109,7 +109,8 @@ typedef struct {
   int32_t num_kv_heads; /* must divide num_q_heads */
   int32_t lq;           /* head dim of q and k */
   int32_t lv;           /* head dim of v and o */
-  int64_t total_q_tokens;     /* qo_indptr[bs] */
+  int64_t total_q_tokens;     /* qo_indptr[bs]; if the device arrays hold more new-token rows than this,
+                                 the call plans no work and leaves o unwritten */
   int64_t num_prefix_indices; /* kv_indptr[bs] - kv_indptr[0] (length of kv_indices) */
   int64_t pool_slots;
   int64_t q_stride_tok, q_stride_head;

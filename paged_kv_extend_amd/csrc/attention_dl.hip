@@ -71,21 +71,27 @@ struct DlCfg {
   static constexpr int V_CHUNKS = V_BYTES / 1024;
   static constexpr int K_LOADS = K_CHUNKS / NW;  // per wave
   static constexpr int V_LOADS = V_CHUNKS / NW;
-  static constexpr int L = K_LOADS + V_LOADS;     // tile loads per wave per tile
-  static constexpr int I = BN * 8 / 256;          // row-slot loads (64 lanes x 4 bytes) per tile, wave 0
+  // Eight waves (two per SIMD): the second half of the waves issues all the
+  // loads and builds the tables, so the first half starts its products right
+  // after each barrier and the two waves of a SIMD work out of phase.
+  static constexpr bool OFFLOAD = SPLIT == 1 && NW == 8;
+  static constexpr int LOADERS = OFFLOAD ? NW / 2 : NW;   // waves that issue loads
+  static constexpr int TW = OFFLOAD ? NW / 2 : 0;         // the wave that builds tables
+  static constexpr int L = (K_LOADS + V_LOADS) * (NW / LOADERS);  // tile loads per loading wave per tile
+  static constexpr int I = BN * 8 / 256;  // row-slot loads (64 lanes x 4 bytes) per tile, table wave
   // waits at the top of an iteration (see the loop): outstanding loads allowed
   static constexpr int W_OTHER = (NS - 2) * L;
-  static constexpr int W_WAVE0 = (NS - 2) * (I + L) < 2 * L + I ? (NS - 2) * (I + L) : 2 * L + I;
+  static constexpr int W_TABLE = (NS - 2) * (I + L) < 2 * L + I ? (NS - 2) * (I + L) : 2 * L + I;
   static constexpr int XCH_BYTES = SPLIT > 1 ? NW * BN * 32 * 4 : 0;  // S^T halves exchanged
   static_assert(CK == 8 || CK == 16 || CK == 32 || CK == 72, "lq");
   static_assert(VK ? LV <= LQ : (CV == 8 || CV == 16 || CV == 32), "lv");
   static_assert(!WIDE || VK, "576-wide rows only with V inside K");
   static_assert(K_CHUNKS % NW == 0 && V_CHUNKS % NW == 0, "the same whole 1 KB loads in every wave");
-  static_assert(NS >= 3 && W_WAVE0 < 64 && W_OTHER < 64, "pipeline depth");
+  static_assert(NS >= 2 && W_TABLE < 64 && W_OTHER < 64, "pipeline depth");
   static_assert(RG == 2 || SPLIT == 1, "split variant: two row groups");
   static_assert(QD % 16 == 0 && VD % 32 == 0, "split");
   static_assert(SPLIT == 1 || WIDE, "the split interleaves halves inside 8-chunk swizzle groups");
-  static_assert(BN % 32 == 0 && BN <= 64, "key tile");
+  static_assert(BN % 32 == 0 && BN <= 128, "key tile");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r.  K: the 32 rows read at
@@ -178,7 +184,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
     }
   }
 
-  // ---- row pointer tables (two slots), built by wave 0; lane j < BN owns key kt*BN + j.
+  // ---- row pointer tables (NS slots), built by the table wave C::TW; lane e owns key kt*BN + e.
   //      Strides and per-head bases are read once into scalar registers.
   const int64_t kp_ss = uniform64(a.kp_ss), vp_ss = uniform64(a.vp_ss);
   const int64_t ke_st = uniform64(a.ke_st), ve_st = uniform64(a.ve_st);
@@ -186,9 +192,8 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
   const gptr<T> vpool_g = vpool + (int64_t)g * uniform64(a.vp_sh);
   const gptr<T> kext_g = kext + (int64_t)g * uniform64(a.ke_sh);
   const gptr<T> vext_g = vext + (int64_t)g * uniform64(a.ve_sh);
-  // pointers of key kt*BN + lane (lane < BN) for the table of tile kt
-  auto key_ptrs = [&](int kt, int64_t slot, gptr<T>& kp, gptr<T>& vp) __attribute__((always_inline)) {
-    const int j = kt * BN + lane;
+  // pointers of key j (pool slot `slot` when j is a prefix key) for a table
+  auto key_ptrs = [&](int j, int64_t slot, gptr<T>& kp, gptr<T>& vp) __attribute__((always_inline)) {
     kp = zrow;
     vp = zrow;
     if (j <= key_last) {
@@ -202,16 +207,19 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
       }
     }
   };
-  // table of tile kt from the row slots already in LDS (wave 0)
+  // table of tile kt from the row slots already in LDS (table wave)
   auto write_table = [&](int kt) __attribute__((always_inline)) {
-    if (lane < BN) {
-      gptr<T> kp, vp;
-      key_ptrs(kt, slots[kt & 3][lane], kp, vp);
-      kptr[kt % NS][lane] = kp;
-      vptr[kt % NS][lane] = vp;
+#pragma unroll
+    for (int e = lane; e < (BN > 64 ? BN : 64); e += 64) {
+      if (e < BN) {
+        gptr<T> kp, vp;
+        key_ptrs(kt * BN + e, slots[kt & 3][e], kp, vp);
+        kptr[kt % NS][e] = kp;
+        vptr[kt % NS][e] = vp;
+      }
     }
   };
-  // row slots of tile kt into LDS (wave 0): I loads of 64 lanes x 4 bytes;
+  // row slots of tile kt into LDS (table wave): I loads of 64 lanes x 4 bytes;
   // keys outside the prefix or past the last visible key read the zero row
   auto issue_slots = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
@@ -227,27 +235,37 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
   // ---- direct loads of tile kt into stage kt % NS: wave w covers bytes
   //      [(i * NW + w) * 1024, +1024) of the K and V regions
   auto issue_tile = [&](int kt) __attribute__((always_inline)) {
+    if (C::OFFLOAD && wv < C::LOADERS) return;  // waves that only compute
+    constexpr int PER = C::NW / C::LOADERS;     // chunk sets per loading wave
     const uint32_t stage = lds_addr(lds + (kt % NS) * C::STAGE_BYTES);
     // all row pointers first: each load is a compiler memory barrier
-    gptr<T> ksrc[C::K_LOADS];
-    gptr<T> vsrc[C::V_LOADS > 0 ? C::V_LOADS : 1];
+    gptr<T> ksrc[PER][C::K_LOADS];
+    gptr<T> vsrc[PER][C::V_LOADS > 0 ? C::V_LOADS : 1];
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-      const int off = (i * C::NW + wv) * 1024 + lane * 16;
-      const int row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
-      ksrc[i] = kptr[kt % NS][row] + swz_k<C>(row, p) * 8;
+    for (int q = 0; q < PER; ++q) {
+      const int vw = C::OFFLOAD ? wv - C::LOADERS + q * C::LOADERS : wv;  // wave whose chunks these are
+#pragma unroll
+      for (int i = 0; i < C::K_LOADS; ++i) {
+        const int off = (i * C::NW + vw) * 1024 + lane * 16;
+        const int row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
+        ksrc[q][i] = kptr[kt % NS][row] + swz_k<C>(row, p) * 8;
+      }
+#pragma unroll
+      for (int i = 0; i < C::V_LOADS; ++i) {
+        const int off = (i * C::NW + vw) * 1024 + lane * 16;
+        const int row = off / (LV * 2), p = (off % (LV * 2)) / 16;
+        vsrc[q][i] = vptr[kt % NS][row] + swz_v<C>(row, p) * 8;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i) {
-      const int off = (i * C::NW + wv) * 1024 + lane * 16;
-      const int row = off / (LV * 2), p = (off % (LV * 2)) / 16;
-      vsrc[i] = vptr[kt % NS][row] + swz_v<C>(row, p) * 8;
+    for (int q = 0; q < PER; ++q) {
+      const int vw = C::OFFLOAD ? wv - C::LOADERS + q * C::LOADERS : wv;
+#pragma unroll
+      for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ksrc[q][i], stage + (i * C::NW + vw) * 1024);
+#pragma unroll
+      for (int i = 0; i < C::V_LOADS; ++i)
+        load_lds_16((gptr<void>)vsrc[q][i], stage + C::K_BYTES + (i * C::NW + vw) * 1024);
     }
-#pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ksrc[i], stage + (i * C::NW + wv) * 1024);
-#pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i)
-      load_lds_16((gptr<void>)vsrc[i], stage + C::K_BYTES + (i * C::NW + wv) * 1024);
   };
 
   // wide rows: per-lane byte offsets of the operand reads inside a stage.
@@ -275,26 +293,34 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
 
   // Pipeline.  Iteration kt computes tile kt while tiles kt+1 .. kt+NS-2 are
   // in flight; after its barrier it requests the row slots of tile kt+NS+1
-  // (wave 0) and then tile kt+NS-1.  Tiles and slots past the end of the
+  // (table wave) and then tile kt+NS-1.  Tiles and slots past the end of the
   // range are requested too (zero rows, unused), so every wave has the same
   // number of loads in flight on every trip and the waits are fixed counts.
   if (kt0 < kt1) {
     // tables of the first NS-1 tiles straight from global memory
     for (int v = wv; v < NS - 1; v += C::NW) {
-      if (lane < BN) {
-        const int j = (kt0 + v) * BN + lane;
-        const int64_t slot = (j < P && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
-        gptr<T> kp, vp;
-        key_ptrs(kt0 + v, slot, kp, vp);
-        kptr[(kt0 + v) % NS][lane] = kp;
-        vptr[(kt0 + v) % NS][lane] = vp;
+#pragma unroll
+      for (int e = lane; e < (BN > 64 ? BN : 64); e += 64) {
+        if (e < BN) {
+          const int j = (kt0 + v) * BN + e;
+          const int64_t slot = (j < P && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
+          gptr<T> kp, vp;
+          key_ptrs(j, slot, kp, vp);
+          kptr[(kt0 + v) % NS][e] = kp;
+          vptr[(kt0 + v) % NS][e] = vp;
+        }
       }
     }
     __syncthreads();
+    // with two stages, the first trip's table comes from slots no earlier
+    // group carries
+    if constexpr (NS == 2) {
+      if (wv == C::TW) issue_slots(kt0 + 1);
+    }
     // the groups that iterations kt0-NS+1 .. kt0-1 would have issued
 #pragma unroll
     for (int v = 0; v < NS - 1; ++v) {
-      if (wv == 0) issue_slots(kt0 + v + 2);
+      if (wv == C::TW) issue_slots(kt0 + v + 2);
       issue_tile(kt0 + v);
     }
   }
@@ -461,12 +487,12 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
 
   // Top of iteration kt.  Tile kt was requested NS-1 groups ago and the row
   // slots of tile kt+NS-1 two groups ago (first in that group): wait until at
-  // most the later loads are outstanding.  Wave 0 then writes table kt+NS-1
+  // most the later loads are outstanding.  The table wave then writes table kt+NS-1
   // (its slot held table kt-1, issued long ago) before the barrier that
   // publishes it and tile kt.
   auto tile_top = [&](int kt) __attribute__((always_inline)) {
-    if (wv == 0) {
-      wait_vm<C::W_WAVE0>();
+    if (wv == C::TW) {
+      wait_vm<C::W_TABLE>();
       write_table(kt + NS - 1);
       wait_lds();
     } else {
@@ -474,10 +500,10 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
     }
     barrier_fence();
   };
-  // the group of iteration kt: row slots of tile kt+NS+1 (wave 0) and tile
+  // the group of iteration kt: row slots of tile kt+NS+1 (table wave) and tile
   // kt+NS-1 into stage (kt-1) % NS, which tile kt-1 no longer needs
   auto issue_group = [&](int kt) __attribute__((always_inline)) {
-    if (wv == 0) issue_slots(kt + NS + 1);
+    if (wv == C::TW) issue_slots(kt + NS + 1);
     issue_tile(kt + NS - 1);
   };
 
@@ -562,7 +588,7 @@ int dl_occupancy_t() {
 // LDS stages, workgroups per CU)
 #define PKV_DL_VARIANTS(X)            \
   X(64, 64, 64, false, 4, 4, 2)       \
-  X(128, 128, 64, false, 8, 4, 1)     \
+  X(128, 128, 128, false, 8, 2, 1)    \
   X(256, 256, 32, false, 4, 4, 1)     \
   X(576, 512, 32, true, 2, 3, 1)
 

@@ -96,7 +96,7 @@ struct PlanArgs {
   void* zero_row;    // zeroed by the planner: kZeroRowBytes bytes
   WorkItem* work;    // [max_work]
   MergeItem* merge;  // [max_merge]
-  int32_t* scratch;  // [bs + 1 + 8 * max_items]
+  int32_t* scratch;  // [3 * bs + 1 + 3 * max_items], used when the batch exceeds the LDS arrays
 };
 
 // Kernel variants: (dtype, lq, lv).  Returns false when unsupported.

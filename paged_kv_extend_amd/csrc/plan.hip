@@ -26,151 +26,168 @@
 namespace pkv {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBuckets = 256;
 constexpr int kMaxXcd = 8;
-constexpr int kSeqLds = 8192;  // sequence offsets kept in LDS up to this batch size
+constexpr int kSeqLds = 4096;   // per-sequence arrays kept in LDS up to this batch size
+constexpr int kItemLds = 8192;  // per-item arrays kept in LDS up to this many items
 
 struct Shared {
-  int32_t wave_tot[kWaves];
-  int32_t wave_tot3[kWaves][3];
-  int64_t red[kWaves];
+  int64_t wave_tot[kWaves][3];
   int32_t bucket[kMaxXcd * kBuckets];
   int32_t bin_count[kMaxXcd];
   int32_t bin_start[kMaxXcd];
-  int32_t seq_base[kSeqLds + 1];
+  int32_t seq_base[kSeqLds + 1];  // first item of sequence b
+  int32_t seq_e[kSeqLds];         // new tokens E_b
+  int32_t seq_p[kSeqLds];         // prefix tokens P_b
+  int32_t cost[kItemLds];         // KV tiles of item n
+  int32_t cum[kItemLds];          // exclusive running sum of costs
+  int32_t pm[kItemLds];           // partial base << 16 | merge index (split items)
 };
 
-// Exclusive block-wide scan of one int per thread; returns the block total.
-__device__ int32_t block_excl_scan(int32_t v, int32_t* total, Shared& sh) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t u = __shfl_up(inc, off);
-    if (lane >= off) inc += u;
-  }
-  if (lane == 63) sh.wave_tot[w] = inc;
-  __syncthreads();
-  int32_t before = 0, all = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const int32_t t = sh.wave_tot[i];
-    before += i < w ? t : 0;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return before + inc - v;
+// Inclusive scan over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then the row totals broadcast to later rows.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
 }
 
-// Exclusive block-wide scans of three ints per thread in one pass.
-__device__ int3 block_excl_scan3(int3 v, int3* total, Shared& sh) {
+// Exclusive block-wide scans of up to three 64-bit-summed ints per thread
+// (each value and each total must fit 31 bits); returns the scans, sets the totals.
+template <int N>
+__device__ void block_excl_scan(const int (&v)[N], int (&ex)[N], int64_t (&total)[N], Shared& sh) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int3 inc = v;
+  int inc[N];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int ux = __shfl_up(inc.x, off), uy = __shfl_up(inc.y, off), uz = __shfl_up(inc.z, off);
-    if (lane >= off) {
-      inc.x += ux;
-      inc.y += uy;
-      inc.z += uz;
-    }
-  }
+  for (int i = 0; i < N; ++i) inc[i] = wave_incl_scan(v[i]);
   if (lane == 63) {
-    sh.wave_tot3[w][0] = inc.x;
-    sh.wave_tot3[w][1] = inc.y;
-    sh.wave_tot3[w][2] = inc.z;
-  }
-  __syncthreads();
-  int3 before = make_int3(0, 0, 0), all = make_int3(0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const int tx = sh.wave_tot3[i][0], ty = sh.wave_tot3[i][1], tz = sh.wave_tot3[i][2];
-    if (i < w) {
-      before.x += tx;
-      before.y += ty;
-      before.z += tz;
-    }
-    all.x += tx;
-    all.y += ty;
-    all.z += tz;
+    for (int i = 0; i < N; ++i) sh.wave_tot[w][i] = inc[i];
   }
   __syncthreads();
-  *total = all;
-  return make_int3(before.x + inc.x - v.x, before.y + inc.y - v.y, before.z + inc.z - v.z);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    int64_t before = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const int64_t t = sh.wave_tot[k][i];
+      before += k < w ? t : 0;
+      all += t;
+    }
+    ex[i] = (int)before + inc[i] - v[i];
+    total[i] = all;
+  }
+  __syncthreads();
 }
 
 __device__ int64_t block_sum(int64_t v, Shared& sh) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) sh.wave_tot[threadIdx.x >> 6][0] = v;
   __syncthreads();
   int64_t t = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += sh.red[w];
+  for (int w = 0; w < kWaves; ++w) t += sh.wave_tot[w][0];
   __syncthreads();
   return t;
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-__global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
-  __shared__ Shared sh;
+// Per-item arrays in LDS when the batch fits (the only global reads are the
+// indptrs), else in the global scratch.  Items and sequences are handed out
+// in contiguous runs per thread, so each scan is a local pass, one block
+// scan and a second local pass, whatever the batch size.
+template <bool LDS_ARRAYS>
+__device__ void plan_body(const PlanArgs& a, Shared& sh) {
   const int tid = threadIdx.x;
   const int G = a.group, BM = a.bm, BN = a.bn, H = a.num_kv_heads;
-  // global scratch: seq_base[bs+1] | cost | part_base | merge_idx | b | g | t | cum  (per item)
-  int32_t* seq_base_g = a.scratch;
-  int32_t* cost_of = seq_base_g + a.bs + 1;
-  int32_t* part_base = cost_of + a.max_items;
-  int32_t* merge_idx = part_base + a.max_items;
-  int32_t* item_b = merge_idx + a.max_items;
-  int32_t* item_g = item_b + a.max_items;
-  int32_t* item_t = item_g + a.max_items;
-  int32_t* cum_cost = item_t + a.max_items;  // exclusive running sum of item costs
-  const bool seq_in_lds = a.bs <= kSeqLds;
-  int32_t* seq_base = seq_in_lds ? sh.seq_base : seq_base_g;
+  // global scratch: seq_base[bs+1] | E[bs] | P[bs] | cost | cum | pm  (per item)
+  int32_t* seq_base = LDS_ARRAYS ? sh.seq_base : a.scratch;
+  int32_t* seq_e = LDS_ARRAYS ? sh.seq_e : a.scratch + a.bs + 1;
+  int32_t* seq_p = LDS_ARRAYS ? sh.seq_p : a.scratch + 2 * a.bs + 1;
+  int32_t* cost_of = LDS_ARRAYS ? sh.cost : a.scratch + 3 * a.bs + 1;
+  int32_t* cum_cost = LDS_ARRAYS ? sh.cum : cost_of + a.max_items;
+  int32_t* pm = LDS_ARRAYS ? sh.pm : cum_cost + a.max_items;
 
-  // zero row read for keys past a sequence
-  for (int i = tid; i < kZeroRowBytes / 16; i += kThreads)
-    reinterpret_cast<uint4*>(a.zero_row)[i] = make_uint4(0, 0, 0, 0);
-
-  // 1. items per sequence, H * ceil(E_b G / BM); exclusive scan in runs of kThreads
-  int32_t carry = 0;
-  for (int base = 0; base < a.bs; base += kThreads) {
-    const int b = base + tid;
-    int32_t v = 0;
-    if (b < a.bs) v = H * ceil_div((a.qo_indptr[b + 1] - a.qo_indptr[b]) * G, BM);
-    int32_t tot;
-    const int32_t ex = block_excl_scan(v, &tot, sh);
-    if (b < a.bs) seq_base[b] = carry + ex;
-    carry += tot;
+  // 1. per sequence: E, P and items H * ceil(E G / BM), exclusive scan
+  const int spt = ceil_div(a.bs, kThreads);  // sequences per thread
+  const int s0 = min(a.bs, tid * spt), s1 = min(a.bs, s0 + spt);
+  int local = 0;
+  for (int b = s0; b < s1; ++b) {
+    const int E = a.qo_indptr[b + 1] - a.qo_indptr[b];
+    const int P = a.kv_indptr[b + 1] - a.kv_indptr[b];
+    seq_e[b] = E;
+    seq_p[b] = P;
+    local += H * ceil_div(E * G, BM);
   }
-  const int n_items = carry;
-  if (tid == 0) seq_base[a.bs] = n_items;
+  {
+    int v[1] = {local}, ex[1];
+    int64_t tot[1];
+    block_excl_scan<1>(v, ex, tot, sh);
+    int run = ex[0];
+    for (int b = s0; b < s1; ++b) {
+      seq_base[b] = run;
+      run += H * ceil_div(seq_e[b] * G, BM);
+    }
+    if (tid == 0) seq_base[a.bs] = (int)tot[0];
+    local = (int)tot[0];
+  }
+  const int n_items = local;
   __syncthreads();
+  if (n_items > a.max_items) {
+    // qo_indptr holds more rows than the descriptor's total_q_tokens allows:
+    // plan nothing (the attention and merge launches then do nothing)
+    if (tid == 0) {
+      a.hdr->num_work = 0;
+      a.hdr->num_merge = 0;
+      a.hdr->num_chunks = 0;
+      a.hdr->num_items = n_items;
+    }
+    return;
+  }
 
-  // 2. cost of every item in KV tiles; items ordered (b, g, t)
-  int64_t my_total = 0;
-  for (int n = tid; n < n_items; n += kThreads) {
+  // (b, g, t) of item n: items are ordered (b, g, t)
+  auto decode = [&](int n, int& b, int& g, int& t) {
     int lo = 0, hi = a.bs - 1;  // last b with seq_base[b] <= n
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (seq_base[mid] <= n) lo = mid; else hi = mid - 1;
     }
-    const int b = lo;
-    const int E = a.qo_indptr[b + 1] - a.qo_indptr[b];
-    const int P = a.kv_indptr[b + 1] - a.kv_indptr[b];
-    const int T = ceil_div(E * G, BM);
-    const int local = n - seq_base[b];
-    const int t = local % T;
-    const int row_hi = min((t + 1) * BM, E * G) - 1;
-    const int cost = ceil_div(P + row_hi / G + 1, BN);
-    cost_of[n] = cost;
-    item_b[n] = b;
-    item_g[n] = local / T;
-    item_t[n] = t;
-    my_total += cost;
+    b = lo;
+    const int T = ceil_div(seq_e[b] * G, BM);
+    const int loc = n - seq_base[b];
+    g = loc / T;
+    t = loc % T;
+  };
+  const int ipt = ceil_div(n_items, kThreads);  // items per thread, contiguous
+  const int n0 = min(n_items, tid * ipt), n1 = min(n_items, n0 + ipt);
+
+  // 2. cost of every item in KV tiles (keys up to the last token of its rows)
+  int64_t my_total = 0;
+  if (n0 < n1) {
+    int b, g, t;
+    decode(n0, b, g, t);
+    for (int n = n0; n < n1; ++n) {
+      const int row_hi = min((t + 1) * BM, seq_e[b] * G) - 1;
+      const int cost = ceil_div(seq_p[b] + row_hi / G + 1, BN);
+      cost_of[n] = cost;
+      my_total += cost;
+      // next item: next tile, next head, or next sequence
+      const int T = ceil_div(seq_e[b] * G, BM);
+      if (++t == T) {
+        t = 0;
+        if (++g == H) {
+          g = 0;
+          do ++b; while (b < a.bs && seq_e[b] == 0);
+        }
+      }
+    }
   }
   const int64_t total = block_sum(my_total, sh);
 
@@ -180,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
   if (chunk < a.min_chunk) chunk = a.min_chunk;
   for (;;) {
     int64_t parts = 0;
-    for (int n = tid; n < n_items; n += kThreads) {
+    for (int n = n0; n < n1; ++n) {
       const int c = cost_of[n];
       if (c > chunk) parts += (c + chunk - 1) / chunk;
     }
@@ -188,27 +205,30 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     if (parts <= a.part_budget) break;
     chunk *= 2;
   }
+  auto pieces = [&](int c) { return c > chunk ? (int)((c + chunk - 1) / chunk) : 1; };
 
-  // 4. partial-slot and merge-record offsets of split items, running cost (scans in runs)
-  int32_t pcarry = 0, mcarry = 0, ccarry = 0;
-  for (int base = 0; base < n_items; base += kThreads) {
-    const int n = base + tid;
-    int k = 1, c = 0;
-    if (n < n_items) {
-      c = cost_of[n];
-      k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
+  // 4. partial-slot and merge-record offsets of split items, running cost
+  int mcarry;
+  {
+    int v[3] = {0, 0, 0}, ex[3];
+    int64_t tot[3];
+    for (int n = n0; n < n1; ++n) {
+      const int c = cost_of[n], k = pieces(c);
+      v[0] += k > 1 ? k : 0;
+      v[1] += k > 1 ? 1 : 0;
+      v[2] += c;
     }
-    int3 tot;
-    const int3 ex = block_excl_scan3(make_int3(k > 1 ? k : 0, k > 1 ? 1 : 0, c), &tot, sh);
-    if (n < n_items) {
-      part_base[n] = pcarry + ex.x;
-      merge_idx[n] = mcarry + ex.y;
-      cum_cost[n] = ccarry + ex.z;
+    block_excl_scan<3>(v, ex, tot, sh);
+    for (int n = n0; n < n1; ++n) {
+      const int c = cost_of[n], k = pieces(c);
+      // partial bases < part_budget <= 4096 and merge indices < part_budget fit 16 bits each
+      pm[n] = (ex[0] << 16) | ex[1];
+      cum_cost[n] = ex[2];
+      ex[0] += k > 1 ? k : 0;
+      ex[1] += k > 1 ? 1 : 0;
+      ex[2] += c;
     }
-    const int32_t ptot = tot.x, mtot = tot.y, ctot = tot.z;
-    pcarry += ptot;
-    mcarry += mtot;
-    ccarry += ctot;
+    mcarry = (int)tot[1];
   }
 
   // 5. XCD bin of every chunk (midpoint rule), then heaviest first inside a bin
@@ -219,15 +239,15 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     const int64_t mid2 = 2 * (int64_t)cum_cost[n] + k0 + k1;  // twice the chunk midpoint
     return (int)min<int64_t>(X - 1, mid2 * X / (2 * (total > 0 ? total : 1)));
   };
+  constexpr int kPer = kMaxXcd * kBuckets / kThreads;  // counters per thread in the scan
   int32_t my_chunks = 0;
   int max_count = 0;
   for (int attempt = 0; attempt < 2; ++attempt) {
     for (int i = tid; i < kMaxXcd * kBuckets; i += kThreads) sh.bucket[i] = 0;
     __syncthreads();
     my_chunks = 0;
-    for (int n = tid; n < n_items; n += kThreads) {
-      const int c = cost_of[n];
-      const int k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
+    for (int n = n0; n < n1; ++n) {
+      const int c = cost_of[n], k = pieces(c);
       my_chunks += k;
       for (int s = 0; s < k; ++s) {
         const int k0 = (int)((int64_t)c * s / k), k1 = (int)((int64_t)c * (s + 1) / k);
@@ -235,20 +255,31 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
       }
     }
     __syncthreads();
-    // one exclusive scan over all (bin, class) counters, two per thread; a bin's
-    // ranks are offsets from its first counter's scan value
+    // one exclusive scan over all (bin, class) counters, kPer per thread; a
+    // bin's ranks are offsets from its first counter's scan value
     {
-      const int i0 = 2 * tid;
-      const int32_t v0 = i0 < X * kBuckets ? sh.bucket[i0] : 0;
-      const int32_t v1 = i0 + 1 < X * kBuckets ? sh.bucket[i0 + 1] : 0;
-      int32_t tot;
-      const int32_t ex = block_excl_scan(v0 + v1, &tot, sh);
-      if (i0 < X * kBuckets) sh.bucket[i0] = ex;
-      if (i0 + 1 < X * kBuckets) sh.bucket[i0 + 1] = ex + v0;
+      int cnt[kPer], sum = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int idx = tid * kPer + i;
+        cnt[i] = idx < X * kBuckets ? sh.bucket[idx] : 0;
+        sum += cnt[i];
+      }
+      int v[1] = {sum}, ex[1];
+      int64_t tot[1];
+      block_excl_scan<1>(v, ex, tot, sh);
+      int run = ex[0];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int idx = tid * kPer + i;
+        if (idx < X * kBuckets) sh.bucket[idx] = run;
+        run += cnt[i];
+      }
       __syncthreads();
       if (tid < X) {
         sh.bin_start[tid] = sh.bucket[tid * kBuckets];
-        sh.bin_count[tid] = (tid + 1 < X ? sh.bucket[(tid + 1) * kBuckets] : tot) - sh.bucket[tid * kBuckets];
+        sh.bin_count[tid] =
+            (tid + 1 < X ? sh.bucket[(tid + 1) * kBuckets] : (int)tot[0]) - sh.bucket[tid * kBuckets];
       }
       __syncthreads();
     }
@@ -258,35 +289,46 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     X = 1;  // bins too uneven for the grid: plain heaviest-first order
     __syncthreads();
   }
-  for (int n = tid; n < n_items; n += kThreads) {
-    const int c = cost_of[n];
-    const int k = c > chunk ? (int)((c + chunk - 1) / chunk) : 1;
-    const int b = item_b[n], ig = item_g[n], itt = item_t[n];
-    for (int s = 0; s < k; ++s) {
-      const int k0 = (int)((int64_t)c * s / k), k1 = (int)((int64_t)c * (s + 1) / k);
-      const int x = bin_of(n, k0, k1);
-      const int rank = atomicAdd(&sh.bucket[x * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1) -
-                       sh.bin_start[x];
-      WorkItem w;
-      w.b = b;
-      w.g = ig;
-      w.t = itt;
-      w.kt_begin = k0;
-      w.kt_end = k1;
-      w.part = k > 1 ? part_base[n] + s : -1;
-      w.pad0 = 0;
-      w.pad1 = 0;
-      a.work[rank * X + x] = w;
-    }
-    if (k > 1) {
-      MergeItem m;
-      m.b = b;
-      m.g = ig;
-      m.t = itt;
-      m.part_base = part_base[n];
-      m.n = k;
-      m.pad0 = m.pad1 = m.pad2 = 0;
-      a.merge[merge_idx[n]] = m;
+  if (n0 < n1) {
+    int b, ig, itt;
+    decode(n0, b, ig, itt);
+    for (int n = n0; n < n1; ++n) {
+      const int c = cost_of[n], k = pieces(c);
+      const int pbase = (int)((uint32_t)pm[n] >> 16), midx = pm[n] & 0xFFFF;
+      for (int s = 0; s < k; ++s) {
+        const int k0 = (int)((int64_t)c * s / k), k1 = (int)((int64_t)c * (s + 1) / k);
+        const int x = bin_of(n, k0, k1);
+        const int rank = atomicAdd(&sh.bucket[x * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1) -
+                         sh.bin_start[x];
+        WorkItem w;
+        w.b = b;
+        w.g = ig;
+        w.t = itt;
+        w.kt_begin = k0;
+        w.kt_end = k1;
+        w.part = k > 1 ? pbase + s : -1;
+        w.pad0 = 0;
+        w.pad1 = 0;
+        a.work[rank * X + x] = w;
+      }
+      if (k > 1) {
+        MergeItem m;
+        m.b = b;
+        m.g = ig;
+        m.t = itt;
+        m.part_base = pbase;
+        m.n = k;
+        m.pad0 = m.pad1 = m.pad2 = 0;
+        a.merge[midx] = m;
+      }
+      const int T = ceil_div(seq_e[b] * G, BM);
+      if (++itt == T) {
+        itt = 0;
+        if (++ig == H) {
+          ig = 0;
+          do ++b; while (b < a.bs && seq_e[b] == 0);
+        }
+      }
     }
   }
   // unused slots of shorter bins hold empty items
@@ -310,6 +352,17 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     a.hdr->total_tiles = (int32_t)total;
     a.hdr->num_items = n_items;
   }
+}
+
+__global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
+  __shared__ Shared sh;
+  // zero row read for keys past a sequence
+  for (int i = threadIdx.x; i < kZeroRowBytes / 16; i += kThreads)
+    reinterpret_cast<uint4*>(a.zero_row)[i] = make_uint4(0, 0, 0, 0);
+  if (a.bs <= kSeqLds && a.max_items <= kItemLds)
+    plan_body<true>(a, sh);
+  else
+    plan_body<false>(a, sh);
 }
 
 }  // namespace

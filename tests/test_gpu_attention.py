@@ -6,6 +6,8 @@ sizes in the launch configuration the benchmark uses, edge cases, and
 bitwise invariants (determinism, pool-slot permutation, batch order).
 """
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -93,6 +95,35 @@ def test_long_prefix_split_mla():
     assert pkv.extend_attention_kernel_name(desc, dev["k_ext"], dev["v_ext"], dev["k_pool"],
                                             dev["v_pool"]) == "attn_dl_kernel"
     parity_full(w, "mla-bs1-P24000")
+
+
+def test_planner_arrays_in_global_memory():
+    # more sequences, or more row tiles, than the planner keeps in LDS
+    w = wl.custom(dtype="bf16", prefix_lens=[3] * 4500, extend_lens=[1] * 4500, hq=4, hkv=2, lq=64, lv=64)
+    parity_full(w, "bs4500")
+    w = wl.custom(dtype="bf16", prefix_lens=[5] * 1100, extend_lens=[1] * 1100, hq=64, hkv=8, lq=64, lv=64)
+    parity_full(w, "items9352")
+
+
+def test_rows_beyond_descriptor_plan_nothing():
+    # qo_indptr names far more rows than the descriptor's total_q_tokens (32 row
+    # tiles against a bound of 4): no work, o untouched
+    w = wl.custom(dtype="bf16", prefix_lens=[40], extend_lens=[2000], hq=4, hkv=2, lq=128, lv=128)
+    dev = wl.to_torch(w)
+    desc = pkv.make_desc(dev["q"], dev["k_ext"], dev["v_ext"], dev["o"], dev["k_pool"], dev["v_pool"], w.bs,
+                         w.num_prefix)
+    desc.total_q_tokens = 10
+    nbytes = pkv.extend_attention_workspace_size(desc)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev["q"].device)
+    lib = pkv.library()
+    p = lambda t: t.data_ptr()
+    rc = lib.extend_attention_fwd(p(dev["q"]), p(dev["k_ext"]), p(dev["v_ext"]), p(dev["o"]), p(dev["k_pool"]),
+                                  p(dev["v_pool"]), p(dev["qo_indptr"]), p(dev["kv_indptr"]), p(dev["kv_indices"]),
+                                  0.0, 0.0, ctypes.byref(desc), p(ws), nbytes,
+                                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.isnan(dev["o"].float()).all(), "rows were written although the plan should be empty"
 
 
 def test_empty_batch_is_noop():
