@@ -35,16 +35,25 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// s_waitcnt encodings (gfx9: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+// s_waitcnt encodings (gfx9: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+// Each wait is also a compiler memory fence: the loads it guards (LDS data
+// written by global-to-LDS loads the compiler does not track) stay after it.
 // vmcnt(0) lgkmcnt(0)
-__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0x7 << 4); }
+__device__ __forceinline__ void wait_all_mem() {
+  __builtin_amdgcn_s_waitcnt(0x7 << 4);
+  asm volatile("" ::: "memory");
+}
 // lgkmcnt(0) only: LDS traffic done, global loads may stay in flight
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
 // vmcnt(N) lgkmcnt(0)
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+  asm volatile("" ::: "memory");
 }
 
 // Workgroup barrier that is also a compiler memory fence (no LDS access is
@@ -62,7 +71,10 @@ __device__ __forceinline__ void barrier_fence() {
 // math.  Kernels wait for these loads themselves (vmcnt) before the barrier
 // that publishes a tile, and must not read the destination before that.
 // M0 is saved and restored around the load (the compiler reserves it), with
-// one wait state between each write of M0 and the load.
+// one wait state between each write of M0 and the load.  No memory clobber:
+// the asm is volatile, so it keeps its order against the fenced waits and
+// barriers that bound every use of its destination, and the compiler stays
+// free to schedule the LDS operand reads of other stages around it.
 __device__ __forceinline__ void load_lds_16(gptr<void> src, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
@@ -73,8 +85,7 @@ __device__ __forceinline__ void load_lds_16(gptr<void> src, uint32_t lds_base) {
       "s_nop 0\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(lds_base)
-      : "memory");
+      : "v"(src), "s"(lds_base));
 }
 
 // 4 bytes per active lane from global memory into LDS at lds_base + 4 * lane
@@ -89,8 +100,7 @@ __device__ __forceinline__ void load_lds_4(gptr<void> src, uint32_t lds_base) {
       "s_nop 0\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(lds_base)
-      : "memory");
+      : "v"(src), "s"(lds_base));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lptr<const void>)p; }
