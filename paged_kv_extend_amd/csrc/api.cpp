@@ -1,7 +1,7 @@
 // C ABI of libpkv.so: host-side argument checks, workspace sizing and the
-// stream-ordered launch sequence (plan -> attention -> merge).  Checks use
-// only host-visible sizes, so no call reads device memory or waits for the
-// device.
+// stream-ordered launch sequence (plan, then attention, whose last chunk of
+// a split item merges it).  Checks use only host-visible sizes, so no call
+// reads device memory or waits for the device.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -421,8 +421,6 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   }
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   if (ev.second) (void)hipEventRecord(ev.second, s);
-  e = pkv::launch_merge(d.dtype, d.lv, a, t.bm, pb.max_merge, s);
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -38,6 +38,7 @@
 //    rounding of probabilities), so fp32 results carry fp32 products.
 #include <type_traits>
 
+#include "merge_tile.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -430,55 +431,7 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
       }
     }
     if (hi == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref, l_tot);
-  }
-}
-
-// Merge of the chunks of split items, in chunk order (deterministic):
-//   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s acc_s 2^(m_s - M) / L
-// which is the log-sum-exp state merge (page "flashinfer_backend.py",
-// forward_extend, merge_state of the ragged and paged partial outputs).
-// One workgroup per split item; thread = (row, 4 columns).
-template <bool F32, int LV>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int bm) {
-  using T = typename Elem<F32>::T;
-  if ((int)blockIdx.x >= a.hdr->num_merge) return;
-  const MergeItem mi = a.merge[blockIdx.x];
-  const int G = a.group;
-  const int q0 = a.qo_indptr[mi.b], E = a.qo_indptr[mi.b + 1] - q0;
-  const int R = E * G;
-  constexpr int V4 = LV / 4;
-  for (int idx = threadIdx.x; idx < bm * V4; idx += 256) {
-    const int row = idx / V4, d = (idx % V4) * 4;
-    const int r = mi.t * bm + row;
-    if (r >= R) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < mi.n; ++s) M = fmaxf(M, a.part_ml[((int64_t)(mi.part_base + s) * bm + row) * 2]);
-    float L = 0.0f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < mi.n; ++s) {
-      const int64_t prow = (int64_t)(mi.part_base + s) * bm + row;
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
-      const float w = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
-      L += ml.y * w;
-      const float4 v = *reinterpret_cast<const float4*>(a.part_acc + prow * LV + d);
-      o.x += v.x * w;
-      o.y += v.y * w;
-      o.z += v.z * w;
-      o.w += v.w * w;
-    }
-    const float inv = 1.0f / L;
-    const int tok = r / G, head = mi.g * G + r % G;
-    T* orow = reinterpret_cast<T*>(a.o) + (int64_t)(q0 + tok) * a.o_st + (int64_t)head * a.o_sh + d;
-    if constexpr (F32) {
-      *reinterpret_cast<float4*>(orow) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-    } else {
-      bf16x4 ov;
-      ov[0] = (__bf16)(o.x * inv);
-      ov[1] = (__bf16)(o.y * inv);
-      ov[2] = (__bf16)(o.z * inv);
-      ov[3] = (__bf16)(o.w * inv);
-      *reinterpret_cast<bf16x4*>(orow) = ov;
-    }
+    finish_split<F32, LV>(a, it.merge, BM);
   }
 }
 
@@ -544,24 +497,6 @@ int attention_blocks_per_cu(int dtype, int lq, int lv) {
   PKV_VARIANTS(PKV_OCC)
 #undef PKV_OCC
   return 1;
-}
-
-hipError_t launch_merge(int dtype, int lv, const AttnArgs& a, int bm, int64_t grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
-  const bool f32 = dtype == 1;
-#define PKV_MERGE(F, V)                                                                             \
-  if (f32 == F && lv == V) {                                                                        \
-    hipLaunchKernelGGL((merge_kernel<F, V>), dim3((unsigned)grid), dim3(256), 0, s, a, bm);          \
-    return hipGetLastError();                                                                       \
-  }
-  PKV_MERGE(false, 64)
-  PKV_MERGE(false, 128)
-  PKV_MERGE(false, 256)
-  PKV_MERGE(false, 512)
-  PKV_MERGE(true, 64)
-  PKV_MERGE(true, 128)
-#undef PKV_MERGE
-  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

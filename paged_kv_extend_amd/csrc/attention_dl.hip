@@ -29,6 +29,7 @@
 //    "cpu_graph_runner.py", qkv_proj_with_rope: v = k.narrow(-1, 0, lv)), only
 //    the K tile is loaded and the V^T operand is read from it.
 #include "device_common.h"
+#include "merge_tile.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -558,6 +559,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
       }
     }
     if (hi == 0 && half == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref, l_tot);
+    finish_split<false, LV>(a, it.merge, BM);
   }
 }
 

@@ -16,12 +16,16 @@ namespace pkv {
 // one chunk of a split item and writes unnormalised partial state into
 // partial slot `part`.  b < 0 marks an empty slot.
 struct WorkItem {
-  int32_t b, g, t, kt_begin, kt_end, part, pad0, pad1;
+  int32_t b, g, t, kt_begin, kt_end, part;
+  int32_t merge;  // merge record of a split item's chunk, else -1
+  int32_t pad0;
 };
 
 // A split item whose chunks occupy partial slots [part_base, part_base + n).
 struct MergeItem {
-  int32_t b, g, t, part_base, n, pad0, pad1, pad2;
+  int32_t b, g, t, part_base, n;
+  int32_t arrived;  // chunks whose partial state is written (zeroed by the planner)
+  int32_t pad0, pad1;
 };
 
 // Planner output header at the start of the workspace.
@@ -78,7 +82,7 @@ struct AttnArgs {
   const void* zero_row;  // >= max(lq, lv) zero elements, read for keys past a sequence
   const PlanHeader* hdr;
   const WorkItem* work;
-  const MergeItem* merge;
+  MergeItem* merge;
   float* part_acc;   // [part][bm][lv]
   float* part_ml;    // [part][bm][2]: running max (base-2 units), sum of weights
 };
@@ -103,7 +107,6 @@ struct PlanArgs {
 bool attn_tiling(int dtype, int lq, int lv, Tiling* t);
 hipError_t launch_attention(int dtype, int lq, int lv, const AttnArgs& a, int64_t grid,
                             hipStream_t s);
-hipError_t launch_merge(int dtype, int lv, const AttnArgs& a, int bm, int64_t grid, hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_index_build(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
                               const int32_t* extend_start_loc, const int32_t* extend_seq_lens,

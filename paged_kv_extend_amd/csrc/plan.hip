@@ -307,8 +307,8 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
         w.kt_begin = k0;
         w.kt_end = k1;
         w.part = k > 1 ? pbase + s : -1;
+        w.merge = k > 1 ? midx : -1;
         w.pad0 = 0;
-        w.pad1 = 0;
         a.work[rank * X + x] = w;
       }
       if (k > 1) {
@@ -318,7 +318,8 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
         m.t = itt;
         m.part_base = pbase;
         m.n = k;
-        m.pad0 = m.pad1 = m.pad2 = 0;
+        m.arrived = 0;
+        m.pad0 = m.pad1 = 0;
         a.merge[midx] = m;
       }
       const int T = ceil_div(seq_e[b] * G, BM);
@@ -338,7 +339,8 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       w.b = -1;
       w.g = w.t = w.kt_begin = w.kt_end = 0;
       w.part = -1;
-      w.pad0 = w.pad1 = 0;
+      w.merge = -1;
+      w.pad0 = 0;
       a.work[rank * X + x] = w;
     }
   }
