@@ -34,7 +34,7 @@ constexpr int kSeqLds = 4096;   // per-sequence arrays kept in LDS up to this ba
 constexpr int kItemLds = 8192;  // per-item arrays kept in LDS up to this many items
 
 struct Shared {
-  int64_t wave_tot[kWaves][3];
+  int64_t wave_tot[kWaves][4];
   int32_t bucket[kMaxXcd * kBuckets];
   int32_t bin_count[kMaxXcd];
   int32_t bin_start[kMaxXcd];
@@ -207,18 +207,20 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   }
   auto pieces = [&](int c) { return c > chunk ? (int)((c + chunk - 1) / chunk) : 1; };
 
-  // 4. partial-slot and merge-record offsets of split items, running cost
-  int mcarry;
+  // 4. partial-slot and merge-record offsets of split items, running cost,
+  //    and the number of chunks
+  int mcarry, n_chunks;
   {
-    int v[3] = {0, 0, 0}, ex[3];
-    int64_t tot[3];
+    int v[4] = {0, 0, 0, 0}, ex[4];
+    int64_t tot[4];
     for (int n = n0; n < n1; ++n) {
       const int c = cost_of[n], k = pieces(c);
       v[0] += k > 1 ? k : 0;
       v[1] += k > 1 ? 1 : 0;
       v[2] += c;
+      v[3] += k;
     }
-    block_excl_scan<3>(v, ex, tot, sh);
+    block_excl_scan<4>(v, ex, tot, sh);
     for (int n = n0; n < n1; ++n) {
       const int c = cost_of[n], k = pieces(c);
       // partial bases < part_budget <= 4096 and merge indices < part_budget fit 16 bits each
@@ -229,28 +231,47 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       ex[2] += c;
     }
     mcarry = (int)tot[1];
+    n_chunks = (int)tot[3];
   }
 
   // 5. XCD bin of every chunk (midpoint rule), then heaviest first inside a bin
-  const int64_t cls_div = (chunk + kBuckets - 1) / kBuckets;  // chunk sizes are <= chunk
-  auto size_class = [&](int sz) { return (int)min<int64_t>(kBuckets - 1, (sz - 1) / cls_div); };
+  // size class of a chunk of sz tiles (sizes are <= chunk); only orders
+  // chunks, so the float rounding near class edges is harmless
+  const float cls_scale = (float)kBuckets / (float)chunk;
+  auto size_class = [&](int sz) { return min(kBuckets - 1, (int)((float)(sz - 1) * cls_scale)); };
   int X = a.xcds < 1 ? 1 : (a.xcds > kMaxXcd ? kMaxXcd : a.xcds);
+  // XCD of a chunk: which of X equal-cost ranges holds its midpoint (twice the
+  // midpoint against twice the range ends; integer compares only)
+  int64_t bnd2[kMaxXcd];
+#pragma unroll
+  for (int x = 0; x < kMaxXcd; ++x) bnd2[x] = 2 * ((x + 1) * total / X);
   auto bin_of = [&](int n, int k0, int k1) {
-    const int64_t mid2 = 2 * (int64_t)cum_cost[n] + k0 + k1;  // twice the chunk midpoint
-    return (int)min<int64_t>(X - 1, mid2 * X / (2 * (total > 0 ? total : 1)));
+    const int64_t mid2 = 2 * (int64_t)cum_cost[n] + k0 + k1;
+    int x = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxXcd - 1; ++i) x += (i < X - 1 && mid2 >= bnd2[i]) ? 1 : 0;
+    return x;
+  };
+  // tile range of chunk s of k over c tiles
+  auto chunk_range = [&](int c, int s, int k, int& k0, int& k1) {
+    if (k == 1) {
+      k0 = 0;
+      k1 = c;
+    } else {
+      k0 = (int)((int64_t)c * s / k);
+      k1 = (int)((int64_t)c * (s + 1) / k);
+    }
   };
   constexpr int kPer = kMaxXcd * kBuckets / kThreads;  // counters per thread in the scan
-  int32_t my_chunks = 0;
   int max_count = 0;
   for (int attempt = 0; attempt < 2; ++attempt) {
     for (int i = tid; i < kMaxXcd * kBuckets; i += kThreads) sh.bucket[i] = 0;
     __syncthreads();
-    my_chunks = 0;
     for (int n = n0; n < n1; ++n) {
       const int c = cost_of[n], k = pieces(c);
-      my_chunks += k;
       for (int s = 0; s < k; ++s) {
-        const int k0 = (int)((int64_t)c * s / k), k1 = (int)((int64_t)c * (s + 1) / k);
+        int k0, k1;
+        chunk_range(c, s, k, k0, k1);
         atomicAdd(&sh.bucket[bin_of(n, k0, k1) * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1);
       }
     }
@@ -289,6 +310,15 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     X = 1;  // bins too uneven for the grid: plain heaviest-first order
     __syncthreads();
   }
+  if (tid == 0) {
+    a.hdr->num_work = max_count * X;  // grid slots in use, empty items included
+    a.hdr->num_chunks = n_chunks;
+    a.hdr->xcds = X;
+    a.hdr->num_merge = mcarry;
+    a.hdr->chunk_tiles = (int32_t)chunk;
+    a.hdr->total_tiles = (int32_t)total;
+    a.hdr->num_items = n_items;
+  }
   if (n0 < n1) {
     int b, ig, itt;
     decode(n0, b, ig, itt);
@@ -296,7 +326,8 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       const int c = cost_of[n], k = pieces(c);
       const int pbase = (int)((uint32_t)pm[n] >> 16), midx = pm[n] & 0xFFFF;
       for (int s = 0; s < k; ++s) {
-        const int k0 = (int)((int64_t)c * s / k), k1 = (int)((int64_t)c * (s + 1) / k);
+        int k0, k1;
+        chunk_range(c, s, k, k0, k1);
         const int x = bin_of(n, k0, k1);
         const int rank = atomicAdd(&sh.bucket[x * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1) -
                          sh.bin_start[x];
@@ -343,16 +374,6 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       w.pad0 = 0;
       a.work[rank * X + x] = w;
     }
-  }
-  const int64_t n_chunks = block_sum(my_chunks, sh);
-  if (tid == 0) {
-    a.hdr->num_work = max_count * X;  // grid slots in use, empty items included
-    a.hdr->num_chunks = (int32_t)n_chunks;
-    a.hdr->xcds = X;
-    a.hdr->num_merge = mcarry;
-    a.hdr->chunk_tiles = (int32_t)chunk;
-    a.hdr->total_tiles = (int32_t)total;
-    a.hdr->num_items = n_items;
   }
 }
 
