@@ -70,8 +70,11 @@ struct DlCfg {
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
   static constexpr int K_CHUNKS = K_BYTES / 1024;  // 1 KB load instructions per tile
   static constexpr int V_CHUNKS = V_BYTES / 1024;
-  static constexpr int K_LOADS = K_CHUNKS / NW;  // per wave
-  static constexpr int V_LOADS = V_CHUNKS / NW;
+  // per wave; when the chunks do not divide evenly, waves past the last chunk
+  // load again a chunk of the last round (same bytes to the same place), so
+  // every wave issues the same number of loads
+  static constexpr int K_LOADS = (K_CHUNKS + NW - 1) / NW;
+  static constexpr int V_LOADS = (V_CHUNKS + NW - 1) / NW;
   // Eight waves (two per SIMD): the second half of the waves issues all the
   // loads and builds the tables, so the first half starts its products right
   // after each barrier and the two waves of a SIMD work out of phase.
@@ -87,9 +90,9 @@ struct DlCfg {
   static_assert(CK == 8 || CK == 16 || CK == 32 || CK == 72, "lq");
   static_assert(VK ? LV <= LQ : (CV == 8 || CV == 16 || CV == 32), "lv");
   static_assert(!WIDE || VK, "576-wide rows only with V inside K");
-  static_assert(K_CHUNKS % NW == 0 && V_CHUNKS % NW == 0, "the same whole 1 KB loads in every wave");
+  static_assert(K_CHUNKS >= NW && (V_CHUNKS == 0 || V_CHUNKS >= NW), "every wave has a chunk to repeat");
   static_assert(NS >= 2 && W_TABLE < 64 && W_OTHER < 64, "pipeline depth");
-  static_assert(RG == 2 || SPLIT == 1, "split variant: two row groups");
+  static_assert(RG >= 2 || SPLIT == 1, "split variant: at least two row groups");
   static_assert(QD % 16 == 0 && VD % 32 == 0, "split");
   static_assert(SPLIT == 1 || WIDE, "the split interleaves halves inside 8-chunk swizzle groups");
   static_assert(BN % 32 == 0 && BN <= 128, "key tile");
@@ -235,6 +238,15 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
 
   // ---- direct loads of tile kt into stage kt % NS: wave w covers bytes
   //      [(i * NW + w) * 1024, +1024) of the K and V regions
+  // 1 KB chunk of load i of wave w (a chunk of the last round again past the end)
+  auto kchunk = [&](int i, int w) __attribute__((always_inline)) {
+    const int li = i * C::NW + w;
+    return li < C::K_CHUNKS ? li : li - C::NW;
+  };
+  auto vchunk = [&](int i, int w) __attribute__((always_inline)) {
+    const int li = i * C::NW + w;
+    return li < C::V_CHUNKS ? li : li - C::NW;
+  };
   auto issue_tile = [&](int kt) __attribute__((always_inline)) {
     if (C::OFFLOAD && wv < C::LOADERS) return;  // waves that only compute
     constexpr int PER = C::NW / C::LOADERS;     // chunk sets per loading wave
@@ -247,13 +259,15 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
       const int vw = C::OFFLOAD ? wv - C::LOADERS + q * C::LOADERS : wv;  // wave whose chunks these are
 #pragma unroll
       for (int i = 0; i < C::K_LOADS; ++i) {
-        const int off = (i * C::NW + vw) * 1024 + lane * 16;
+        const int li = kchunk(i, vw);
+        const int off = li * 1024 + lane * 16;
         const int row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
         ksrc[q][i] = kptr[kt % NS][row] + swz_k<C>(row, p) * 8;
       }
 #pragma unroll
       for (int i = 0; i < C::V_LOADS; ++i) {
-        const int off = (i * C::NW + vw) * 1024 + lane * 16;
+        const int li = vchunk(i, vw);
+        const int off = li * 1024 + lane * 16;
         const int row = off / (LV * 2), p = (off % (LV * 2)) / 16;
         vsrc[q][i] = vptr[kt % NS][row] + swz_v<C>(row, p) * 8;
       }
@@ -262,10 +276,10 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
     for (int q = 0; q < PER; ++q) {
       const int vw = C::OFFLOAD ? wv - C::LOADERS + q * C::LOADERS : wv;
 #pragma unroll
-      for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ksrc[q][i], stage + (i * C::NW + vw) * 1024);
+      for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ksrc[q][i], stage + kchunk(i, vw) * 1024);
 #pragma unroll
       for (int i = 0; i < C::V_LOADS; ++i)
-        load_lds_16((gptr<void>)vsrc[q][i], stage + C::K_BYTES + (i * C::NW + vw) * 1024);
+        load_lds_16((gptr<void>)vsrc[q][i], stage + C::K_BYTES + vchunk(i, vw) * 1024);
     }
   };
 
@@ -592,7 +606,7 @@ int dl_occupancy_t() {
   X(64, 64, 64, false, 4, 4, 2)       \
   X(128, 128, 128, false, 8, 2, 1)    \
   X(256, 256, 32, false, 4, 4, 1)     \
-  X(576, 512, 32, true, 2, 3, 1)
+  X(576, 512, 32, true, 4, 3, 1)
 
 }  // namespace
 
