@@ -35,7 +35,7 @@
 namespace pkv {
 namespace {
 
-template <int LQ, int LV, int BN, bool VK, int RG_, int NS_>
+template <int LQ, int LV, int BN, bool VK, int RG_, int SPLIT_, int NS_>
 struct DlCfg {
   // Waves per row group.  When one wave cannot hold both its Q^T operand
   // (LQ / 4 registers) and its O^T accumulator (LV / 2 registers), two waves
@@ -44,7 +44,7 @@ struct DlCfg {
   // chunks 4h..4h+3 of every 8-chunk group of a row (Q/K dims) and the
   // 32-column output blocks 2m + h, so that inside a swizzle group its
   // operand addresses differ from one per-lane base by constants only.
-  static constexpr int SPLIT = LQ / 4 + LV / 2 > 320 ? 2 : 1;
+  static constexpr int SPLIT = SPLIT_;
   // 32-row groups per workgroup (the split variant uses 2, i.e. 4 waves and
   // one wave per SIMD, which leaves each wave the whole 512-entry register
   // file: its Q^T and O^T halves alone take ~200 entries)
@@ -58,6 +58,7 @@ struct DlCfg {
   static constexpr int VD = LV / SPLIT;  // O columns per wave
   static constexpr int CK = LQ / 8;      // 16-byte chunks per K row
   static constexpr int CV = LV / 8;
+  static constexpr int NDB_ALL = LV / 32;  // 32-column output blocks
   static constexpr bool WIDE = CK == 72;  // 576-element rows: swizzle inside 8-chunk groups
   // rows sharing one 256-byte window of the 64 LDS banks
   static constexpr int RPK = CK >= 16 ? 1 : 16 / CK;
@@ -94,7 +95,7 @@ struct DlCfg {
   static_assert(NS >= 2 && W_TABLE < 64 && W_OTHER < 64, "pipeline depth");
   static_assert(RG >= 2 || SPLIT == 1, "split variant: at least two row groups");
   static_assert(QD % 16 == 0 && VD % 32 == 0, "split");
-  static_assert(SPLIT == 1 || WIDE, "the split interleaves halves inside 8-chunk swizzle groups");
+  static_assert(SPLIT == 1 || (SPLIT == 2 && CK % 8 == 0 && NDB_ALL % 2 == 0), "split: halves interleave in 8-chunk groups");
   static_assert(BN % 32 == 0 && BN <= 128, "key tile");
 };
 
@@ -125,9 +126,9 @@ __device__ __forceinline__ int swz_v(int r, int c) {
   }
 }
 
-template <int LQ, int LV, int BN, bool VK, int RG, int NS, bool CAP, int MINB>
-__global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void attn_dl_kernel(AttnArgs a) {
-  using C = DlCfg<LQ, LV, BN, VK, RG, NS>;
+template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, bool CAP, int MINB>
+__global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void attn_dl_kernel(AttnArgs a) {
+  using C = DlCfg<LQ, LV, BN, VK, RG, SP, NS>;
   using T = uint16_t;
   constexpr int BM = C::BM;
   constexpr int NKB = BN / 32;
@@ -577,46 +578,46 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, NS>::NT), MINB) void att
   }
 }
 
-template <int LQ, int LV, int BN, bool VK, int RG, int NS, int MINB>
+template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, int MINB>
 hipError_t launch_dl_t(const AttnArgs& a, int64_t grid, hipStream_t s) {
-  using C = DlCfg<LQ, LV, BN, VK, RG, NS>;
+  using C = DlCfg<LQ, LV, BN, VK, RG, SP, NS>;
   if (grid <= 0) return hipSuccess;
   if (a.use_cap)
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, NS, true, MINB>), dim3((unsigned)grid), dim3(C::NT), 0,
-                       s, a);
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, true, MINB>), dim3((unsigned)grid), dim3(C::NT),
+                       0, s, a);
   else
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, NS, false, MINB>), dim3((unsigned)grid), dim3(C::NT), 0,
-                       s, a);
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, MINB>), dim3((unsigned)grid), dim3(C::NT),
+                       0, s, a);
   return hipGetLastError();
 }
 
-template <int LQ, int LV, int BN, bool VK, int RG, int NS, int MINB>
+template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, int MINB>
 int dl_occupancy_t() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, VK, RG, NS, false, MINB>),
-          DlCfg<LQ, LV, BN, VK, RG, NS>::NT, 0) != hipSuccess)
+          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, MINB>),
+          DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT, 0) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
 }
 
 // bf16 variants served here: (lq, lv, key tile, V inside K, 32-row groups,
-// LDS stages, workgroups per CU)
-#define PKV_DL_VARIANTS(X)            \
-  X(64, 64, 64, false, 4, 4, 2)       \
-  X(128, 128, 128, false, 8, 2, 1)    \
-  X(256, 256, 32, false, 4, 4, 1)     \
-  X(576, 512, 32, true, 4, 3, 1)
+// waves per row group, LDS stages, workgroups per CU)
+#define PKV_DL_VARIANTS(X)                \
+  X(64, 64, 64, false, 4, 1, 4, 2)        \
+  X(128, 128, 128, false, 8, 1, 2, 1)     \
+  X(256, 256, 32, false, 4, 2, 3, 1)      \
+  X(576, 512, 32, true, 4, 2, 3, 1)
 
 }  // namespace
 
 bool dl_tiling(int dtype, int lq, int lv, bool v_in_k, Tiling* t) {
   if (dtype != 0) return false;
-#define PKV_DT(Q, V, N, VK, RG, NS, M)                  \
+#define PKV_DT(Q, V, N, VK, RG, SP, NS, M)              \
   if (lq == Q && lv == V && (!VK || v_in_k)) {          \
-    t->bm = DlCfg<Q, V, N, VK, RG, NS>::BM;             \
+    t->bm = DlCfg<Q, V, N, VK, RG, SP, NS>::BM;         \
     t->bn = N;                                          \
-    t->threads = DlCfg<Q, V, N, VK, RG, NS>::NT;        \
+    t->threads = DlCfg<Q, V, N, VK, RG, SP, NS>::NT;    \
     return true;                                        \
   }
   PKV_DL_VARIANTS(PKV_DT)
@@ -625,16 +626,16 @@ bool dl_tiling(int dtype, int lq, int lv, bool v_in_k, Tiling* t) {
 }
 
 hipError_t launch_dl(int lq, int lv, bool v_in_k, const AttnArgs& a, int64_t grid, hipStream_t s) {
-#define PKV_DLL(Q, V, N, VK, RG, NS, M) \
-  if (lq == Q && lv == V && (!VK || v_in_k)) return launch_dl_t<Q, V, N, VK, RG, NS, M>(a, grid, s);
+#define PKV_DLL(Q, V, N, VK, RG, SP, NS, M) \
+  if (lq == Q && lv == V && (!VK || v_in_k)) return launch_dl_t<Q, V, N, VK, RG, SP, NS, M>(a, grid, s);
   PKV_DL_VARIANTS(PKV_DLL)
 #undef PKV_DLL
   return hipErrorInvalidValue;
 }
 
 int dl_blocks_per_cu(int lq, int lv, bool v_in_k) {
-#define PKV_DLO(Q, V, N, VK, RG, NS, M) \
-  if (lq == Q && lv == V && (!VK || v_in_k)) return dl_occupancy_t<Q, V, N, VK, RG, NS, M>();
+#define PKV_DLO(Q, V, N, VK, RG, SP, NS, M) \
+  if (lq == Q && lv == V && (!VK || v_in_k)) return dl_occupancy_t<Q, V, N, VK, RG, SP, NS, M>();
   PKV_DL_VARIANTS(PKV_DLO)
 #undef PKV_DLO
   return 1;
