@@ -24,7 +24,9 @@
 //    MFMA operand reads of K and the transposing reads of V stay free of bank
 //    conflicts.
 //  * Head dim 128 runs 256 rows (8 waves, two per SIMD) per workgroup, so one
-//    K/V tile in LDS serves twice the rows of a 128-row workgroup.
+//    K/V tile in LDS serves twice the rows of a 128-row workgroup; waves 4-7
+//    issue every load and build the row tables while waves 0-3 only compute
+//    (waves w and w+4 share a SIMD, so each SIMD holds one loading wave).
 //  * When V is the first Lv columns of K (the MLA layout on page
 //    "cpu_graph_runner.py", qkv_proj_with_rope: v = k.narrow(-1, 0, lv)), only
 //    the K tile is loaded and the V^T operand is read from it.
@@ -45,9 +47,9 @@ struct DlCfg {
   // 32-column output blocks 2m + h, so that inside a swizzle group its
   // operand addresses differ from one per-lane base by constants only.
   static constexpr int SPLIT = SPLIT_;
-  // 32-row groups per workgroup (the split variant uses 2, i.e. 4 waves and
-  // one wave per SIMD, which leaves each wave the whole 512-entry register
-  // file: its Q^T and O^T halves alone take ~200 entries)
+  // 32-row groups per workgroup.  The split variants use 4 (8 waves, two
+  // per SIMD): a wave's Q^T and O^T halves take ~200 registers at 576/512
+  // and ~100 at 256/256, so two waves fit one SIMD's register file.
   static constexpr int RG = RG_;
   // LDS stages: tile kt+NS-1 is requested while tile kt is computed
   static constexpr int NS = NS_;
@@ -109,20 +111,23 @@ __device__ __forceinline__ int wide_xor(int r) {
   const int s = (r >> 1) & 7;
   return ((s & 1) << 2) | (s >> 1);
 }
+// (r and c are never negative; unsigned arithmetic keeps the divisions shifts)
 template <class C>
 __device__ __forceinline__ int swz_k(int r, int c) {
+  const unsigned ur = r, uc = c;
   if constexpr (C::WIDE) {
-    return (c & ~7) | ((c & 7) ^ wide_xor(r));
+    return (int)((uc & ~7u) | ((uc & 7u) ^ (unsigned)wide_xor(r)));
   } else {
-    return c ^ ((r / C::RPK) % C::SWK);
+    return (int)(uc ^ ((ur / C::RPK) % C::SWK));
   }
 }
 template <class C>
 __device__ __forceinline__ int swz_v(int r, int c) {
+  const unsigned ur = r, uc = c;
   if constexpr (C::WIDE) {
     return swz_k<C>(r, c);
   } else {
-    return c ^ (4 * ((r / C::RPV) % C::SWV));
+    return (int)(uc ^ (4u * ((ur / C::RPV) % C::SWV)));
   }
 }
 
@@ -252,7 +257,6 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
     if (C::OFFLOAD && wv < C::LOADERS) return;  // waves that only compute
     constexpr int PER = C::NW / C::LOADERS;     // chunk sets per loading wave
     const uint32_t stage = lds_addr(lds + (kt % NS) * C::STAGE_BYTES);
-    // all row pointers first: each load is a compiler memory barrier
     gptr<T> ksrc[PER][C::K_LOADS];
     gptr<T> vsrc[PER][C::V_LOADS > 0 ? C::V_LOADS : 1];
 #pragma unroll
@@ -260,17 +264,15 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
       const int vw = C::OFFLOAD ? wv - C::LOADERS + q * C::LOADERS : wv;  // wave whose chunks these are
 #pragma unroll
       for (int i = 0; i < C::K_LOADS; ++i) {
-        const int li = kchunk(i, vw);
-        const int off = li * 1024 + lane * 16;
-        const int row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
-        ksrc[q][i] = kptr[kt % NS][row] + swz_k<C>(row, p) * 8;
+        const unsigned off = (unsigned)kchunk(i, vw) * 1024u + (unsigned)lane * 16u;
+        const unsigned row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
+        ksrc[q][i] = kptr[kt % NS][row] + (unsigned)swz_k<C>(row, p) * 8u;
       }
 #pragma unroll
       for (int i = 0; i < C::V_LOADS; ++i) {
-        const int li = vchunk(i, vw);
-        const int off = li * 1024 + lane * 16;
-        const int row = off / (LV * 2), p = (off % (LV * 2)) / 16;
-        vsrc[q][i] = vptr[kt % NS][row] + swz_v<C>(row, p) * 8;
+        const unsigned off = (unsigned)vchunk(i, vw) * 1024u + (unsigned)lane * 16u;
+        const unsigned row = off / (LV * 2), p = (off % (LV * 2)) / 16;
+        vsrc[q][i] = vptr[kt % NS][row] + (unsigned)swz_v<C>(row, p) * 8u;
       }
     }
 #pragma unroll
