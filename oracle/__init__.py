@@ -57,6 +57,9 @@ def _load():
         lib.oracle_extend_attention.argtypes = (
             [i32] + [P, i64, i64] * 5 + [i64, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32])
         lib.oracle_extend_attention.restype = ctypes.c_int
+        lib.oracle_extend_attention_unified.argtypes = (
+            [i32] + [P, i64, i64] * 3 + [i64, P, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32])
+        lib.oracle_extend_attention_unified.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -134,6 +137,47 @@ def extend_attention(q, k_ext, v_ext, k_pool, v_pool, qo_indptr, kv_indptr, kv_i
     rc = lib.oracle_extend_attention(*args)
     if rc != 0:
         raise ValueError(f"oracle attention failed: {rc}")
+    return out[:n]
+
+
+def extend_attention_unified(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, prefix_lens,
+                             sm_scale=0.0, logit_cap=0.0, dtype="bf16", rows=None, num_threads=0):
+    """Exact (double) unified one-stage extend attention: every key through
+    kv_indices (the unified index array), prefix_lens[b] of them prefix keys.
+    Same array conventions and return value as extend_attention."""
+    lib = _load()
+    dt = 0 if dtype == "bf16" else 1
+    want = np.uint16 if dt == 0 else np.float32
+    for x in (q, k_pool, v_pool):
+        assert x.dtype == want, (x.dtype, want)
+    qo = np.ascontiguousarray(qo_indptr, np.int32)
+    kvp = np.ascontiguousarray(kv_indptr, np.int32)
+    kvi = np.ascontiguousarray(kv_indices, np.int64)
+    pl = np.ascontiguousarray(prefix_lens, np.int32)
+    if kvi.size == 0:
+        kvi = np.zeros(1, np.int64)
+    if pl.size == 0:
+        pl = np.zeros(1, np.int32)
+    bs = len(qo) - 1
+    hq, lq = q.shape[1], q.shape[2]
+    hkv, lv = k_pool.shape[1], v_pool.shape[2]
+    total = int(qo[-1]) if bs > 0 else 0
+    if rows is None:
+        rows_arr, n = None, total
+    else:
+        rows_arr = np.ascontiguousarray(rows, np.int64)
+        n = len(rows_arr)
+    out = np.zeros((max(n, 1), hq, lv), np.float64)
+    args = [dt]
+    for x in (q, k_pool, v_pool):
+        s0, s1 = _strides(x)
+        args += [_ptr(x) if x.size else 0, s0, s1]
+    args += [k_pool.shape[0], _ptr(qo), _ptr(kvp), _ptr(kvi), _ptr(pl), bs, hq, hkv, lq, lv,
+             float(sm_scale), float(logit_cap),
+             _ptr(rows_arr) if rows_arr is not None else None, n, _ptr(out), int(num_threads)]
+    rc = lib.oracle_extend_attention_unified(*args)
+    if rc != 0:
+        raise ValueError(f"oracle unified attention failed: {rc}")
     return out[:n]
 
 

@@ -10,7 +10,8 @@
  *    0.5.4.post1 diff), functions build_unified_kv_indices and
  *    _copy_unified_indices_kernel;
  *  - attention: the same page, kernel _fwd_kernel_unified (causal mask, scale,
- *    soft-cap, softmax) and the reference helper redundant_attention
+ *    soft-cap, softmax; and, for the unified entry, keys read through one
+ *    index array) and the reference helper redundant_attention
  *    (attention over the concatenated prefix + extend sequence, keeping the
  *    extend rows); page "flashinfer_backend.py", forward_extend and
  *    call_begin_forward (the prefix is read through kv_indptr/kv_indices,
@@ -200,6 +201,112 @@ int oracle_extend_attention(int32_t dtype,
       }
     }
     free(s);
+    free(acc);
+  }
+  return status;
+}
+
+/*
+ * Unified one-stage extend attention (extend_attention.py,
+ * extend_attention_fwd_unified and _fwd_kernel_unified): every key of a
+ * sequence, prefix and new tokens alike, is read from the pool through one
+ * index array.
+ *
+ * Sequence b owns extend-token row t, i = t - qo_indptr[b].  Its keys are
+ * j = 0 .. L-1 with L = kv_indptr[b+1] - kv_indptr[b]; key j is pool slot
+ * kv_indices[kv_indptr[b] + j].  With P = prefix_lens[b], key j is visible to
+ * query i iff j < P (a prefix key) or j - P <= i (a new token at or before the
+ * query).  Scale, cap and softmax as in oracle_extend_attention.  A row with no
+ * visible key gets NaN (the softmax denominator is zero).
+ */
+int oracle_extend_attention_unified(int32_t dtype,
+                                    const void* q, int64_t q_st, int64_t q_sh,
+                                    const void* k_pool, int64_t kp_ss, int64_t kp_sh,
+                                    const void* v_pool, int64_t vp_ss, int64_t vp_sh,
+                                    int64_t pool_slots,
+                                    const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                    const int64_t* kv_indices, const int32_t* prefix_lens,
+                                    int32_t bs, int32_t hq, int32_t hkv, int32_t lq, int32_t lv,
+                                    double sm_scale, double logit_cap,
+                                    const int64_t* rows, int64_t n_rows,
+                                    double* out, int32_t num_threads) {
+  if (bs < 0 || hq <= 0 || hkv <= 0 || lq <= 0 || lv <= 0) return ORACLE_EINVAL;
+  if (hq % hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_EINVAL;
+  const int32_t group = hq / hkv;
+  const int64_t total_q = bs > 0 ? qo_indptr[bs] : 0;
+  const double scale = sm_scale != 0.0 ? sm_scale : 1.0 / sqrt((double)lq);
+  if (rows == NULL) n_rows = total_q;
+
+  int64_t max_keys = 1;
+  for (int32_t b = 0; b < bs; ++b) {
+    int64_t keys = (int64_t)(kv_indptr[b + 1] - kv_indptr[b]);
+    if (keys > max_keys) max_keys = keys;
+  }
+  for (int64_t n = 0; n < kv_indptr[bs] - kv_indptr[0]; ++n) {
+    int64_t slot = kv_indices[kv_indptr[0] + n];
+    if (slot < 0 || slot >= pool_slots) return ORACLE_ERANGE;
+  }
+
+  int status = ORACLE_OK;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#endif
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)max_keys);
+    char* seen = (char*)malloc((size_t)max_keys);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)lv);
+    if (!s || !seen || !acc) {
+#pragma omp atomic write
+      status = ORACLE_ENOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t w = 0; w < n_rows * hq; ++w) {
+        int64_t r = w / hq;
+        int32_t h = (int32_t)(w % hq);
+        int64_t t = rows ? rows[r] : r;
+        int32_t b = owner_seq(qo_indptr, bs, t);
+        double* o = out + (r * hq + h) * (int64_t)lv;
+        if (b < 0) {
+#pragma omp atomic write
+          status = ORACLE_EINVAL;
+          continue;
+        }
+        int64_t i = t - qo_indptr[b];
+        int64_t L = kv_indptr[b + 1] - kv_indptr[b];
+        int64_t P = prefix_lens[b];
+        int32_t g = h / group;
+
+        /* logits of the visible keys */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < L; ++j) {
+          seen[j] = (j < P) || (j - P <= i);
+          if (!seen[j]) continue;
+          int64_t koff = kv_indices[kv_indptr[b] + j] * kp_ss + (int64_t)g * kp_sh;
+          double dot = 0.0;
+          for (int32_t d = 0; d < lq; ++d)
+            dot += load_elem(q, dtype, t * q_st + (int64_t)h * q_sh + d) * load_elem(k_pool, dtype, koff + d);
+          double x = dot * scale;
+          if (logit_cap > 0.0) x = logit_cap * tanh(x / logit_cap);
+          s[j] = x;
+          if (x > m) m = x;
+        }
+
+        /* softmax-weighted sum of the visible values */
+        double den = 0.0;
+        for (int32_t d = 0; d < lv; ++d) acc[d] = 0.0;
+        for (int64_t j = 0; j < L; ++j) {
+          if (!seen[j]) continue;
+          int64_t voff = kv_indices[kv_indptr[b] + j] * vp_ss + (int64_t)g * vp_sh;
+          double wgt = exp(s[j] - m);
+          den += wgt;
+          for (int32_t d = 0; d < lv; ++d) acc[d] += wgt * load_elem(v_pool, dtype, voff + d);
+        }
+        for (int32_t d = 0; d < lv; ++d) o[d] = den > 0.0 ? acc[d] / den : NAN;
+      }
+    }
+    free(s);
+    free(seen);
     free(acc);
   }
   return status;

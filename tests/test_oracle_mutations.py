@@ -25,6 +25,10 @@ MUTATIONS = {
                          "koff = (qo_indptr[b] + (j - P) + (j > P)) * ke_st"),
     "index_copy_shift": ("unified_kv_indices[u + p_len + o]", "unified_kv_indices[u + p_len + o - (o > 0)]"),
     "first_weight_bias": ("double wgt = exp(s[j] - m);", "double wgt = exp(s[j] - m) * (j == 0 ? 1.0001 : 1.0);"),
+    "unified_drops_diagonal": ("seen[j] = (j < P) || (j - P <= i);", "seen[j] = (j < P) || (j - P < i);"),
+    "unified_causal_prefix": ("seen[j] = (j < P) || (j - P <= i);", "seen[j] = (j - P <= i);"),
+    "unified_batch_index_base": ("int64_t koff = kv_indices[kv_indptr[b] + j] * kp_ss",
+                                 "int64_t koff = kv_indices[kv_indptr[0] + j] * kp_ss"),
 }
 
 

@@ -269,3 +269,60 @@ def test_out_of_range_slot_is_an_error():
     w.kv_indices[1] = 8
     with pytest.raises(ValueError):
         oracle.extend_attention_workload(w)
+
+
+# ----------------------------------------------------------------------------- unified one-stage entry
+# (page extend_attention.py, extend_attention_fwd_unified / _fwd_kernel_unified: every key through one
+# index array, prefix_lens[b] of them prefix keys)
+
+def _unified_arrays(w):
+    """Unified indptr / indices / prefix_lens from the oracle's own index build."""
+    indptr, indices, plens = oracle.build_unified_kv_indices(
+        w.kv_indptr, w.kv_indices, w.extend_start_loc, w.extend_lens, w.extend_kv_indices, w.bs)
+    return indptr, indices[:int(indptr[-1])], plens
+
+
+def _unified(w, indptr, indices, plens, k_pool=None, v_pool=None):
+    return oracle.extend_attention_unified(
+        w.q, w.k_pool if k_pool is None else k_pool, w.v_pool if v_pool is None else v_pool,
+        w.qo_indptr, indptr, indices, plens, w.sm_scale, w.logit_cap, w.cfg.dtype)
+
+
+@pytest.mark.parametrize("case", SDPA_CASES, ids=lambda c: f"{c['dtype']}-{c['lq']}x{c['lv']}-h{c['hq']}/{c['hkv']}")
+def test_unified_matches_library_attention(case):
+    # the pool holds every new token's K/V at its extend slot (the caller's cache
+    # store), so the one-index-array path must give the concatenated attention
+    w = wl.custom(**case)
+    got = _unified(w, *_unified_arrays(w))
+    np.testing.assert_allclose(got, sdpa_reference(w), rtol=0, atol=1e-12)
+
+
+def test_unified_all_prefix_is_full_attention():
+    # prefix_lens equal to the whole span: no key is causal, every query sees
+    # every key of its sequence (library attention without a mask)
+    w = wl.custom(dtype="bf16", prefix_lens=[10, 3], extend_lens=[4, 6], hq=4, hkv=2, lq=64, lv=64)
+    indptr, indices, _ = _unified_arrays(w)
+    span = np.diff(indptr).astype(np.int32)
+    got = _unified(w, indptr, indices, span)
+    outs = []
+    for b in range(w.bs):
+        q0, q1 = w.qo_indptr[b], w.qo_indptr[b + 1]
+        slots = indices[indptr[b]:indptr[b + 1]]
+        q = _f64(w.q[q0:q1], "bf16").transpose(0, 1)
+        k = _f64(w.k_pool[slots], "bf16").transpose(0, 1).repeat_interleave(2, 0)
+        v = _f64(w.v_pool[slots], "bf16").transpose(0, 1).repeat_interleave(2, 0)
+        outs.append(torch.nn.functional.scaled_dot_product_attention(q, k, v).transpose(0, 1))
+    np.testing.assert_allclose(got, torch.cat(outs).numpy(), atol=1e-12)
+
+
+def test_unified_pool_slot_permutation_is_exact():
+    w = wl.custom(dtype="bf16", prefix_lens=[12, 0, 25], extend_lens=[3, 9, 2], hq=4, hkv=2,
+                  lq=64, lv=64, pool_slots=80)
+    indptr, indices, plens = _unified_arrays(w)
+    base = _unified(w, indptr, indices, plens)
+    perm = np.random.default_rng(5).permutation(80)
+    k2 = np.empty_like(w.k_pool)
+    v2 = np.empty_like(w.v_pool)
+    k2[perm] = w.k_pool
+    v2[perm] = w.v_pool
+    assert np.array_equal(_unified(w, indptr, perm[indices], plens, k2, v2), base)
