@@ -78,13 +78,14 @@ struct DlCfg {
   // every wave issues the same number of loads
   static constexpr int K_LOADS = (K_CHUNKS + NW - 1) / NW;
   static constexpr int V_LOADS = (V_CHUNKS + NW - 1) / NW;
-  // Eight waves (two per SIMD): the second half of the waves issues all the
-  // loads and builds the tables, so the first half starts its products right
-  // after each barrier and the two waves of a SIMD work out of phase.
+  // Eight waves (two per SIMD), staggered loads: waves 0..3 issue the K rows
+  // of the next tile right after each barrier and waves 4..7 its V rows after
+  // their S = K Q^T products, so while one wave of a SIMD waits for the
+  // memory pipeline to take its loads, the other has products to run.
   static constexpr bool OFFLOAD = SPLIT == 1 && NW == 8;
-  static constexpr int LOADERS = OFFLOAD ? NW / 2 : NW;   // waves that issue loads
+  static constexpr int LOADERS = OFFLOAD ? NW / 2 : NW;   // waves per load group
   static constexpr int TW = OFFLOAD ? NW / 2 : 0;         // the wave that builds tables
-  static constexpr int L = (K_LOADS + V_LOADS) * (NW / LOADERS);  // tile loads per loading wave per tile
+  static constexpr int L = OFFLOAD ? 2 * V_LOADS : K_LOADS + V_LOADS;  // tile loads per wave per tile
   static constexpr int I = BN * 8 / 256;  // row-slot loads (64 lanes x 4 bytes) per tile, table wave
   // waits at the top of an iteration (see the loop): outstanding loads allowed
   static constexpr int W_OTHER = (NS - 2) * L;
@@ -95,6 +96,7 @@ struct DlCfg {
   static_assert(!WIDE || VK, "576-wide rows only with V inside K");
   static_assert(K_CHUNKS >= NW && (V_CHUNKS == 0 || V_CHUNKS >= NW), "every wave has a chunk to repeat");
   static_assert(NS >= 2 && W_TABLE < 64 && W_OTHER < 64, "pipeline depth");
+  static_assert(!OFFLOAD || (NS == 2 && K_LOADS == V_LOADS), "staggered loads: every wait is vmcnt(0)");
   static_assert(RG >= 2 || SPLIT == 1, "split variant: at least two row groups");
   static_assert(QD % 16 == 0 && VD % 32 == 0, "split");
   static_assert(SPLIT == 1 || (SPLIT == 2 && CK % 8 == 0 && NDB_ALL % 2 == 0), "split: halves interleave in 8-chunk groups");
@@ -253,36 +255,53 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
     const int li = i * C::NW + w;
     return li < C::V_CHUNKS ? li : li - C::NW;
   };
-  auto issue_tile = [&](int kt) __attribute__((always_inline)) {
-    if (C::OFFLOAD && wv < C::LOADERS) return;  // waves that only compute
-    constexpr int PER = C::NW / C::LOADERS;     // chunk sets per loading wave
+  // K rows (do_k) and V rows (do_v) of tile kt; with staggered loads a wave
+  // of either group covers the chunks of two waves (itself and 4 apart)
+  auto issue_loads = [&](int kt, bool do_k, bool do_v) __attribute__((always_inline)) {
+    constexpr int PER = C::NW / C::LOADERS;  // chunk sets per wave
     const uint32_t stage = lds_addr(lds + (kt % NS) * C::STAGE_BYTES);
     gptr<T> ksrc[PER][C::K_LOADS];
     gptr<T> vsrc[PER][C::V_LOADS > 0 ? C::V_LOADS : 1];
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-      const int vw = C::OFFLOAD ? wv - C::LOADERS + q * C::LOADERS : wv;  // wave whose chunks these are
+      const int vw = C::OFFLOAD ? wv % C::LOADERS + q * C::LOADERS : wv;  // wave whose chunks these are
+      if (do_k) {
 #pragma unroll
-      for (int i = 0; i < C::K_LOADS; ++i) {
-        const unsigned off = (unsigned)kchunk(i, vw) * 1024u + (unsigned)lane * 16u;
-        const unsigned row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
-        ksrc[q][i] = kptr[kt % NS][row] + (unsigned)swz_k<C>(row, p) * 8u;
+        for (int i = 0; i < C::K_LOADS; ++i) {
+          const unsigned off = (unsigned)kchunk(i, vw) * 1024u + (unsigned)lane * 16u;
+          const unsigned row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
+          ksrc[q][i] = kptr[kt % NS][row] + (unsigned)swz_k<C>(row, p) * 8u;
+        }
       }
+      if (do_v) {
 #pragma unroll
-      for (int i = 0; i < C::V_LOADS; ++i) {
-        const unsigned off = (unsigned)vchunk(i, vw) * 1024u + (unsigned)lane * 16u;
-        const unsigned row = off / (LV * 2), p = (off % (LV * 2)) / 16;
-        vsrc[q][i] = vptr[kt % NS][row] + (unsigned)swz_v<C>(row, p) * 8u;
+        for (int i = 0; i < C::V_LOADS; ++i) {
+          const unsigned off = (unsigned)vchunk(i, vw) * 1024u + (unsigned)lane * 16u;
+          const unsigned row = off / (LV * 2), p = (off % (LV * 2)) / 16;
+          vsrc[q][i] = vptr[kt % NS][row] + (unsigned)swz_v<C>(row, p) * 8u;
+        }
       }
     }
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-      const int vw = C::OFFLOAD ? wv - C::LOADERS + q * C::LOADERS : wv;
+      const int vw = C::OFFLOAD ? wv % C::LOADERS + q * C::LOADERS : wv;
+      if (do_k) {
 #pragma unroll
-      for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ksrc[q][i], stage + kchunk(i, vw) * 1024);
+        for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ksrc[q][i], stage + kchunk(i, vw) * 1024);
+      }
+      if (do_v) {
 #pragma unroll
-      for (int i = 0; i < C::V_LOADS; ++i)
-        load_lds_16((gptr<void>)vsrc[q][i], stage + C::K_BYTES + vchunk(i, vw) * 1024);
+        for (int i = 0; i < C::V_LOADS; ++i)
+          load_lds_16((gptr<void>)vsrc[q][i], stage + C::K_BYTES + vchunk(i, vw) * 1024);
+      }
+    }
+  };
+  // every load of tile kt: K by waves 0..3 and V by waves 4..7 when staggered
+  auto issue_tile = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (C::OFFLOAD) {
+      issue_loads(kt, wv < C::LOADERS, wv >= C::LOADERS);
+    } else {
+      issue_loads(kt, true, true);
     }
   };
 
@@ -522,7 +541,11 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   // kt+NS-1 into stage (kt-1) % NS, which tile kt-1 no longer needs
   auto issue_group = [&](int kt) __attribute__((always_inline)) {
     if (wv == C::TW) issue_slots(kt + NS + 1);
-    issue_tile(kt + NS - 1);
+    if constexpr (C::OFFLOAD) {
+      if (wv < C::LOADERS) issue_loads(kt + NS - 1, true, false);
+    } else {
+      issue_tile(kt + NS - 1);
+    }
   };
 
   for (int kt = kt0; kt < kt1; ++kt) {
@@ -533,6 +556,10 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
     if (act) qk(kt, s);
+    // staggered loads: the V rows of the tile the group requested
+    if constexpr (C::OFFLOAD) {
+      if (wv >= C::LOADERS) issue_loads(kt + NS - 1, false, true);
+    }
     if constexpr (C::SPLIT > 1) exchange(act, s);
     if (act) {
       bf16x8 pb[NKB][2];
