@@ -175,6 +175,45 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
                          void* stream);
 
 /*
+ * Unified one-stage extend attention.
+ * Page "extend_attention.py": extend_attention_fwd_unified and
+ * _fwd_kernel_unified.  Every key of a sequence, prefix and new tokens alike,
+ * is read from the pool through one index array -- the arrays
+ * build_unified_kv_indices produces -- so the new tokens' K/V must already be
+ * stored in the pool at their slots.
+ *
+ * For sequence b (L_b = unified_kv_indptr[b+1] - unified_kv_indptr[b] keys,
+ * P_b = prefix_lens[b], E_b = qo_indptr[b+1] - qo_indptr[b]), new token i in
+ * [0, E_b), query head h and KV head g = h / (num_q_heads / num_kv_heads):
+ *   key j in [0, L_b) : k_pool[unified_kv_indices[unified_kv_indptr[b] + j], g], v_pool likewise
+ *   visible keys      : j < P_b (prefix) or j - P_b <= i (new tokens up to the query)
+ *   scale, soft-cap and softmax as in extend_attention_fwd.
+ * With L_b = P_b + E_b and the new tokens' rows stored at their slots this is
+ * the two-part result of extend_attention_fwd.
+ *
+ * Arguments (device pointers unless noted):
+ *  q_extend, o, k_pool, v_pool: as in pkv_attn_desc_t (the ke / ve strides of
+ *              desc are not used).
+ *  qo_indptr   int32[bs+1], as in extend_attention_fwd.
+ *  unified_kv_indptr  int32[bs+1], non-decreasing; unified_kv_indptr[bs] -
+ *              unified_kv_indptr[0] == desc->num_prefix_indices (the length
+ *              of the index array).
+ *  unified_kv_indices int64[num_prefix_indices], each in [0, pool_slots).
+ *  prefix_lens int32[bs], 0 <= prefix_lens[b] <= L_b.  Keys at or past
+ *              P_b + E_b are never visible and never read; a row that sees no
+ *              key (L_b == 0) gets an undefined value.
+ *  sm_scale, logit_cap, desc, workspace, workspace_bytes, stream: as in
+ *              extend_attention_fwd (the same workspace size query applies).
+ * Returns as extend_attention_fwd; prefix_lens == NULL with work to do is
+ * PKV_ERR_INVALID.
+ */
+int extend_attention_fwd_unified(const void* q_extend, void* o, const void* k_pool, const void* v_pool,
+                                 const int32_t* qo_indptr, const int32_t* unified_kv_indptr,
+                                 const int64_t* unified_kv_indices, const int32_t* prefix_lens,
+                                 float sm_scale, float logit_cap, const pkv_attn_desc_t* desc,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Process-wide kernel preference for later extend_attention_fwd calls, for
  * tests and benchmarks: "auto" (the default: the fastest measured kernel that
  * serves the shape), "r64" (64 query rows per wave; bf16, lq == lv == 128), "dl"
@@ -191,7 +230,7 @@ int extend_attention_prefer_kernel(const char* name);
 /*
  * Name of the attention kernel symbol that serves a call with `desc` and these
  * K/V base pointers ("attn_r64_kernel", "attn_dl_kernel" or "attn_kernel", as
- * profilers list it),
+ * profilers list it; pass NULL new-token pointers for a unified call),
  * or NULL when desc is invalid.  The pointers are only compared (V inside K
  * selects a variant), never dereferenced.  For matching profiler output;
  * results do not depend on it.

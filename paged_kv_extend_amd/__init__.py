@@ -16,7 +16,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_workspace_size",
+__all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_fwd_unified",
+           "extend_attention_workspace_size",
            "extend_attention_kernel_name", "extend_attention_prefer_kernel",
            "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "LIB_PATH", "PkvError"]
 
@@ -60,6 +61,9 @@ def library() -> ctypes.CDLL:
     lib.extend_attention_fwd.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
                                          ctypes.POINTER(AttnDesc), P, ctypes.c_size_t, P]
     lib.extend_attention_fwd.restype = ctypes.c_int
+    lib.extend_attention_fwd_unified.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
+                                                 ctypes.POINTER(AttnDesc), P, ctypes.c_size_t, P]
+    lib.extend_attention_fwd_unified.restype = ctypes.c_int
     lib.pkv_profile_enable.argtypes = [ctypes.c_int]
     lib.pkv_profile_enable.restype = ctypes.c_int
     lib.pkv_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -148,6 +152,7 @@ def build_unified_kv_indices(prefix_kv_indptr: torch.Tensor, prefix_kv_indices: 
 
 def make_desc(q_extend, k_extend, v_extend, o, k_pool, v_pool, bs: int,
               num_prefix_indices: int) -> AttnDesc:
+    """Descriptor of a call; k_extend / v_extend are None for a unified call."""
     if q_extend.dtype == torch.bfloat16:
         dt = PKV_BF16
     elif q_extend.dtype == torch.float32:
@@ -156,10 +161,14 @@ def make_desc(q_extend, k_extend, v_extend, o, k_pool, v_pool, bs: int,
         raise ValueError(f"unsupported dtype {q_extend.dtype}")
     for t, n in ((q_extend, "q_extend"), (k_extend, "k_extend"), (v_extend, "v_extend"), (o, "o"),
                  (k_pool, "k_pool"), (v_pool, "v_pool")):
+        if t is None and n in ("k_extend", "v_extend"):
+            continue
         _want(t, n, q_extend.dtype)
         if t.dim() != 3 or (t.numel() > 0 and t.stride(2) != 1):
             raise ValueError(f"{n} must be 3-D with a contiguous last dimension")
     def st(t):  # strides of an empty tensor carry no meaning; report contiguous ones
+        if t is None:
+            return 0, 0
         return (t.stride(0), t.stride(1)) if t.numel() > 0 else (t.shape[1] * t.shape[2], t.shape[2])
 
     d = AttnDesc()
@@ -238,6 +247,33 @@ def extend_attention_fwd(q_extend: torch.Tensor, k_extend: torch.Tensor, v_exten
         _ptr(q_extend), _ptr(k_extend), _ptr(v_extend), _ptr(o), _ptr(k_pool), _ptr(v_pool),
         _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
         float(sm_scale or 0.0), float(logit_cap), ctypes.byref(desc),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    _check(rc)
+    return o
+
+
+def extend_attention_fwd_unified(q_extend: torch.Tensor, o: torch.Tensor, k_pool: torch.Tensor,
+                                 v_pool: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,
+                                 kv_indices: torch.Tensor, prefix_lens: torch.Tensor,
+                                 sm_scale: Optional[float] = None, logit_cap: float = 0.0,
+                                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Unified one-stage extend attention into ``o``: every key through the
+    unified kv_indptr / kv_indices (as build_unified_kv_indices returns them),
+    prefix_lens[b] of sequence b's keys prefix keys (see include/pkv.h)."""
+    _want(qo_indptr, "qo_indptr", torch.int32)
+    _want(kv_indptr, "kv_indptr", torch.int32)
+    _want(kv_indices, "kv_indices", torch.int64)
+    _want(prefix_lens, "prefix_lens", torch.int32)
+    bs = qo_indptr.numel() - 1
+    desc = make_desc(q_extend, None, None, o, k_pool, v_pool, bs, kv_indices.numel())
+    dev = q_extend.device
+    stream = _stream(dev)
+    nbytes = extend_attention_workspace_size(desc)
+    if workspace is None:
+        workspace = _workspace(dev, stream, nbytes)
+    rc = library().extend_attention_fwd_unified(
+        _ptr(q_extend), _ptr(o), _ptr(k_pool), _ptr(v_pool), _ptr(qo_indptr), _ptr(kv_indptr),
+        _ptr(kv_indices), _ptr(prefix_lens), float(sm_scale or 0.0), float(logit_cap), ctypes.byref(desc),
         _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
     _check(rc)
     return o

@@ -43,10 +43,12 @@ constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dealt
 
 // V is the first lv columns of K (same base pointers and strides), as in the
 // MLA layout: the direct-load kernel then reads V out of the K tile.
+// (without new-token tensors, as in a unified call, only the pool decides)
 bool v_inside_k(const pkv_attn_desc_t& d, const void* k_extend, const void* v_extend, const void* k_pool,
                 const void* v_pool) {
-  return d.lv <= d.lq && k_extend == v_extend && k_pool == v_pool && d.ke_stride_tok == d.ve_stride_tok &&
-         d.ke_stride_head == d.ve_stride_head && d.kp_stride_slot == d.vp_stride_slot &&
+  const bool ext = (!k_extend && !v_extend) ||
+                   (k_extend == v_extend && d.ke_stride_tok == d.ve_stride_tok && d.ke_stride_head == d.ve_stride_head);
+  return d.lv <= d.lq && ext && k_pool == v_pool && d.kp_stride_slot == d.vp_stride_slot &&
          d.kp_stride_head == d.vp_stride_head;
 }
 
@@ -317,23 +319,30 @@ size_t extend_attention_workspace_size(const pkv_attn_desc_t* desc) {
   return total;
 }
 
-int extend_attention_fwd(const void* q_extend, const void* k_extend, const void* v_extend, void* o,
-                         const void* k_pool, const void* v_pool, const int32_t* qo_indptr,
-                         const int32_t* kv_indptr, const int64_t* kv_indices, float sm_scale,
-                         float logit_cap, const pkv_attn_desc_t* desc, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both entry points: two-part when prefix_lens is NULL (new tokens' K/V from
+// k_extend / v_extend), unified otherwise (every key through kv_indices).
+int attention_call(const void* q_extend, const void* k_extend, const void* v_extend, void* o, const void* k_pool,
+                   const void* v_pool, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                   const int64_t* kv_indices, const int32_t* prefix_lens, float sm_scale, float logit_cap,
+                   const pkv_attn_desc_t* desc, void* workspace, size_t workspace_bytes, void* stream) {
   pkv::Tiling t;
   int rc = check_desc(desc, &t);
   if (rc != PKV_OK) return rc;
   const pkv_attn_desc_t& d = *desc;
+  const bool unified = prefix_lens != nullptr;
   if (!std::isfinite(sm_scale) || std::isnan(logit_cap))
     return fail(PKV_ERR_INVALID, "sm_scale must be finite and logit_cap not NaN");
   if (d.bs == 0 || d.total_q_tokens == 0) return ok();  // no query rows: nothing to write
   if (!qo_indptr || !kv_indptr) return fail(PKV_ERR_INVALID, "qo_indptr / kv_indptr is NULL");
-  if (!q_extend || !k_extend || !v_extend || !o)
-    return fail(PKV_ERR_INVALID, "q_extend / k_extend / v_extend / o is NULL");
+  if (!q_extend || !o) return fail(PKV_ERR_INVALID, "q_extend / o is NULL");
+  if (!unified && (!k_extend || !v_extend)) return fail(PKV_ERR_INVALID, "k_extend / v_extend is NULL");
+  if (unified) k_extend = v_extend = nullptr;  // not read
   if (d.num_prefix_indices > 0 && (!kv_indices || !k_pool || !v_pool))
-    return fail(PKV_ERR_INVALID, "kv_indices / k_pool / v_pool is NULL with a non-empty prefix");
+    return fail(PKV_ERR_INVALID, "kv_indices / k_pool / v_pool is NULL with a non-empty index array");
   const void* ptrs[] = {q_extend, k_extend, v_extend, o, k_pool, v_pool};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(PKV_ERR_UNSUPPORTED, "tensor base pointers must be 16-byte aligned");
@@ -355,6 +364,7 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   pkv::PlanArgs pa;
   pa.qo_indptr = qo_indptr;
   pa.kv_indptr = kv_indptr;
+  pa.prefix_lens = prefix_lens;
   pa.bs = d.bs;
   pa.num_kv_heads = d.num_kv_heads;
   pa.group = group;
@@ -387,6 +397,7 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   a.qo_indptr = qo_indptr;
   a.kv_indptr = kv_indptr;
   a.kv_indices = kv_indices;
+  a.prefix_lens = prefix_lens;
   a.q_st = d.q_stride_tok;
   a.q_sh = d.q_stride_head;
   a.o_st = d.o_stride_tok;
@@ -422,6 +433,32 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   if (ev.second) (void)hipEventRecord(ev.second, s);
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int extend_attention_fwd(const void* q_extend, const void* k_extend, const void* v_extend, void* o,
+                         const void* k_pool, const void* v_pool, const int32_t* qo_indptr,
+                         const int32_t* kv_indptr, const int64_t* kv_indices, float sm_scale,
+                         float logit_cap, const pkv_attn_desc_t* desc, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return attention_call(q_extend, k_extend, v_extend, o, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices,
+                        nullptr, sm_scale, logit_cap, desc, workspace, workspace_bytes, stream);
+}
+
+int extend_attention_fwd_unified(const void* q_extend, void* o, const void* k_pool, const void* v_pool,
+                                 const int32_t* qo_indptr, const int32_t* unified_kv_indptr,
+                                 const int64_t* unified_kv_indices, const int32_t* prefix_lens,
+                                 float sm_scale, float logit_cap, const pkv_attn_desc_t* desc,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!prefix_lens && desc && desc->bs > 0 && desc->total_q_tokens > 0)
+    return fail(PKV_ERR_INVALID, "prefix_lens is NULL");
+  static const int32_t kNoPrefix = 0;  // never read: the call returns before any launch
+  return attention_call(q_extend, nullptr, nullptr, o, k_pool, v_pool, qo_indptr, unified_kv_indptr,
+                        unified_kv_indices, prefix_lens ? prefix_lens : &kNoPrefix, sm_scale, logit_cap, desc,
+                        workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -127,8 +127,8 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   const int qi = lane & 31, hi = lane >> 5;
   const int G = a.group;
   const int b = it.b, g = it.g;
-  const int q0 = a.qo_indptr[b], E = a.qo_indptr[b + 1] - q0;
-  const int kvs = a.kv_indptr[b], P = a.kv_indptr[b + 1] - kvs;
+  const SeqKeys sk = seq_keys(a.qo_indptr, a.kv_indptr, a.prefix_lens, b);
+  const int q0 = sk.q0, E = sk.E, kvs = sk.kvs, P = sk.P;
   const int R = E * G;
 
   // this lane's query row
@@ -136,13 +136,13 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   const bool valid = r < R;
   const int tok = valid ? r / G : 0;
   const int head = g * G + (valid ? r % G : 0);
-  const int lim = valid ? P + tok : -1;  // last visible key
+  const int lim = valid ? min(P + tok, sk.n_keys - 1) : -1;  // last visible key
   // the wave's token range (rows are token-major) and the workgroup's last visible key
   const int rw0 = it.t * BM + wv * 32;
   const bool wave_live = rw0 < R;
-  const int i_lo_w = wave_live ? rw0 / G : 0;
-  const int i_hi_w = wave_live ? min(R - 1, rw0 + 31) / G : 0;
-  const int key_last = P + min(R - 1, it.t * BM + BM - 1) / G;
+  const int lim_lo_w = min(P + (wave_live ? rw0 / G : 0), sk.n_keys - 1);
+  const int lim_hi_w = min(P + (wave_live ? min(R - 1, rw0 + 31) / G : 0), sk.n_keys - 1);
+  const int key_last = min(P + min(R - 1, it.t * BM + BM - 1) / G, sk.n_keys - 1);
 
   const gptr<T> kpool = (gptr<T>)a.k_pool;
   const gptr<T> vpool = (gptr<T>)a.v_pool;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   int64_t slot_next = 0;  // prefetched pool slot for the key this thread owns two tiles ahead
   auto fetch_slot = [&](int kt) __attribute__((always_inline)) {
     const int j = kt * BN + tid;
-    slot_next = (tid < BN && j < P && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
+    slot_next = (tid < BN && j < sk.n_idx && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
   };
   auto write_ptrs = [&](int kt) __attribute__((always_inline)) {
     if (tid < BN) {
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
       gptr<T> kp = zrow;
       gptr<T> vp = zrow;
       if (j <= key_last) {
-        if (j < P) {
+        if (j < sk.n_idx) {
           kp = kpool + slot_next * a.kp_ss + (int64_t)g * a.kp_sh;
           vp = vpool + slot_next * a.vp_ss + (int64_t)g * a.vp_sh;
         } else {
@@ -282,8 +282,8 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
     if (kt + 2 < kt1) fetch_slot(kt + 2);
 
     const int j0 = kt * BN;
-    if (wave_live && j0 <= P + i_hi_w) {
-      const bool need_mask = j0 + BN - 1 > P + i_lo_w;
+    if (wave_live && j0 <= lim_hi_w) {
+      const bool need_mask = j0 + BN - 1 > lim_lo_w;
 
       // S^T = K Q^T for the tile's 32-key blocks
       f32x16 s[NKB];

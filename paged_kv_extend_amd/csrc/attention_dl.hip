@@ -162,18 +162,19 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   auto o_block = [&](int db) __attribute__((always_inline)) { return C::SPLIT > 1 ? 2 * db + half : db; };
   const int G = a.group;
   const int b = it.b, g = it.g;
-  const int q0 = a.qo_indptr[b], E = a.qo_indptr[b + 1] - q0;
-  const int kvs = a.kv_indptr[b], P = a.kv_indptr[b + 1] - kvs;
+  const SeqKeys sk = seq_keys(a.qo_indptr, a.kv_indptr, a.prefix_lens, b);
+  const int q0 = sk.q0, E = sk.E, kvs = sk.kvs, P = sk.P;
   const int R = E * G;
 
   const int r = it.t * BM + rg * 32 + qi;
   const bool valid = r < R;
-  const int lim = valid ? P + r / G : -1;  // last visible key of this lane's row
+  const int lim = valid ? min(P + r / G, sk.n_keys - 1) : -1;  // last visible key of this lane's row
   const int rw0 = it.t * BM + rg * 32;
   const bool wave_live = rw0 < R;
-  const int i_lo_w = wave_live ? rw0 / G : 0;
-  const int i_hi_w = wave_live ? min(R - 1, rw0 + 31) / G : 0;
-  const int key_last = P + min(R - 1, it.t * BM + BM - 1) / G;
+  // the wave's smallest and largest last visible key
+  const int lim_lo_w = min(P + (wave_live ? rw0 / G : 0), sk.n_keys - 1);
+  const int lim_hi_w = min(P + (wave_live ? min(R - 1, rw0 + 31) / G : 0), sk.n_keys - 1);
+  const int key_last = min(P + min(R - 1, it.t * BM + BM - 1) / G, sk.n_keys - 1);
 
   const gptr<T> kpool = (gptr<T>)a.k_pool;
   const gptr<T> vpool = (gptr<T>)a.v_pool;
@@ -209,7 +210,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
     kp = zrow;
     vp = zrow;
     if (j <= key_last) {
-      if (j < P) {
+      if (j < sk.n_idx) {
         kp = kpool_g + slot * kp_ss;
         vp = vpool_g + slot * vp_ss;
       } else {
@@ -239,7 +240,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
       const int o = i * 256 + lane * 4;  // byte offset in the tile's slot block
       const int j = kt * BN + o / 8;
       gptr<char> src = (gptr<char>)zrow;
-      if (j < P && j <= key_last) src = (gptr<char>)a.kv_indices + (int64_t)(kvs + j) * 8 + (o & 4);
+      if (j < sk.n_idx && j <= key_last) src = (gptr<char>)a.kv_indices + (int64_t)(kvs + j) * 8 + (o & 4);
       load_lds_4((gptr<void>)src, lds_addr(&slots[kt & 3][0]) + i * 256);
     }
   };
@@ -340,7 +341,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
       for (int e = lane; e < (BN > 64 ? BN : 64); e += 64) {
         if (e < BN) {
           const int j = (kt0 + v) * BN + e;
-          const int64_t slot = (j < P && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
+          const int64_t slot = (j < sk.n_idx && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
           gptr<T> kp, vp;
           key_ptrs(j, slot, kp, vp);
           kptr[(kt0 + v) % NS][e] = kp;
@@ -363,7 +364,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   }
 
   // ---- tile math
-  auto active = [&](int kt) __attribute__((always_inline)) { return wave_live && kt * BN <= P + i_hi_w; };
+  auto active = [&](int kt) __attribute__((always_inline)) { return wave_live && kt * BN <= lim_hi_w; };
 
   // S^T = K Q^T over this wave's Q dims
   auto qk = [&](int kt, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
@@ -427,7 +428,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   // max and lazy rescale; returns the value subtracted in the exponent
   auto softmax_head = [&](int kt, f32x16 (&s)[NKB]) __attribute__((always_inline)) -> float {
     const int j0 = kt * BN;
-    const bool need_mask = j0 + BN - 1 > P + i_lo_w;
+    const bool need_mask = j0 + BN - 1 > lim_lo_w;
     if constexpr (CAP) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)

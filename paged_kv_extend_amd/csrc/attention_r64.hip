@@ -72,8 +72,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int qi = lane & 31, hi = lane >> 5;
   const int G = a.group;
   const int b = it.b, g = it.g;
-  const int q0 = a.qo_indptr[b], E = a.qo_indptr[b + 1] - q0;
-  const int kvs = a.kv_indptr[b], P = a.kv_indptr[b + 1] - kvs;
+  const SeqKeys sk = seq_keys(a.qo_indptr, a.kv_indptr, a.prefix_lens, b);
+  const int q0 = sk.q0, E = sk.E, kvs = sk.kvs, P = sk.P;
   const int R = E * G;
 
   const int rw0 = it.t * BM + wv * 64;  // first row of this wave
@@ -83,12 +83,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int rs = 0; rs < RS; ++rs) {
     const int r = rw0 + rs * 32 + qi;
     valid[rs] = r < R;
-    lim[rs] = valid[rs] ? P + r / G : -1;  // last visible key of this lane's row
+    lim[rs] = valid[rs] ? min(P + r / G, sk.n_keys - 1) : -1;  // last visible key of this lane's row
   }
   const bool wave_live = rw0 < R;
-  const int i_lo_w = wave_live ? rw0 / G : 0;
-  const int i_hi_w = wave_live ? min(R - 1, rw0 + 63) / G : 0;
-  const int key_last = P + min(R - 1, it.t * BM + BM - 1) / G;
+  const int lim_lo_w = min(P + (wave_live ? rw0 / G : 0), sk.n_keys - 1);
+  const int lim_hi_w = min(P + (wave_live ? min(R - 1, rw0 + 63) / G : 0), sk.n_keys - 1);
+  const int key_last = min(P + min(R - 1, it.t * BM + BM - 1) / G, sk.n_keys - 1);
 
   const gptr<T> kpool = (gptr<T>)a.k_pool;
   const gptr<T> vpool = (gptr<T>)a.v_pool;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int64_t slot_next = 0;
   auto fetch_slot = [&](int kt) __attribute__((always_inline)) {
     const int j = kt * BN + lane;
-    slot_next = (lane < BN && j < P && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
+    slot_next = (lane < BN && j < sk.n_idx && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
   };
   auto write_ptrs = [&](int kt) __attribute__((always_inline)) {
     if (lane < BN) {
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       gptr<T> kp = zrow;
       gptr<T> vp = zrow;
       if (j <= key_last) {
-        if (j < P) {
+        if (j < sk.n_idx) {
           kp = kpool + slot_next * a.kp_ss + (int64_t)g * a.kp_sh;
           vp = vpool + slot_next * a.vp_ss + (int64_t)g * a.vp_sh;
         } else {
@@ -168,8 +168,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < C::LOADS; ++i) load_lds_16((gptr<void>)src[i], st + (i * C::NW + wv) * 1024);
   };
 
-  auto active = [&](int kt) __attribute__((always_inline)) { return wave_live && kt * BN <= P + i_hi_w; };
-  auto needs_mask = [&](int kt) __attribute__((always_inline)) { return kt * BN + BN - 1 > P + i_lo_w; };
+  auto active = [&](int kt) __attribute__((always_inline)) { return wave_live && kt * BN <= lim_hi_w; };
+  auto needs_mask = [&](int kt) __attribute__((always_inline)) { return kt * BN + BN - 1 > lim_lo_w; };
 
   typedef f32x16 STile[RS][NKB];  // S^T of one key tile, both row blocks
   typedef bf16x8 PTile[NKB][2][RS];  // probabilities in B-operand layout

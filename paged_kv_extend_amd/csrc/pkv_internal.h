@@ -72,6 +72,10 @@ struct AttnArgs {
   const int32_t* qo_indptr;
   const int32_t* kv_indptr;
   const int64_t* kv_indices;
+  // NULL: two-part call (kv_indices hold the prefix, new tokens' K/V are
+  // k_ext / v_ext rows).  Else unified call: kv_indices hold every key and
+  // prefix_lens[b] of sequence b's keys are prefix keys.
+  const int32_t* prefix_lens;
   int64_t q_st, q_sh, o_st, o_sh, ke_st, ke_sh, ve_st, ve_sh, kp_ss, kp_sh, vp_ss, vp_sh;
   int32_t group;     // query heads per KV head
   int32_t use_cap;   // soft-cap enabled
@@ -90,6 +94,7 @@ struct AttnArgs {
 struct PlanArgs {
   const int32_t* qo_indptr;
   const int32_t* kv_indptr;
+  const int32_t* prefix_lens;  // as in AttnArgs
   int32_t bs, num_kv_heads, group, bm, bn;
   int32_t slots;          // workgroups resident at once on the device
   int32_t min_chunk;      // never split below this many KV tiles
@@ -102,6 +107,38 @@ struct PlanArgs {
   MergeItem* merge;  // [max_merge]
   int32_t* scratch;  // [3 * bs + 1 + 3 * max_items], used when the batch exceeds the LDS arrays
 };
+
+// Keys of sequence b as the attention kernels see them.
+//  Two-part call: P = prefix indices of b (keys j < P through kv_indices),
+//    keys P .. P+E-1 are new-token rows; n_idx = P, n_keys = P + E.
+//  Unified call (page extend_attention.py, _fwd_kernel_unified): every key j
+//    < span goes through kv_indices, P = prefix_lens[b]; keys at or past P + E
+//    are never visible, so n_idx = n_keys = min(span, P + E), which also keeps
+//    every index read inside the sequence's own span.
+// A query at new-token position i sees key j iff j < n_keys and j <= P + i.
+struct SeqKeys {
+  int q0, E;   // first new-token row, new tokens
+  int kvs, P;  // first index of the sequence, prefix keys
+  int n_idx;   // keys read through kv_indices: j < n_idx
+  int n_keys;  // keys that exist: j < n_keys
+};
+__device__ __forceinline__ SeqKeys seq_keys(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                            const int32_t* prefix_lens, int b) {
+  SeqKeys k;
+  k.q0 = qo_indptr[b];
+  k.E = qo_indptr[b + 1] - k.q0;
+  k.kvs = kv_indptr[b];
+  const int span = kv_indptr[b + 1] - k.kvs;
+  if (prefix_lens) {
+    k.P = prefix_lens[b];
+    k.n_idx = k.n_keys = min(span, k.P + k.E);
+  } else {
+    k.P = span;
+    k.n_idx = span;
+    k.n_keys = span + k.E;
+  }
+  return k;
+}
 
 // Kernel variants: (dtype, lq, lv).  Returns false when unsupported.
 bool attn_tiling(int dtype, int lq, int lv, Tiling* t);

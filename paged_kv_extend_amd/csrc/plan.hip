@@ -121,7 +121,8 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   int local = 0;
   for (int b = s0; b < s1; ++b) {
     const int E = a.qo_indptr[b + 1] - a.qo_indptr[b];
-    const int P = a.kv_indptr[b + 1] - a.kv_indptr[b];
+    // prefix keys: the sequence's index span, or prefix_lens[b] for a unified call
+    const int P = a.prefix_lens ? a.prefix_lens[b] : a.kv_indptr[b + 1] - a.kv_indptr[b];
     seq_e[b] = E;
     seq_p[b] = P;
     local += H * ceil_div(E * G, BM);

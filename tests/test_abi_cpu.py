@@ -143,3 +143,27 @@ def test_index_build_argument_errors_without_device():
     assert lib.build_unified_kv_indices(p, p, p, p, p, -1, 10, 5, p, p, 15, p, None) == -1
     assert lib.build_unified_kv_indices(p, p, p, p, p, 3, 10, 5, None, p, 15, p, None) == -1
     assert lib.build_unified_kv_indices(p, None, p, p, p, 3, 10, 5, p, p, 15, p, None) == -1
+
+
+def test_unified_argument_errors_without_device():
+    lib = pkv.library()
+    p = 4096
+    d = desc()
+    # no prefix_lens with rows to compute
+    assert lib.extend_attention_fwd_unified(p, p, p, p, p, p, p, None, 0.0, 0.0, ctypes.byref(d), p,
+                                            1 << 30, None) == -1
+    assert "prefix_lens" in pkv.last_error()
+    assert lib.extend_attention_fwd_unified(p, p, p, p, p, p, p, p, 0.0, 0.0, ctypes.byref(desc(bs=0)), p,
+                                            1 << 30, None) == 0
+    assert lib.extend_attention_fwd_unified(p, None, p, p, p, p, p, p, 0.0, 0.0, ctypes.byref(d), p,
+                                            1 << 30, None) == -1
+    assert lib.extend_attention_fwd_unified(p, p, p, p, p, p, p, p, 0.0, 0.0, ctypes.byref(d), p, 16,
+                                            None) == -3
+
+
+def test_unified_kernel_name_uses_the_pool_only():
+    mla = desc(lq=576, lv=512, num_kv_heads=1, q_stride_head=576, q_stride_tok=32 * 576, ke_stride_tok=0,
+               ke_stride_head=0, kp_stride_slot=576, kp_stride_head=576, o_stride_tok=32 * 512,
+               o_stride_head=512, ve_stride_tok=0, ve_stride_head=0, vp_stride_slot=576, vp_stride_head=576)
+    assert kernel_name(mla, None, None, 12288, 12288) == "attn_dl_kernel"
+    assert kernel_name(mla, None, None, 12288, 16384) == "attn_kernel"
