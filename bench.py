@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel", default="auto", help="attention kernel preference: auto, r64, dl, attn")
+    ap.add_argument("--path", default="two-part", choices=["two-part", "unified"],
+                    help="two-part: prefix through kv_indices, new tokens from k/v_extend (the index build "
+                         "runs beside it); unified: attention reads every key through the index build's output")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attention_traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -124,9 +127,15 @@ def main():
         s = sets[i % copies]
         pkv.build_unified_kv_indices(s["kv_indptr"], s["kv_indices"], s["extend_start_loc"],
                                      s["extend_seq_lens"], s["extend_kv_indices"], w.bs, out=s["uni"])
-        pkv.extend_attention_fwd(s["q"], s["k_ext"], s["v_ext"], s["o"], s["k_pool"], s["v_pool"],
-                                 s["qo_indptr"], s["kv_indptr"], s["kv_indices"], sm_scale=w.sm_scale,
-                                 logit_cap=w.logit_cap, workspace=s["ws"])
+        if args.path == "unified":
+            u_indptr, u_indices, u_plens = s["uni"]
+            pkv.extend_attention_fwd_unified(s["q"], s["o"], s["k_pool"], s["v_pool"], s["qo_indptr"], u_indptr,
+                                             u_indices, u_plens, sm_scale=w.sm_scale, logit_cap=w.logit_cap,
+                                             workspace=s["ws"])
+        else:
+            pkv.extend_attention_fwd(s["q"], s["k_ext"], s["v_ext"], s["o"], s["k_pool"], s["v_pool"],
+                                     s["qo_indptr"], s["kv_indptr"], s["kv_indices"], sm_scale=w.sm_scale,
+                                     logit_cap=w.logit_cap, workspace=s["ws"])
 
     for i in range(args.warmup):
         step(i)
@@ -152,7 +161,8 @@ def main():
     if os.path.exists(args.traffic_json):
         with open(args.traffic_json) as f:
             tj = json.load(f)
-        if tj.get("workload") == args.workload and tj.get("kernel_source_sha") == kernel_source_sha():
+        if (tj.get("workload") == args.workload and tj.get("kernel_source_sha") == kernel_source_sha()
+                and args.path == "two-part"):
             traffic = tj.get("bytes_per_launch")
     line = {
         "metric": "extend-attention TFLOP/s (causal-adjusted) + % of bf16 MFMA peak, 1 GPU",
@@ -171,7 +181,7 @@ def main():
                    "q_heads": w.cfg.hq, "kv_heads": w.cfg.hkv, "lq": w.cfg.lq, "lv": w.cfg.lv,
                    "extend_tokens": w.total_q, "prefix_tokens": w.num_prefix, "seed": w.cfg.seed,
                    "causal_gflop": round(flops / 1e9, 3), "algorithmic_mb": round(algo_bytes / 1e6, 2),
-                   "input_copies_rotated": copies, "wall_s_timed": round(wall, 3)},
+                   "input_copies_rotated": copies, "wall_s_timed": round(wall, 3), "path": args.path},
         "mfma_frac_step": round(flops / (ms_per_step * 1e-3) / 1e12 / peak, 4),
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -188,7 +198,8 @@ def kernel_source_sha():
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("device_common.h", "attention.hip", "attention_dl.hip", "attention_r64.hip", "plan.hip"):
+    for f in ("device_common.h", "pkv_internal.h", "attention.hip", "attention_dl.hip", "attention_r64.hip",
+              "plan.hip"):
         with open(os.path.join(ROOT, "paged_kv_extend_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
