@@ -24,9 +24,9 @@
 //    MFMA operand reads of K and the transposing reads of V stay free of bank
 //    conflicts.
 //  * Head dim 128 runs 256 rows (8 waves, two per SIMD) per workgroup, so one
-//    K/V tile in LDS serves twice the rows of a 128-row workgroup; waves 4-7
-//    issue every load and build the row tables while waves 0-3 only compute
-//    (waves w and w+4 share a SIMD, so each SIMD holds one loading wave).
+//    K/V tile in LDS serves twice the rows of a 128-row workgroup; waves 0-3
+//    request the next tile's K rows after each barrier and waves 4-7 its V
+//    rows after their QK products (waves w and w+4 share a SIMD).
 //  * When V is the first Lv columns of K (the MLA layout on page
 //    "cpu_graph_runner.py", qkv_proj_with_rope: v = k.narrow(-1, 0, lv)), only
 //    the K tile is loaded and the V^T operand is read from it.
