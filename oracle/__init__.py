@@ -60,6 +60,10 @@ def _load():
         lib.oracle_extend_attention_unified.argtypes = (
             [i32] + [P, i64, i64] * 3 + [i64, P, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32])
         lib.oracle_extend_attention_unified.restype = ctypes.c_int
+        lib.oracle_store_kv_cache.argtypes = [i32, i64, i32, i32, i32] + [P, i64, i64] * 4 + [i64, P]
+        lib.oracle_store_kv_cache.restype = ctypes.c_int
+        lib.oracle_gather_kv_indices.argtypes = [P, i64, P, P, P, i32, P, P]
+        lib.oracle_gather_kv_indices.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -179,6 +183,49 @@ def extend_attention_unified(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices
     if rc != 0:
         raise ValueError(f"oracle unified attention failed: {rc}")
     return out[:n]
+
+
+def store_kv_cache(k_ext, v_ext, k_pool, v_pool, out_cache_loc):
+    """KV-cache store into copies of the pools: returns (k_pool', v_pool').
+
+    Arrays [tokens|slots, heads, dim] with a contiguous last dim, bf16 as
+    uint16 bit patterns or float32.  When v_pool is a view into k_pool (V the
+    first lv columns of K), pass k_pool for both and v_ext a view of k_ext:
+    the copies then alias the same way."""
+    lib = _load()
+    kp = np.array(k_pool, copy=True)
+    alias = v_pool is k_pool or (isinstance(v_pool, np.ndarray) and np.shares_memory(v_pool, k_pool))
+    vp = kp[..., :v_pool.shape[2]] if alias else np.array(v_pool, copy=True)
+    loc = np.ascontiguousarray(out_cache_loc, np.int64)
+    if loc.size == 0:
+        loc = np.zeros(1, np.int64)
+    n = len(np.asarray(out_cache_loc))
+    args = [k_ext.itemsize, n, k_pool.shape[1], k_ext.shape[2], v_ext.shape[2]]
+    for x in (k_ext, v_ext, kp, vp):
+        s0, s1 = _strides(x)
+        args += [_ptr(x) if x.size else 0, s0, s1]
+    args += [kp.shape[0], _ptr(loc)]
+    rc = lib.oracle_store_kv_cache(*args)
+    if rc != 0:
+        raise ValueError(f"oracle store failed: {rc}")
+    return kp, vp
+
+
+def gather_kv_indices(req_to_token, req_pool_indices, kv_lens, kv_start_idx=None):
+    """Prefix index gather: returns (kv_indptr int32 [bs+1], kv_indices int64)."""
+    lib = _load()
+    r2t = np.ascontiguousarray(req_to_token, np.int32)
+    rpi = np.ascontiguousarray(req_pool_indices, np.int64)
+    lens = np.ascontiguousarray(kv_lens, np.int32)
+    bs = len(lens)
+    start = None if kv_start_idx is None else np.ascontiguousarray(kv_start_idx, np.int32)
+    indptr = np.zeros(bs + 1, np.int32)
+    out = np.zeros(max(1, int(lens.sum()) if bs else 0), np.int64)
+    rc = lib.oracle_gather_kv_indices(_ptr(r2t), r2t.shape[1], _ptr(rpi) if bs else None, _ptr(lens) if bs else None,
+                                      _ptr(start) if start is not None else None, bs, _ptr(indptr), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle gather failed: {rc}")
+    return indptr, out[:int(indptr[-1])]
 
 
 def extend_attention_workload(w, rows=None, num_threads=0):

@@ -17,8 +17,13 @@
  *    call_begin_forward (the prefix is read through kv_indptr/kv_indices,
  *    the new tokens' K/V share qo_indptr with the queries).
  *
- * Parity of both functions is pinned by tests/test_oracle_pins.py (worked
- * example, library attention, closed forms and invariants).
+ *  - the steps before attention: the KV-cache store of the new tokens
+ *    (page "flashinfer_backend.py", forward_extend, set_kv_buffer) and the
+ *    prefix index gather from the request-to-token table (the same page,
+ *    create_flashinfer_kv_indices_triton).
+ *
+ * Parity of every function is pinned by tests/test_oracle_pins.py (worked
+ * examples, library routines, closed forms and invariants).
  */
 #include <math.h>
 #include <stdint.h>
@@ -310,6 +315,62 @@ int oracle_extend_attention_unified(int32_t dtype,
     free(acc);
   }
   return status;
+}
+
+/*
+ * KV-cache store of the new tokens (flashinfer_backend.py, forward_extend:
+ * set_kv_buffer(layer, cache_loc, k, v) before attention reads the pool):
+ *   k_pool[out_cache_loc[t], g, :lq] = k_ext[t, g, :lq]
+ *   v_pool[out_cache_loc[t], g, :lv] = v_ext[t, g, :lv]
+ * for every token t < n_tokens and KV head g; other slots are left alone.
+ * Elements are copied as raw bytes of elem_bytes each.  Slots out of
+ * [0, pool_slots) are an error (nothing is written then).
+ */
+int oracle_store_kv_cache(int32_t elem_bytes, int64_t n_tokens, int32_t hkv, int32_t lq, int32_t lv,
+                          const void* k_ext, int64_t ke_st, int64_t ke_sh,
+                          const void* v_ext, int64_t ve_st, int64_t ve_sh,
+                          void* k_pool, int64_t kp_ss, int64_t kp_sh,
+                          void* v_pool, int64_t vp_ss, int64_t vp_sh,
+                          int64_t pool_slots, const int64_t* out_cache_loc) {
+  if (n_tokens < 0 || hkv <= 0 || lq < 0 || lv < 0 || (elem_bytes != 2 && elem_bytes != 4)) return ORACLE_EINVAL;
+  for (int64_t t = 0; t < n_tokens; ++t)
+    if (out_cache_loc[t] < 0 || out_cache_loc[t] >= pool_slots) return ORACLE_ERANGE;
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    int64_t slot = out_cache_loc[t];
+    for (int32_t g = 0; g < hkv; ++g) {
+      memcpy((char*)k_pool + (slot * kp_ss + (int64_t)g * kp_sh) * elem_bytes,
+             (const char*)k_ext + (t * ke_st + (int64_t)g * ke_sh) * elem_bytes, (size_t)lq * elem_bytes);
+      memcpy((char*)v_pool + (slot * vp_ss + (int64_t)g * vp_sh) * elem_bytes,
+             (const char*)v_ext + (t * ve_st + (int64_t)g * ve_sh) * elem_bytes, (size_t)lv * elem_bytes);
+    }
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * Prefix index gather from the request-to-token table
+ * (flashinfer_backend.py, create_flashinfer_kv_indices_triton and the
+ * kv_indptr running sum of call_begin_forward):
+ *   kv_indptr[0] = 0, kv_indptr[b+1] = kv_indptr[b] + kv_lens[b]
+ *   kv_indices[kv_indptr[b] + o] = req_to_token[req_pool_indices[b] * stride + start_b + o]
+ * for o < kv_lens[b], start_b = kv_start_idx[b] (0 when kv_start_idx is NULL).
+ * req_to_token holds int32 slots; kv_indices are written as int64.
+ */
+int oracle_gather_kv_indices(const int32_t* req_to_token, int64_t stride, const int64_t* req_pool_indices,
+                             const int32_t* kv_lens, const int32_t* kv_start_idx, int32_t bs,
+                             int32_t* kv_indptr, int64_t* kv_indices) {
+  if (bs < 0 || stride < 0) return ORACLE_EINVAL;
+  kv_indptr[0] = 0;
+  for (int32_t b = 0; b < bs; ++b) {
+    if (kv_lens[b] < 0) return ORACLE_EINVAL;
+    kv_indptr[b + 1] = kv_indptr[b] + kv_lens[b];
+  }
+  for (int32_t b = 0; b < bs; ++b) {
+    int64_t start = kv_start_idx ? kv_start_idx[b] : 0;
+    for (int32_t o = 0; o < kv_lens[b]; ++o)
+      kv_indices[kv_indptr[b] + o] = (int64_t)req_to_token[req_pool_indices[b] * stride + start + o];
+  }
+  return ORACLE_OK;
 }
 
 int oracle_max_threads(void) {

@@ -27,6 +27,10 @@ MUTATIONS = {
     "first_weight_bias": ("double wgt = exp(s[j] - m);", "double wgt = exp(s[j] - m) * (j == 0 ? 1.0001 : 1.0);"),
     "unified_drops_diagonal": ("seen[j] = (j < P) || (j - P <= i);", "seen[j] = (j < P) || (j - P < i);"),
     "unified_causal_prefix": ("seen[j] = (j < P) || (j - P <= i);", "seen[j] = (j - P <= i);"),
+    "store_k_rows_by_token": ("memcpy((char*)k_pool + (slot * kp_ss", "memcpy((char*)k_pool + (t * kp_ss"),
+    "gather_ignores_start": ("int64_t start = kv_start_idx ? kv_start_idx[b] : 0;", "int64_t start = 0;"),
+    "gather_indptr_skips_first": ("kv_indptr[b + 1] = kv_indptr[b] + kv_lens[b];",
+                                  "kv_indptr[b + 1] = kv_indptr[b] + kv_lens[b] + (b == 0);"),
     "unified_batch_index_base": ("int64_t koff = kv_indices[kv_indptr[b] + j] * kp_ss",
                                  "int64_t koff = kv_indices[kv_indptr[0] + j] * kp_ss"),
 }

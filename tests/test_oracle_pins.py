@@ -326,3 +326,71 @@ def test_unified_pool_slot_permutation_is_exact():
     k2[perm] = w.k_pool
     v2[perm] = w.v_pool
     assert np.array_equal(_unified(w, indptr, perm[indices], plens, k2, v2), base)
+
+
+# ----------------------------------------------------------------------------- steps before attention
+# (page flashinfer_backend.py: set_kv_buffer of the new tokens in forward_extend, and
+# create_flashinfer_kv_indices_triton for the prefix indices)
+
+def test_gather_worked_example():
+    with open(os.path.join(GOLDEN, "req_to_token_gather_worked_example.json")) as f:
+        ex = json.load(f)
+    indptr, idx = oracle.gather_kv_indices(ex["req_to_token"], ex["req_pool_indices"], ex["kv_lens"],
+                                           ex["kv_start_idx"])
+    assert indptr.tolist() == ex["expected_kv_indptr"]
+    assert idx.tolist() == ex["expected_kv_indices"]
+    _, idx0 = oracle.gather_kv_indices(ex["req_to_token"], ex["req_pool_indices"], ex["kv_lens"])
+    assert idx0.tolist() == ex["expected_kv_indices_without_start"]
+
+
+@pytest.mark.parametrize("bs,with_start", [(0, False), (1, True), (7, False), (33, True)])
+def test_gather_matches_slicing(bs, with_start):
+    rng = np.random.default_rng(bs)
+    table = rng.integers(0, 1 << 30, size=(40, 300)).astype(np.int32)
+    rpi = rng.integers(0, 40, size=bs)
+    start = rng.integers(0, 100, size=bs) if with_start else np.zeros(bs, np.int64)
+    lens = rng.integers(0, 200, size=bs)
+    indptr, idx = oracle.gather_kv_indices(table, rpi, lens, start if with_start else None)
+    want = [table[r, s:s + n] for r, s, n in zip(rpi, start, lens)]
+    want = np.concatenate(want).astype(np.int64) if bs else np.zeros(0, np.int64)
+    assert np.array_equal(idx, want)
+    assert indptr.tolist() == [0] + np.cumsum(lens).tolist()
+
+
+def test_store_matches_fancy_index_assignment():
+    rng = np.random.default_rng(7)
+    k_ext = rng.integers(0, 1 << 16, size=(13, 3, 64)).astype(np.uint16)
+    v_ext = rng.integers(0, 1 << 16, size=(13, 3, 32)).astype(np.uint16)
+    k_pool = rng.integers(0, 1 << 16, size=(50, 3, 64)).astype(np.uint16)
+    v_pool = rng.integers(0, 1 << 16, size=(50, 3, 32)).astype(np.uint16)
+    loc = rng.permutation(50)[:13]
+    kp, vp = oracle.store_kv_cache(k_ext, v_ext, k_pool, v_pool, loc)
+    want_k, want_v = k_pool.copy(), v_pool.copy()
+    want_k[loc] = k_ext
+    want_v[loc] = v_ext
+    assert np.array_equal(kp, want_k) and np.array_equal(vp, want_v)
+
+
+def test_store_with_v_inside_k_writes_k_rows():
+    rng = np.random.default_rng(8)
+    k_ext = rng.standard_normal((5, 1, 48)).astype(np.float32)
+    k_pool = rng.standard_normal((20, 1, 48)).astype(np.float32)
+    loc = np.array([3, 19, 0, 7, 11])
+    kp, vp = oracle.store_kv_cache(k_ext, k_ext[..., :32], k_pool, k_pool[..., :32], loc)
+    want = k_pool.copy()
+    want[loc] = k_ext
+    assert np.array_equal(kp, want) and np.shares_memory(kp, vp) and np.array_equal(vp, want[..., :32])
+
+
+@pytest.mark.parametrize("case", SDPA_CASES[:3], ids=lambda c: f"{c['dtype']}-{c['lq']}x{c['lv']}")
+def test_store_then_unified_attention_is_library_attention(case):
+    # overwrite the new tokens' pool rows, store them back, and attend through
+    # the unified indices: the library attention over the concatenation
+    w = wl.custom(**case)
+    junk_k = np.full_like(w.k_pool, 0x7FC0 if w.cfg.dtype == "bf16" else 0)
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    kp[w.extend_kv_indices] = junk_k[w.extend_kv_indices]
+    vp[w.extend_kv_indices] = 0
+    kp, vp = oracle.store_kv_cache(w.k_ext, w.v_ext, kp, vp, w.extend_kv_indices)
+    got = _unified(w, *_unified_arrays(w), k_pool=kp, v_pool=vp)
+    np.testing.assert_allclose(got, sdpa_reference(w), rtol=0, atol=1e-12)
