@@ -85,6 +85,35 @@ int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* pre
                              int64_t capacity, int32_t* prefix_lens, void* stream);
 
 /*
+ * Prefix index gather from the request-to-token table.
+ * Page "flashinfer_backend.py": create_flashinfer_kv_indices_triton, and the
+ * running sum kv_indptr[1:bs+1] = cumsum(paged_kernel_lens) of
+ * call_begin_forward (computed here on the device).  For b in [0, bs):
+ *   kv_indptr[0] = 0, kv_indptr[b+1] = kv_indptr[b] + kv_lens[b]
+ *   kv_indices[kv_indptr[b] + o] = req_to_token[req_pool_indices[b] * req_to_token_stride + s_b + o]
+ *   for o < kv_lens[b], s_b = kv_start_idx[b] (0 when kv_start_idx is NULL).
+ * The table holds int32 slots (as the page's request-to-token pool does); the
+ * indices are written as int64, the type extend_attention_fwd reads.
+ *
+ * Arguments (device pointers unless noted):
+ *  req_to_token       int32[rows * req_to_token_stride] (row-major table).
+ *  req_to_token_stride host int, >= 0: elements between table rows.
+ *  req_pool_indices   int64[bs], table rows.
+ *  kv_lens            int32[bs], >= 0.
+ *  kv_start_idx       int32[bs] or NULL.
+ *  bs                 host int, >= 0; bs == 0 writes kv_indptr[0] = 0 only.
+ *  kv_indptr          out int32[bs+1].
+ *  kv_indices         out int64[capacity]; nothing at or past capacity is
+ *                     written, whatever the lengths hold.
+ *  capacity           host int >= 0: the sum of kv_lens, as the caller
+ *                     sizes the output (the page's paged_kernel_lens_sum).
+ * The caller guarantees that every request's run lies inside the table.
+ */
+int gather_kv_indices(const int32_t* req_to_token, int64_t req_to_token_stride, const int64_t* req_pool_indices,
+                      const int32_t* kv_lens, const int32_t* kv_start_idx, int32_t bs, int32_t* kv_indptr,
+                      int64_t* kv_indices, int64_t capacity, void* stream);
+
+/*
  * Shapes and strides of one extend-attention call.  Strides are in
  * ELEMENTS; the last dimension of every tensor is contiguous.
  *
@@ -173,6 +202,27 @@ int extend_attention_fwd(const void* q_extend, const void* k_extend, const void*
                          const int64_t* kv_indices, float sm_scale, float logit_cap,
                          const pkv_attn_desc_t* desc, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * KV-cache store of the new tokens.
+ * Page "flashinfer_backend.py": forward_extend stores the new tokens' K/V
+ * into the pool (set_kv_buffer(layer, cache_loc, k, v)) before the paged
+ * attention reads it:
+ *   k_pool[out_cache_loc[t], g, :lq] = k_extend[t, g, :lq]
+ *   v_pool[out_cache_loc[t], g, :lv] = v_extend[t, g, :lv]
+ * for t < desc->total_q_tokens and every KV head g; other slots are left
+ * alone.  When V lies inside K (the MLA layout, see pkv_attn_desc_t) the K
+ * row carries it and is written once.
+ *
+ * Arguments (device pointers unless noted):
+ *  k_extend, v_extend, k_pool, v_pool: as in pkv_attn_desc_t (q and o strides
+ *              of desc are not used).
+ *  out_cache_loc int64[total_q_tokens], each in [0, pool_slots), distinct.
+ *  desc        host pointer, checked as for extend_attention_fwd.
+ *  stream      hipStream_t.
+ */
+int store_kv_cache(const void* k_extend, const void* v_extend, void* k_pool, void* v_pool,
+                   const int64_t* out_cache_loc, const pkv_attn_desc_t* desc, void* stream);
 
 /*
  * Unified one-stage extend attention.

@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_fwd_unified",
-           "extend_attention_workspace_size",
+           "extend_attention_workspace_size", "store_kv_cache", "gather_kv_indices",
            "extend_attention_kernel_name", "extend_attention_prefer_kernel",
            "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "LIB_PATH", "PkvError"]
 
@@ -64,6 +64,10 @@ def library() -> ctypes.CDLL:
     lib.extend_attention_fwd_unified.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
                                                  ctypes.POINTER(AttnDesc), P, ctypes.c_size_t, P]
     lib.extend_attention_fwd_unified.restype = ctypes.c_int
+    lib.store_kv_cache.argtypes = [P, P, P, P, P, ctypes.POINTER(AttnDesc), P]
+    lib.store_kv_cache.restype = ctypes.c_int
+    lib.gather_kv_indices.argtypes = [P, i64, P, P, P, i32, P, P, i64, P]
+    lib.gather_kv_indices.restype = ctypes.c_int
     lib.pkv_profile_enable.argtypes = [ctypes.c_int]
     lib.pkv_profile_enable.restype = ctypes.c_int
     lib.pkv_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -250,6 +254,43 @@ def extend_attention_fwd(q_extend: torch.Tensor, k_extend: torch.Tensor, v_exten
         _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
     _check(rc)
     return o
+
+
+def store_kv_cache(k_extend: torch.Tensor, v_extend: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                   out_cache_loc: torch.Tensor) -> None:
+    """Store the new tokens' K/V rows into the pool at out_cache_loc (int64)."""
+    _want(out_cache_loc, "out_cache_loc", torch.int64)
+    # the descriptor of the call, with the new tokens' K standing in for q / o (not read)
+    desc = make_desc(k_extend, k_extend, v_extend, k_extend, k_pool, v_pool, 1, 0)
+    desc.total_q_tokens = out_cache_loc.numel()
+    _check(library().store_kv_cache(_ptr(k_extend), _ptr(v_extend), _ptr(k_pool), _ptr(v_pool),
+                                    _ptr(out_cache_loc), ctypes.byref(desc), _stream(k_pool.device)))
+
+
+def gather_kv_indices(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor, kv_lens: torch.Tensor,
+                      kv_start_idx: Optional[torch.Tensor] = None, capacity: Optional[int] = None,
+                      out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Prefix indices of a batch from the request-to-token table: (kv_indptr int32, kv_indices int64).
+    capacity defaults to the sum of kv_lens (read from the device, a host sync)."""
+    _want(req_to_token, "req_to_token", torch.int32)
+    _want(req_pool_indices, "req_pool_indices", torch.int64)
+    _want(kv_lens, "kv_lens", torch.int32)
+    if kv_start_idx is not None:
+        _want(kv_start_idx, "kv_start_idx", torch.int32)
+    if req_to_token.dim() != 2 or req_to_token.stride(1) != 1:
+        raise ValueError("req_to_token must be 2-D with contiguous rows")
+    bs = kv_lens.numel()
+    dev = req_to_token.device
+    if capacity is None:
+        capacity = int(kv_lens.sum().item()) if bs else 0
+    if out is None:
+        out = (torch.empty(bs + 1, dtype=torch.int32, device=dev),
+               torch.empty(max(capacity, 1), dtype=torch.int64, device=dev))
+    indptr, indices = out
+    _check(library().gather_kv_indices(_ptr(req_to_token), req_to_token.stride(0), _ptr(req_pool_indices),
+                                       _ptr(kv_lens), _ptr(kv_start_idx) if kv_start_idx is not None else None,
+                                       bs, _ptr(indptr), _ptr(indices), capacity, _stream(dev)))
+    return indptr, indices[:capacity]
 
 
 def extend_attention_fwd_unified(q_extend: torch.Tensor, o: torch.Tensor, k_pool: torch.Tensor,

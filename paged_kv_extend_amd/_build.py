@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["api.cpp", "index_build.hip", "plan.hip", "attention.hip", "attention_dl.hip", "attention_r64.hip"]
+SOURCES = ["api.cpp", "index_build.hip", "kv_cache.hip", "plan.hip", "attention.hip", "attention_dl.hip",
+           "attention_r64.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          # no packed fp32 instructions from the compiler

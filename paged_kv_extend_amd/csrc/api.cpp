@@ -288,6 +288,70 @@ int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* pre
   return ok();
 }
 
+int store_kv_cache(const void* k_extend, const void* v_extend, void* k_pool, void* v_pool,
+                   const int64_t* out_cache_loc, const pkv_attn_desc_t* desc, void* stream) {
+  pkv::Tiling t;
+  int rc = check_desc(desc, &t);
+  if (rc != PKV_OK) return rc;
+  const pkv_attn_desc_t& d = *desc;
+  if (d.total_q_tokens == 0) return ok();
+  if (!k_extend || !v_extend || !k_pool || !v_pool || !out_cache_loc)
+    return fail(PKV_ERR_INVALID, "k_extend / v_extend / k_pool / v_pool / out_cache_loc is NULL");
+  if (d.pool_slots <= 0) return fail(PKV_ERR_INVALID, "pool_slots is %lld", (long long)d.pool_slots);
+  const void* ptrs[] = {k_extend, v_extend, k_pool, v_pool};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(PKV_ERR_UNSUPPORTED, "tensor base pointers must be 16-byte aligned");
+  const int64_t e = d.dtype == PKV_BF16 ? 2 : 4;
+  const bool vk = v_inside_k(d, k_extend, v_extend, k_pool, v_pool);
+  pkv::StoreArgs a;
+  a.k_ext = static_cast<const char*>(k_extend);
+  a.v_ext = static_cast<const char*>(v_extend);
+  a.k_pool = static_cast<char*>(k_pool);
+  a.v_pool = static_cast<char*>(v_pool);
+  a.loc = out_cache_loc;
+  a.ke_st = d.ke_stride_tok * e;
+  a.ke_sh = d.ke_stride_head * e;
+  a.ve_st = d.ve_stride_tok * e;
+  a.ve_sh = d.ve_stride_head * e;
+  a.kp_ss = d.kp_stride_slot * e;
+  a.kp_sh = d.kp_stride_head * e;
+  a.vp_ss = d.vp_stride_slot * e;
+  a.vp_sh = d.vp_stride_head * e;
+  a.ck = (uint32_t)(d.lq * e / 16);
+  a.cv = vk ? 0u : (uint32_t)(d.lv * e / 16);  // V inside K: its bytes travel with the K row
+  const int64_t rows = d.total_q_tokens * d.num_kv_heads;
+  if (rows * (int64_t)(a.ck + a.cv) >= (1ll << 31)) return fail(PKV_ERR_UNSUPPORTED, "too many rows to store");
+  a.rows = (uint32_t)rows;
+  a.hkv = (uint32_t)d.num_kv_heads;
+  hipError_t he = pkv::launch_store_kv(a, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(PKV_ERR_HIP, "store launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+int gather_kv_indices(const int32_t* req_to_token, int64_t req_to_token_stride, const int64_t* req_pool_indices,
+                      const int32_t* kv_lens, const int32_t* kv_start_idx, int32_t bs, int32_t* kv_indptr,
+                      int64_t* kv_indices, int64_t capacity, void* stream) {
+  if (bs < 0 || req_to_token_stride < 0 || capacity < 0) return fail(PKV_ERR_INVALID, "negative size");
+  if (!kv_indptr) return fail(PKV_ERR_INVALID, "kv_indptr is NULL");
+  if (bs > 0 && (!req_to_token || !req_pool_indices || !kv_lens))
+    return fail(PKV_ERR_INVALID, "req_to_token / req_pool_indices / kv_lens is NULL");
+  if (capacity > 0 && !kv_indices) return fail(PKV_ERR_INVALID, "kv_indices is NULL");
+  if (capacity >= (1ll << 31)) return fail(PKV_ERR_UNSUPPORTED, "more than 2^31 - 1 indices");
+  pkv::GatherArgs a;
+  a.req_to_token = req_to_token;
+  a.stride = req_to_token_stride;
+  a.req_pool_indices = req_pool_indices;
+  a.kv_lens = kv_lens;
+  a.kv_start_idx = kv_start_idx;
+  a.bs = bs;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.capacity = capacity;
+  hipError_t he = pkv::launch_gather_indices(a, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return fail(PKV_ERR_HIP, "gather launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
 int extend_attention_prefer_kernel(const char* name) {
   if (!name) return fail(PKV_ERR_INVALID, "kernel name is NULL");
   static const struct {

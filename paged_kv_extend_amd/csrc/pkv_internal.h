@@ -145,6 +145,33 @@ bool attn_tiling(int dtype, int lq, int lv, Tiling* t);
 hipError_t launch_attention(int dtype, int lq, int lv, const AttnArgs& a, int64_t grid,
                             hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+// KV-cache store: byte strides; ck / cv = 16-byte chunks of a K / V row
+// (cv = 0 when V lies inside K and is stored with it); rows = tokens * hkv.
+struct StoreArgs {
+  const char* k_ext;
+  const char* v_ext;
+  char* k_pool;
+  char* v_pool;
+  const int64_t* loc;  // [tokens] pool slot of each new token
+  int64_t ke_st, ke_sh, ve_st, ve_sh, kp_ss, kp_sh, vp_ss, vp_sh;
+  uint32_t rows, hkv, ck, cv;
+};
+hipError_t launch_store_kv(const StoreArgs& a, hipStream_t s);
+
+// Request-to-token index gather.
+struct GatherArgs {
+  const int32_t* req_to_token;      // [rows, stride]
+  int64_t stride;
+  const int64_t* req_pool_indices;  // [bs]
+  const int32_t* kv_lens;           // [bs]
+  const int32_t* kv_start_idx;      // [bs] or NULL
+  int32_t bs;
+  int32_t* kv_indptr;               // [bs + 1] out
+  int64_t* kv_indices;              // [capacity] out
+  int64_t capacity;
+};
+hipError_t launch_gather_indices(const GatherArgs& a, hipStream_t s);
+
 hipError_t launch_index_build(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
                               const int32_t* extend_start_loc, const int32_t* extend_seq_lens,
                               const int64_t* extend_kv_indices, int32_t bs,

@@ -167,3 +167,17 @@ def test_unified_kernel_name_uses_the_pool_only():
                o_stride_head=512, ve_stride_tok=0, ve_stride_head=0, vp_stride_slot=576, vp_stride_head=576)
     assert kernel_name(mla, None, None, 12288, 12288) == "attn_dl_kernel"
     assert kernel_name(mla, None, None, 12288, 16384) == "attn_kernel"
+
+
+def test_store_and_gather_argument_errors_without_device():
+    lib = pkv.library()
+    p = 4096
+    d = desc()
+    assert lib.store_kv_cache(p, p, p, None, p, ctypes.byref(d), None) == -1
+    assert lib.store_kv_cache(p, p, p, p, p, ctypes.byref(desc(total_q_tokens=0)), None) == 0
+    assert lib.store_kv_cache(p + 4, p, p, p, p, ctypes.byref(d), None) == -2
+    assert lib.store_kv_cache(p, p, p, p, p, ctypes.byref(desc(lq=80, lv=80)), None) == -2
+    assert lib.gather_kv_indices(p, 64, p, p, None, -1, p, p, 10, None) == -1
+    assert lib.gather_kv_indices(p, 64, p, p, None, 3, None, p, 10, None) == -1
+    assert lib.gather_kv_indices(None, 64, p, p, None, 3, p, p, 10, None) == -1
+    assert lib.gather_kv_indices(p, 64, p, p, None, 3, p, None, 10, None) == -1
