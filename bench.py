@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel", default="auto", help="attention kernel preference: auto, r64, dl, attn")
+    ap.add_argument("--op", default="attention", choices=["attention", "store", "gather"],
+                    help="attention: the hot path; store / gather: the KV-cache store of the new tokens or the "
+                         "request-to-token index gather of the same batch, reported in GB/s against HBM")
     ap.add_argument("--path", default="two-part", choices=["two-part", "unified"],
                     help="two-part: prefix through kv_indices, new tokens from k/v_extend (the index build "
                          "runs beside it); unified: attention reads every key through the index build's output")
@@ -110,6 +113,8 @@ def main():
     pkv.extend_attention_prefer_kernel(args.kernel)
     dev = torch.device("cuda", 0)
     w = wl.get(args.workload)
+    if args.op != "attention":
+        return bench_copy_op(args, w, dev, torch, pkv)
     flops = w.causal_flops()
     algo_bytes = w.algorithmic_bytes()
     copies = args.copies or max(1, min(16, int(np.ceil(512e6 / algo_bytes))))
@@ -191,6 +196,79 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_copy_op(args, w, dev, torch, pkv):
+    """KV-cache store or request-to-token gather of the workload's batch, timed over rotated input copies."""
+    c = w.cfg
+    esz = 2 if c.dtype == "bf16" else 4
+    sets = []
+    if args.op == "store":
+        import workloads as wl
+        row_bytes = c.lq * esz + (0 if c.v_aliases_k else c.lv * esz)
+        nbytes = 2 * w.total_q * c.hkv * row_bytes  # each new row read once and written once
+        copies = args.copies or max(1, min(16, int(np.ceil(512e6 / nbytes))))
+        for _ in range(copies):
+            d = wl.to_torch(w, dev)
+            d["loc"] = d["extend_kv_indices"]
+            sets.append(d)
+
+        def step(i):
+            d = sets[i % copies]
+            pkv.store_kv_cache(d["k_ext"], d["v_ext"], d["k_pool"], d["v_pool"], d["loc"])
+        metric, what = "KV-cache store GB/s (new tokens' K/V into the pool), 1 GPU", "store_kv_kernel"
+    else:
+        stride = int(max(1, w.prefix_lens.max()))
+        table = np.zeros((w.bs, stride), np.int32)
+        for b in range(w.bs):
+            p0, p1 = int(w.kv_indptr[b]), int(w.kv_indptr[b + 1])
+            table[b, :p1 - p0] = w.kv_indices[p0:p1]
+        nbytes = w.num_prefix * (4 + 8) + (w.bs + 1) * 4 + w.bs * (8 + 4)
+        copies = args.copies or max(1, min(16, int(np.ceil(64e6 / max(nbytes, 1)))))
+        for _ in range(copies):
+            sets.append(dict(table=torch.from_numpy(table).to(dev),
+                             rpi=torch.arange(w.bs, dtype=torch.int64, device=dev),
+                             lens=torch.from_numpy(w.prefix_lens.astype(np.int32)).to(dev),
+                             out=(torch.empty(w.bs + 1, dtype=torch.int32, device=dev),
+                                  torch.empty(max(w.num_prefix, 1), dtype=torch.int64, device=dev))))
+
+        def step(i):
+            d = sets[i % copies]
+            pkv.gather_kv_indices(d["table"], d["rpi"], d["lens"], capacity=w.num_prefix, out=d["out"])
+        metric, what = "request-to-token index gather GB/s, 1 GPU", "gather_indices_kernel"
+    # these kernels run for microseconds, less than the host needs to issue a
+    # call: one pass over the input copies is captured in a HIP graph and the
+    # replays are timed (the kernels record no memset, so they replay as run)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(args.warmup, 1)):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(copies):
+            step(i)
+    reps = max(1, -(-args.steps // copies))
+    graph.replay()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (reps * copies)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": metric, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "timing": "HIP graph of one pass over the input copies, replays timed",
+        "vs_baseline": None, "dtype": c.dtype if args.op == "store" else "int64", "data": "synthetic",
+        "config": {"workload": c.name, "op": args.op, "bytes_per_step": int(nbytes), "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "kernel": what, "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "traffic": None}}), flush=True)
     return 0
 
 
