@@ -55,10 +55,10 @@ def _load():
         lib.oracle_build_unified_kv_indices.argtypes = [P, P, P, P, P, i32, P, P, P]
         lib.oracle_build_unified_kv_indices.restype = ctypes.c_int
         lib.oracle_extend_attention.argtypes = (
-            [i32] + [P, i64, i64] * 5 + [i64, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32])
+            [i32] + [P, i64, i64] * 5 + [i64, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32, i32, P])
         lib.oracle_extend_attention.restype = ctypes.c_int
         lib.oracle_extend_attention_unified.argtypes = (
-            [i32] + [P, i64, i64] * 3 + [i64, P, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32])
+            [i32] + [P, i64, i64] * 3 + [i64, P, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32, i32, P])
         lib.oracle_extend_attention_unified.restype = ctypes.c_int
         lib.oracle_store_kv_cache.argtypes = [i32, i64, i32, i32, i32] + [P, i64, i64] * 4 + [i64, P]
         lib.oracle_store_kv_cache.restype = ctypes.c_int
@@ -103,9 +103,18 @@ def _strides(a: np.ndarray):
     return a.strides[0] // it, a.strides[1] // it
 
 
+def _sinks(sinks, hq):
+    if sinks is None:
+        return None
+    a = np.ascontiguousarray(sinks, np.float32)
+    assert a.shape == (hq,), a.shape
+    return a
+
+
 def extend_attention(q, k_ext, v_ext, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices,
-                     sm_scale=0.0, logit_cap=0.0, dtype="bf16", rows=None, num_threads=0):
-    """Exact (double) extend attention for the given extend-token rows.
+                     sm_scale=0.0, logit_cap=0.0, dtype="bf16", rows=None, num_threads=0, window=0, sinks=None):
+    """Exact (double) extend attention for the given extend-token rows
+    (window > 0: sliding window; sinks: float32 [Hq] sink logits or None).
 
     Arrays: bf16 tensors as uint16 bit patterns, fp32 tensors as float32,
     shapes [tokens|slots, heads, dim] with a contiguous last dim.  Returns
@@ -138,6 +147,8 @@ def extend_attention(q, k_ext, v_ext, k_pool, v_pool, qo_indptr, kv_indptr, kv_i
     args += [k_pool.shape[0], _ptr(qo), _ptr(kvp), _ptr(kvi), bs, hq, hkv, lq, lv,
              float(sm_scale), float(logit_cap),
              _ptr(rows_arr) if rows_arr is not None else None, n, _ptr(out), int(num_threads)]
+    sk = _sinks(sinks, hq)
+    args += [int(window), _ptr(sk) if sk is not None else None]
     rc = lib.oracle_extend_attention(*args)
     if rc != 0:
         raise ValueError(f"oracle attention failed: {rc}")
@@ -145,7 +156,8 @@ def extend_attention(q, k_ext, v_ext, k_pool, v_pool, qo_indptr, kv_indptr, kv_i
 
 
 def extend_attention_unified(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, prefix_lens,
-                             sm_scale=0.0, logit_cap=0.0, dtype="bf16", rows=None, num_threads=0):
+                             sm_scale=0.0, logit_cap=0.0, dtype="bf16", rows=None, num_threads=0, window=0,
+                             sinks=None):
     """Exact (double) unified one-stage extend attention: every key through
     kv_indices (the unified index array), prefix_lens[b] of them prefix keys.
     Same array conventions and return value as extend_attention."""
@@ -179,6 +191,8 @@ def extend_attention_unified(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices
     args += [k_pool.shape[0], _ptr(qo), _ptr(kvp), _ptr(kvi), _ptr(pl), bs, hq, hkv, lq, lv,
              float(sm_scale), float(logit_cap),
              _ptr(rows_arr) if rows_arr is not None else None, n, _ptr(out), int(num_threads)]
+    sk = _sinks(sinks, hq)
+    args += [int(window), _ptr(sk) if sk is not None else None]
     rc = lib.oracle_extend_attention_unified(*args)
     if rc != 0:
         raise ValueError(f"oracle unified attention failed: {rc}")
@@ -228,8 +242,8 @@ def gather_kv_indices(req_to_token, req_pool_indices, kv_lens, kv_start_idx=None
     return indptr, out[:int(indptr[-1])]
 
 
-def extend_attention_workload(w, rows=None, num_threads=0):
+def extend_attention_workload(w, rows=None, num_threads=0, window=0, sinks=None):
     """Convenience: run the oracle on a workloads.Workload-like object."""
     return extend_attention(w.q, w.k_ext, w.v_ext, w.k_pool, w.v_pool, w.qo_indptr,
                             w.kv_indptr, w.kv_indices, w.sm_scale, w.logit_cap,
-                            w.cfg.dtype, rows=rows, num_threads=num_threads)
+                            w.cfg.dtype, rows=rows, num_threads=num_threads, window=window, sinks=sinks)

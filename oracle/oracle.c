@@ -101,8 +101,12 @@ static int32_t owner_seq(const int32_t* qo_indptr, int32_t bs, int64_t t) {
  * qo_indptr[b] + j - P of k_ext / v_ext).  Query i sees key j iff j <= P + i:
  * the whole prefix, and the new tokens up to and including itself.
  *   s_j = scale * <q, K_j>; with a cap c > 0, s_j = c * tanh(s_j / c)
- *   out = sum_j exp(s_j - max s) V_j / sum_j exp(s_j - max s)
+ *   out = sum_j exp(s_j - max s) V_j / (sum_j exp(s_j - max s) + sink term)
  * scale = sm_scale, or 1/sqrt(lq) when sm_scale == 0.
+ * Options of _fwd_kernel_unified (extend_attention.py): a sliding window
+ * W > 0 also hides keys j < P + i - W (the query's absolute position may be
+ * at most W past the key's); sinks (NULL: none) add exp(sinks[h] - max s) to
+ * the denominator of query head h.
  */
 int oracle_extend_attention(int32_t dtype,
                             const void* q, int64_t q_st, int64_t q_sh,
@@ -116,7 +120,7 @@ int oracle_extend_attention(int32_t dtype,
                             int32_t bs, int32_t hq, int32_t hkv, int32_t lq, int32_t lv,
                             double sm_scale, double logit_cap,
                             const int64_t* rows, int64_t n_rows,
-                            double* out, int32_t num_threads) {
+                            double* out, int32_t num_threads, int32_t window, const float* sinks) {
   if (bs < 0 || hq <= 0 || hkv <= 0 || lq <= 0 || lv <= 0) return ORACLE_EINVAL;
   if (hq % hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_EINVAL;
   const int32_t group = hq / hkv;
@@ -162,10 +166,11 @@ int oracle_extend_attention(int32_t dtype,
         int64_t P = kv_indptr[b + 1] - kv_indptr[b];
         int32_t g = h / group;
         int64_t visible = P + i + 1;
+        int64_t first = (window > 0 && P + i - window > 0) ? P + i - window : 0;
 
         /* logits of the visible keys */
         double m = -INFINITY;
-        for (int64_t j = 0; j < visible; ++j) {
+        for (int64_t j = first; j < visible; ++j) {
           const void* kbase;
           int64_t koff;
           if (j < P) {
@@ -188,7 +193,7 @@ int oracle_extend_attention(int32_t dtype,
         /* softmax-weighted sum of the visible values */
         double den = 0.0;
         for (int32_t d = 0; d < lv; ++d) acc[d] = 0.0;
-        for (int64_t j = 0; j < visible; ++j) {
+        for (int64_t j = first; j < visible; ++j) {
           const void* vbase;
           int64_t voff;
           if (j < P) {
@@ -202,6 +207,7 @@ int oracle_extend_attention(int32_t dtype,
           den += wgt;
           for (int32_t d = 0; d < lv; ++d) acc[d] += wgt * load_elem(vbase, dtype, voff + d);
         }
+        if (sinks) den += exp((double)sinks[h] - m);
         for (int32_t d = 0; d < lv; ++d) o[d] = acc[d] / den;
       }
     }
@@ -221,8 +227,9 @@ int oracle_extend_attention(int32_t dtype,
  * j = 0 .. L-1 with L = kv_indptr[b+1] - kv_indptr[b]; key j is pool slot
  * kv_indices[kv_indptr[b] + j].  With P = prefix_lens[b], key j is visible to
  * query i iff j < P (a prefix key) or j - P <= i (a new token at or before the
- * query).  Scale, cap and softmax as in oracle_extend_attention.  A row with no
- * visible key gets NaN (the softmax denominator is zero).
+ * query).  Scale, cap, softmax, window and sinks as in
+ * oracle_extend_attention (the window also hides j < P + i - W).  A row
+ * with no visible key and no sink gets NaN (the denominator is zero).
  */
 int oracle_extend_attention_unified(int32_t dtype,
                                     const void* q, int64_t q_st, int64_t q_sh,
@@ -234,7 +241,7 @@ int oracle_extend_attention_unified(int32_t dtype,
                                     int32_t bs, int32_t hq, int32_t hkv, int32_t lq, int32_t lv,
                                     double sm_scale, double logit_cap,
                                     const int64_t* rows, int64_t n_rows,
-                                    double* out, int32_t num_threads) {
+                                    double* out, int32_t num_threads, int32_t window, const float* sinks) {
   if (bs < 0 || hq <= 0 || hkv <= 0 || lq <= 0 || lv <= 0) return ORACLE_EINVAL;
   if (hq % hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_EINVAL;
   const int32_t group = hq / hkv;
@@ -285,7 +292,7 @@ int oracle_extend_attention_unified(int32_t dtype,
         /* logits of the visible keys */
         double m = -INFINITY;
         for (int64_t j = 0; j < L; ++j) {
-          seen[j] = (j < P) || (j - P <= i);
+          seen[j] = ((j < P) || (j - P <= i)) && (window <= 0 || j >= P + i - window);
           if (!seen[j]) continue;
           int64_t koff = kv_indices[kv_indptr[b] + j] * kp_ss + (int64_t)g * kp_sh;
           double dot = 0.0;
@@ -307,6 +314,7 @@ int oracle_extend_attention_unified(int32_t dtype,
           den += wgt;
           for (int32_t d = 0; d < lv; ++d) acc[d] += wgt * load_elem(v_pool, dtype, voff + d);
         }
+        if (sinks) den += exp((double)sinks[h] - m);
         for (int32_t d = 0; d < lv; ++d) o[d] = den > 0.0 ? acc[d] / den : NAN;
       }
     }

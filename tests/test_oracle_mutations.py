@@ -25,8 +25,11 @@ MUTATIONS = {
                          "koff = (qo_indptr[b] + (j - P) + (j > P)) * ke_st"),
     "index_copy_shift": ("unified_kv_indices[u + p_len + o]", "unified_kv_indices[u + p_len + o - (o > 0)]"),
     "first_weight_bias": ("double wgt = exp(s[j] - m);", "double wgt = exp(s[j] - m) * (j == 0 ? 1.0001 : 1.0);"),
-    "unified_drops_diagonal": ("seen[j] = (j < P) || (j - P <= i);", "seen[j] = (j < P) || (j - P < i);"),
-    "unified_causal_prefix": ("seen[j] = (j < P) || (j - P <= i);", "seen[j] = (j - P <= i);"),
+    "unified_drops_diagonal": ("seen[j] = ((j < P) || (j - P <= i))", "seen[j] = ((j < P) || (j - P < i))"),
+    "unified_causal_prefix": ("seen[j] = ((j < P) || (j - P <= i))", "seen[j] = ((j - P <= i))"),
+    "window_one_key_short": ("? P + i - window : 0;", "? P + i - window + 1 : 0;"),
+    "unified_window_open_end": ("j >= P + i - window);", "j > P + i - window);"),
+    "sink_without_max": ("if (sinks) den += exp((double)sinks[h] - m);", "if (sinks) den += exp((double)sinks[h]);"),
     "store_k_rows_by_token": ("memcpy((char*)k_pool + (slot * kp_ss", "memcpy((char*)k_pool + (t * kp_ss"),
     "gather_ignores_start": ("int64_t start = kv_start_idx ? kv_start_idx[b] : 0;", "int64_t start = 0;"),
     "gather_indptr_skips_first": ("kv_indptr[b + 1] = kv_indptr[b] + kv_lens[b];",

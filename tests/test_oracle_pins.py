@@ -394,3 +394,104 @@ def test_store_then_unified_attention_is_library_attention(case):
     kp, vp = oracle.store_kv_cache(w.k_ext, w.v_ext, kp, vp, w.extend_kv_indices)
     got = _unified(w, *_unified_arrays(w), k_pool=kp, v_pool=vp)
     np.testing.assert_allclose(got, sdpa_reference(w), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- sliding window and sinks
+# (page extend_attention.py, _fwd_kernel_unified: SLIDING_WINDOW_SIZE hides keys more than W
+# positions before the query; HAS_SINK adds exp(sink - max) to the denominator)
+
+WINDOW_CASE = dict(dtype="bf16", prefix_lens=[30, 0, 9], extend_lens=[12, 20, 5], hq=4, hkv=2, lq=64, lv=64)
+BF16_NAN = 0x7FC0
+
+
+def test_window_wider_than_any_sequence_is_no_window():
+    w = wl.custom(**WINDOW_CASE)
+    assert np.array_equal(oracle.extend_attention_workload(w, window=10_000), oracle.extend_attention_workload(w))
+
+
+@pytest.mark.parametrize("window", [1, 3, 17])
+def test_window_ignores_every_key_before_it(window):
+    # for single rows: poisoning every key more than W positions before the
+    # query leaves the row unchanged (and would spoil it without the window)
+    w = wl.custom(**WINDOW_CASE)
+    for t in (0, 11, 12 + 19, 12 + 20 + 4):
+        b = int(np.searchsorted(w.qo_indptr, t, side="right") - 1)
+        i = t - int(w.qo_indptr[b])
+        P = int(w.kv_indptr[b + 1] - w.kv_indptr[b])
+        kp, vp, ke, ve = w.k_pool.copy(), w.v_pool.copy(), w.k_ext.copy(), w.v_ext.copy()
+        hidden = range(0, max(0, P + i - window))
+        for j in hidden:
+            if j < P:
+                s = w.kv_indices[w.kv_indptr[b] + j]
+                kp[s] = BF16_NAN
+                vp[s] = BF16_NAN
+            else:
+                ke[w.qo_indptr[b] + j - P] = BF16_NAN
+                ve[w.qo_indptr[b] + j - P] = BF16_NAN
+        base = oracle.extend_attention_workload(w, rows=[t], window=window)
+        got = oracle.extend_attention(w.q, ke, ve, kp, vp, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                      dtype="bf16", rows=[t], window=window)
+        assert np.array_equal(got, base), t
+        if len(hidden):
+            plain = oracle.extend_attention(w.q, ke, ve, kp, vp, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                            dtype="bf16", rows=[t])
+            assert np.isnan(plain).all()
+
+
+def _keys_f64(w, b, which):
+    """K or V rows of sequence b's keys in order (prefix then new tokens), float64 [P+E, Hkv, L]."""
+    pool, ext = (w.k_pool, w.k_ext) if which == "k" else (w.v_pool, w.v_ext)
+    p0, p1 = w.kv_indptr[b], w.kv_indptr[b + 1]
+    q0, q1 = w.qo_indptr[b], w.qo_indptr[b + 1]
+    return np.concatenate([wl.as_f32(pool[w.kv_indices[p0:p1]], w.cfg.dtype),
+                           wl.as_f32(ext[q0:q1], w.cfg.dtype)]).astype(np.float64)
+
+
+@pytest.mark.parametrize("window", [1, 4, 25])
+def test_zero_query_with_window_gives_window_mean(window):
+    w = wl.custom(**WINDOW_CASE)
+    w.q[:] = 0
+    got = oracle.extend_attention_workload(w, window=window)
+    g = w.cfg.hq // w.cfg.hkv
+    for t in range(w.total_q):
+        b = int(np.searchsorted(w.qo_indptr, t, side="right") - 1)
+        i = t - int(w.qo_indptr[b])
+        P = int(w.kv_indptr[b + 1] - w.kv_indptr[b])
+        v = _keys_f64(w, b, "v")[max(0, P + i - window):P + i + 1]
+        want = v.mean(axis=0).repeat(g, axis=0)  # [Hq, Lv]
+        np.testing.assert_allclose(got[t], want, atol=1e-12)
+
+
+def test_minus_infinite_sink_is_no_sink():
+    w = wl.custom(**WINDOW_CASE)
+    sinks = np.full(w.cfg.hq, -np.inf, np.float32)
+    assert np.array_equal(oracle.extend_attention_workload(w, sinks=sinks), oracle.extend_attention_workload(w))
+
+
+def test_sink_closed_form_with_zero_query():
+    # all logits 0: out = sum_j V_j / (n + e^sink)
+    w = wl.custom(**WINDOW_CASE)
+    w.q[:] = 0
+    sinks = np.array([-1.0, 0.0, 0.5, 3.0], np.float32)
+    got = oracle.extend_attention_workload(w, sinks=sinks)
+    g = w.cfg.hq // w.cfg.hkv
+    for t in range(w.total_q):
+        b = int(np.searchsorted(w.qo_indptr, t, side="right") - 1)
+        i = t - int(w.qo_indptr[b])
+        P = int(w.kv_indptr[b + 1] - w.kv_indptr[b])
+        v = _keys_f64(w, b, "v")[:P + i + 1]
+        n = P + i + 1
+        for h in range(w.cfg.hq):
+            want = v[:, h // g].sum(axis=0) / (n + math.exp(float(sinks[h])))
+            np.testing.assert_allclose(got[t, h], want, atol=1e-12)
+
+
+def test_unified_window_and_sinks_match_two_part():
+    w = wl.custom(**WINDOW_CASE)
+    sinks = np.array([0.3, -2.0, 1.0, 0.0], np.float32)
+    for window in (2, 9):
+        want = oracle.extend_attention_workload(w, window=window, sinks=sinks)
+        indptr, indices, plens = _unified_arrays(w)
+        got = oracle.extend_attention_unified(w.q, w.k_pool, w.v_pool, w.qo_indptr, indptr, indices, plens,
+                                              dtype="bf16", window=window, sinks=sinks)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
