@@ -148,6 +148,13 @@ typedef struct {
   int64_t ve_stride_tok, ve_stride_head;
   int64_t kp_stride_slot, kp_stride_head;
   int64_t vp_stride_slot, vp_stride_head;
+  /* Options of page "extend_attention.py", _fwd_kernel_unified (zero-initialise
+   * the struct to leave them off): */
+  int32_t sliding_window; /* W > 0: new token i also sees no key j < P_b + i - W */
+  int32_t pad0;
+  const float* sinks;     /* DEVICE float32[num_q_heads] sink logits, or NULL:
+                             exp(sinks[h] - max) joins the softmax denominator
+                             of query head h (logits after scale and cap) */
 } pkv_attn_desc_t;
 
 /*

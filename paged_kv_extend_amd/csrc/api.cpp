@@ -69,13 +69,19 @@ bool kernel_tiling(Kernel k, int dtype, int lq, int lv, bool v_in_k, pkv::Tiling
   }
 }
 
-Kernel pick_kernel(int dtype, int lq, int lv, bool v_in_k, pkv::Tiling* t) {
+// (options: a sliding window or sinks, which the 64-row kernel does not serve)
+Kernel pick_kernel(int dtype, int lq, int lv, bool v_in_k, pkv::Tiling* t, bool options = false) {
   const Kernel pref = static_cast<Kernel>(g_prefer.load(std::memory_order_relaxed));
-  if (pref != Kernel::kNone && kernel_tiling(pref, dtype, lq, lv, v_in_k, t)) return pref;
+  const auto serves = [&](Kernel k) {
+    return !(options && k == Kernel::kR64) && kernel_tiling(k, dtype, lq, lv, v_in_k, t);
+  };
+  if (pref != Kernel::kNone && serves(pref)) return pref;
   for (Kernel k : {Kernel::kDl, Kernel::kR64, Kernel::kAttn})
-    if (kernel_tiling(k, dtype, lq, lv, v_in_k, t)) return k;
+    if (serves(k)) return k;
   return Kernel::kNone;
 }
+
+bool has_options(const pkv_attn_desc_t& d) { return d.sliding_window > 0 || d.sinks != nullptr; }
 
 const char* kernel_symbol(Kernel k) {
   switch (k) {
@@ -87,13 +93,13 @@ const char* kernel_symbol(Kernel k) {
 }
 
 // Resident attention workgroups on the current device, cached per (device, variant).
-int resident_slots(int dtype, int lq, int lv, bool v_in_k) {
+int resident_slots(int dtype, int lq, int lv, bool v_in_k, bool options) {
   static std::mutex mu;
   static std::unordered_map<long long, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   pkv::Tiling t;
-  const Kernel k = pick_kernel(dtype, lq, lv, v_in_k, &t);
+  const Kernel k = pick_kernel(dtype, lq, lv, v_in_k, &t, options);
   const long long key = ((long long)dev << 36) | ((long long)k << 33) | ((long long)v_in_k << 32) |
                         ((long long)dtype << 24) | ((long long)lq << 12) | lv;
   std::lock_guard<std::mutex> lk(mu);
@@ -115,7 +121,7 @@ int resident_slots(int dtype, int lq, int lv, bool v_in_k) {
 
 // Row and key tiling of the kernel serving (dtype, lq, lv) with or without V inside K.
 bool tiling_for(const pkv_attn_desc_t& d, bool v_in_k, pkv::Tiling* t) {
-  return pick_kernel(d.dtype, d.lq, d.lv, v_in_k, t) != Kernel::kNone;
+  return pick_kernel(d.dtype, d.lq, d.lv, v_in_k, t, has_options(d)) != Kernel::kNone;
 }
 
 // Sizes derived from the descriptor; returns 0 and sets the error when invalid.
@@ -258,7 +264,7 @@ const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc, const void
   pkv::Tiling t;
   if (check_desc(desc, &t) != PKV_OK) return nullptr;
   const bool vk = v_inside_k(*desc, k_extend, v_extend, k_pool, v_pool);
-  return kernel_symbol(pick_kernel(desc->dtype, desc->lq, desc->lv, vk, &t));
+  return kernel_symbol(pick_kernel(desc->dtype, desc->lq, desc->lv, vk, &t, has_options(*desc)));
 }
 
 int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
@@ -429,12 +435,13 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   pa.qo_indptr = qo_indptr;
   pa.kv_indptr = kv_indptr;
   pa.prefix_lens = prefix_lens;
+  pa.window = d.sliding_window > 0 ? d.sliding_window : 0;
   pa.bs = d.bs;
   pa.num_kv_heads = d.num_kv_heads;
   pa.group = group;
   pa.bm = t.bm;
   pa.bn = t.bn;
-  pa.slots = resident_slots(d.dtype, d.lq, d.lv, vk);
+  pa.slots = resident_slots(d.dtype, d.lq, d.lv, vk, has_options(d));
   pa.min_chunk = kMinChunkTiles;
   pa.xcds = kXcds;
   pa.max_work = pb.max_work;
@@ -462,6 +469,8 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   a.kv_indptr = kv_indptr;
   a.kv_indices = kv_indices;
   a.prefix_lens = prefix_lens;
+  a.window = pa.window;
+  a.sinks = d.sinks;
   a.q_st = d.q_stride_tok;
   a.q_sh = d.q_stride_head;
   a.o_st = d.o_stride_tok;
@@ -489,7 +498,7 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   const auto ev = profile_slot();
   if (ev.first) (void)hipEventRecord(ev.first, s);
   pkv::Tiling td;
-  switch (pick_kernel(d.dtype, d.lq, d.lv, vk, &td)) {
+  switch (pick_kernel(d.dtype, d.lq, d.lv, vk, &td, has_options(d))) {
     case Kernel::kR64: e = pkv::launch_r64(d.lq, a, pb.max_work, s); break;
     case Kernel::kDl: e = pkv::launch_dl(d.lq, d.lv, vk, a, pb.max_work, s); break;
     default: e = pkv::launch_attention(d.dtype, d.lq, d.lv, a, pb.max_work, s); break;

@@ -136,12 +136,17 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   const bool valid = r < R;
   const int tok = valid ? r / G : 0;
   const int head = g * G + (valid ? r % G : 0);
+  const int W = a.window;
   const int lim = valid ? min(P + tok, sk.n_keys - 1) : -1;  // last visible key
+  const int lo = (W > 0 && valid) ? P + tok - W : kNoLowerKey;  // first visible key (sliding window)
   // the wave's token range (rows are token-major) and the workgroup's last visible key
   const int rw0 = it.t * BM + wv * 32;
   const bool wave_live = rw0 < R;
-  const int lim_lo_w = min(P + (wave_live ? rw0 / G : 0), sk.n_keys - 1);
-  const int lim_hi_w = min(P + (wave_live ? min(R - 1, rw0 + 31) / G : 0), sk.n_keys - 1);
+  const int tok_lo_w = wave_live ? rw0 / G : 0, tok_hi_w = wave_live ? min(R - 1, rw0 + 31) / G : 0;
+  const int lim_lo_w = min(P + tok_lo_w, sk.n_keys - 1);
+  const int lim_hi_w = min(P + tok_hi_w, sk.n_keys - 1);
+  const int lo_lo_w = W > 0 ? P + tok_lo_w - W : kNoLowerKey;
+  const int lo_hi_w = W > 0 ? P + tok_hi_w - W : kNoLowerKey;
   const int key_last = min(P + min(R - 1, it.t * BM + BM - 1) / G, sk.n_keys - 1);
 
   const gptr<T> kpool = (gptr<T>)a.k_pool;
@@ -282,8 +287,8 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
     if (kt + 2 < kt1) fetch_slot(kt + 2);
 
     const int j0 = kt * BN;
-    if (wave_live && j0 <= lim_hi_w) {
-      const bool need_mask = j0 + BN - 1 > lim_lo_w;
+    if (wave_live && j0 <= lim_hi_w && j0 + BN - 1 >= lo_lo_w) {
+      const bool need_mask = j0 + BN - 1 > lim_lo_w || j0 < lo_hi_w;
 
       // S^T = K Q^T for the tile's 32-key blocks
       f32x16 s[NKB];
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
-            s[kb][rr] = j <= lim ? s[kb][rr] : -INFINITY;
+            s[kb][rr] = (j <= lim && j >= lo) ? s[kb][rr] : -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -396,7 +401,8 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   const float l_tot = pair_sum(l_run);
   if (it.part < 0) {
     if (!valid) return;
-    const float inv = 1.0f / l_tot;
+    // a sink joins the denominator once, here or in the merge of split chunks
+    const float inv = 1.0f / (a.sinks ? l_tot + fast_exp2(a.sinks[head] * kLog2e - m_ref) : l_tot);
     T* orow = reinterpret_cast<T*>(a.o) + (int64_t)(q0 + tok) * a.o_st + (int64_t)head * a.o_sh;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

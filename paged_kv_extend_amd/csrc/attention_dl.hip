@@ -168,12 +168,17 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
 
   const int r = it.t * BM + rg * 32 + qi;
   const bool valid = r < R;
+  const int W = a.window;
   const int lim = valid ? min(P + r / G, sk.n_keys - 1) : -1;  // last visible key of this lane's row
+  const int lo = (W > 0 && valid) ? P + r / G - W : kNoLowerKey;  // first visible key (sliding window)
   const int rw0 = it.t * BM + rg * 32;
   const bool wave_live = rw0 < R;
-  // the wave's smallest and largest last visible key
-  const int lim_lo_w = min(P + (wave_live ? rw0 / G : 0), sk.n_keys - 1);
-  const int lim_hi_w = min(P + (wave_live ? min(R - 1, rw0 + 31) / G : 0), sk.n_keys - 1);
+  // the wave's smallest and largest last (lim) and first (lo) visible key
+  const int tok_lo_w = wave_live ? rw0 / G : 0, tok_hi_w = wave_live ? min(R - 1, rw0 + 31) / G : 0;
+  const int lim_lo_w = min(P + tok_lo_w, sk.n_keys - 1);
+  const int lim_hi_w = min(P + tok_hi_w, sk.n_keys - 1);
+  const int lo_lo_w = W > 0 ? P + tok_lo_w - W : kNoLowerKey;
+  const int lo_hi_w = W > 0 ? P + tok_hi_w - W : kNoLowerKey;
   const int key_last = min(P + min(R - 1, it.t * BM + BM - 1) / G, sk.n_keys - 1);
 
   const gptr<T> kpool = (gptr<T>)a.k_pool;
@@ -364,7 +369,9 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   }
 
   // ---- tile math
-  auto active = [&](int kt) __attribute__((always_inline)) { return wave_live && kt * BN <= lim_hi_w; };
+  auto active = [&](int kt) __attribute__((always_inline)) {
+    return wave_live && kt * BN <= lim_hi_w && kt * BN + BN - 1 >= lo_lo_w;
+  };
 
   // S^T = K Q^T over this wave's Q dims
   auto qk = [&](int kt, f32x16 (&s)[NKB]) __attribute__((always_inline)) {
@@ -428,7 +435,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   // max and lazy rescale; returns the value subtracted in the exponent
   auto softmax_head = [&](int kt, f32x16 (&s)[NKB]) __attribute__((always_inline)) -> float {
     const int j0 = kt * BN;
-    const bool need_mask = j0 + BN - 1 > lim_lo_w;
+    const bool need_mask = j0 + BN - 1 > lim_lo_w || j0 < lo_hi_w;
     if constexpr (CAP) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -444,7 +451,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
-          s[kb][rr] = j <= lim ? s[kb][rr] : -INFINITY;
+          s[kb][rr] = (j <= lim && j >= lo) ? s[kb][rr] : -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -576,7 +583,8 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   const float l_tot = pair_sum(l_run);
   if (it.part < 0) {
     if (!valid) return;
-    const float inv = 1.0f / l_tot;
+    // a sink joins the denominator once, here or in the merge of split chunks
+    const float inv = 1.0f / (a.sinks ? l_tot + fast_exp2(a.sinks[g * G + r % G] * kLog2e - m_ref) : l_tot);
     T* orow = reinterpret_cast<T*>(a.o) + (int64_t)(q0 + r / G) * a.o_st + (int64_t)(g * G + r % G) * a.o_sh;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

@@ -38,8 +38,9 @@ __device__ void merge_tile(const AttnArgs& a, const MergeItem& mi, int bm, int t
       o.z += v.z * w;
       o.w += v.w * w;
     }
-    const float inv = 1.0f / L;
     const int tok = r / G, head = mi.g * G + r % G;
+    if (a.sinks) L += fast_exp2(a.sinks[head] * kLog2e - M);
+    const float inv = 1.0f / L;
     const int64_t off = (int64_t)(q0 + tok) * a.o_st + (int64_t)head * a.o_sh + d;
     if constexpr (F32) {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + off) =

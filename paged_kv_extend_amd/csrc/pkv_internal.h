@@ -76,6 +76,8 @@ struct AttnArgs {
   // k_ext / v_ext rows).  Else unified call: kv_indices hold every key and
   // prefix_lens[b] of sequence b's keys are prefix keys.
   const int32_t* prefix_lens;
+  int32_t window;       // > 0: sliding window (keys j < P + i - window hidden)
+  const float* sinks;   // [num_q_heads] sink logits (natural units), or NULL
   int64_t q_st, q_sh, o_st, o_sh, ke_st, ke_sh, ve_st, ve_sh, kp_ss, kp_sh, vp_ss, vp_sh;
   int32_t group;     // query heads per KV head
   int32_t use_cap;   // soft-cap enabled
@@ -95,6 +97,7 @@ struct PlanArgs {
   const int32_t* qo_indptr;
   const int32_t* kv_indptr;
   const int32_t* prefix_lens;  // as in AttnArgs
+  int32_t window;              // as in AttnArgs
   int32_t bs, num_kv_heads, group, bm, bn;
   int32_t slots;          // workgroups resident at once on the device
   int32_t min_chunk;      // never split below this many KV tiles
@@ -116,6 +119,9 @@ struct PlanArgs {
 //    are never visible, so n_idx = n_keys = min(span, P + E), which also keeps
 //    every index read inside the sequence's own span.
 // A query at new-token position i sees key j iff j < n_keys and j <= P + i.
+// "no sliding window": a first visible key below every key
+constexpr int kNoLowerKey = -(1 << 30);
+
 struct SeqKeys {
   int q0, E;   // first new-token row, new tokens
   int kvs, P;  // first index of the sequence, prefix keys

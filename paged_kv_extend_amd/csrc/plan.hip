@@ -176,7 +176,9 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     decode(n0, b, g, t);
     for (int n = n0; n < n1; ++n) {
       const int row_hi = min((t + 1) * BM, seq_e[b] * G) - 1;
-      const int cost = ceil_div(seq_p[b] + row_hi / G + 1, BN);
+      // tiles from the first key any row of the item sees (sliding window) to its last
+      const int first = a.window > 0 ? max(0, seq_p[b] + (t * BM) / G - a.window) / BN : 0;
+      const int cost = ceil_div(seq_p[b] + row_hi / G + 1, BN) - first;
       cost_of[n] = cost;
       my_total += cost;
       // next item: next tile, next head, or next sequence
@@ -326,6 +328,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     for (int n = n0; n < n1; ++n) {
       const int c = cost_of[n], k = pieces(c);
       const int pbase = (int)((uint32_t)pm[n] >> 16), midx = pm[n] & 0xFFFF;
+      const int first = a.window > 0 ? max(0, seq_p[b] + (itt * BM) / G - a.window) / BN : 0;
       for (int s = 0; s < k; ++s) {
         int k0, k1;
         chunk_range(c, s, k, k0, k1);
@@ -336,8 +339,8 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
         w.b = b;
         w.g = ig;
         w.t = itt;
-        w.kt_begin = k0;
-        w.kt_end = k1;
+        w.kt_begin = first + k0;
+        w.kt_end = first + k1;
         w.part = k > 1 ? pbase + s : -1;
         w.merge = k > 1 ? midx : -1;
         w.pad0 = 0;
