@@ -55,10 +55,10 @@ def _load():
         lib.oracle_build_unified_kv_indices.argtypes = [P, P, P, P, P, i32, P, P, P]
         lib.oracle_build_unified_kv_indices.restype = ctypes.c_int
         lib.oracle_extend_attention.argtypes = (
-            [i32] + [P, i64, i64] * 5 + [i64, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32, i32, P])
+            [i32] + [P, i64, i64] * 5 + [i64, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32, i32, P, P, P])
         lib.oracle_extend_attention.restype = ctypes.c_int
         lib.oracle_extend_attention_unified.argtypes = (
-            [i32] + [P, i64, i64] * 3 + [i64, P, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32, i32, P])
+            [i32] + [P, i64, i64] * 3 + [i64, P, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32, i32, P, P, P])
         lib.oracle_extend_attention_unified.restype = ctypes.c_int
         lib.oracle_store_kv_cache.argtypes = [i32, i64, i32, i32, i32] + [P, i64, i64] * 4 + [i64, P]
         lib.oracle_store_kv_cache.restype = ctypes.c_int
@@ -111,10 +111,21 @@ def _sinks(sinks, hq):
     return a
 
 
+def _mask(custom_mask, mask_indptr):
+    if custom_mask is None:
+        return None, None
+    m = np.ascontiguousarray(custom_mask, np.uint8)
+    mi = np.ascontiguousarray(mask_indptr, np.int64)
+    return (m if m.size else np.zeros(1, np.uint8)), mi
+
+
 def extend_attention(q, k_ext, v_ext, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices,
-                     sm_scale=0.0, logit_cap=0.0, dtype="bf16", rows=None, num_threads=0, window=0, sinks=None):
+                     sm_scale=0.0, logit_cap=0.0, dtype="bf16", rows=None, num_threads=0, window=0, sinks=None,
+                     custom_mask=None, mask_indptr=None):
     """Exact (double) extend attention for the given extend-token rows
-    (window > 0: sliding window; sinks: float32 [Hq] sink logits or None).
+    (window > 0: sliding window; sinks: float32 [Hq] sink logits or None;
+    custom_mask: uint8 bytes, sequence b's [E_b, P_b + E_b] matrix at
+    mask_indptr[b], replacing the causal rule).
 
     Arrays: bf16 tensors as uint16 bit patterns, fp32 tensors as float32,
     shapes [tokens|slots, heads, dim] with a contiguous last dim.  Returns
@@ -148,7 +159,9 @@ def extend_attention(q, k_ext, v_ext, k_pool, v_pool, qo_indptr, kv_indptr, kv_i
              float(sm_scale), float(logit_cap),
              _ptr(rows_arr) if rows_arr is not None else None, n, _ptr(out), int(num_threads)]
     sk = _sinks(sinks, hq)
-    args += [int(window), _ptr(sk) if sk is not None else None]
+    cm, mi = _mask(custom_mask, mask_indptr)
+    args += [int(window), _ptr(sk) if sk is not None else None, _ptr(cm) if cm is not None else None,
+             _ptr(mi) if mi is not None else None]
     rc = lib.oracle_extend_attention(*args)
     if rc != 0:
         raise ValueError(f"oracle attention failed: {rc}")
@@ -157,7 +170,7 @@ def extend_attention(q, k_ext, v_ext, k_pool, v_pool, qo_indptr, kv_indptr, kv_i
 
 def extend_attention_unified(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, prefix_lens,
                              sm_scale=0.0, logit_cap=0.0, dtype="bf16", rows=None, num_threads=0, window=0,
-                             sinks=None):
+                             sinks=None, custom_mask=None, mask_indptr=None):
     """Exact (double) unified one-stage extend attention: every key through
     kv_indices (the unified index array), prefix_lens[b] of them prefix keys.
     Same array conventions and return value as extend_attention."""
@@ -192,7 +205,9 @@ def extend_attention_unified(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices
              float(sm_scale), float(logit_cap),
              _ptr(rows_arr) if rows_arr is not None else None, n, _ptr(out), int(num_threads)]
     sk = _sinks(sinks, hq)
-    args += [int(window), _ptr(sk) if sk is not None else None]
+    cm, mi = _mask(custom_mask, mask_indptr)
+    args += [int(window), _ptr(sk) if sk is not None else None, _ptr(cm) if cm is not None else None,
+             _ptr(mi) if mi is not None else None]
     rc = lib.oracle_extend_attention_unified(*args)
     if rc != 0:
         raise ValueError(f"oracle unified attention failed: {rc}")
@@ -242,8 +257,10 @@ def gather_kv_indices(req_to_token, req_pool_indices, kv_lens, kv_start_idx=None
     return indptr, out[:int(indptr[-1])]
 
 
-def extend_attention_workload(w, rows=None, num_threads=0, window=0, sinks=None):
+def extend_attention_workload(w, rows=None, num_threads=0, window=0, sinks=None, custom_mask=None,
+                              mask_indptr=None):
     """Convenience: run the oracle on a workloads.Workload-like object."""
     return extend_attention(w.q, w.k_ext, w.v_ext, w.k_pool, w.v_pool, w.qo_indptr,
                             w.kv_indptr, w.kv_indices, w.sm_scale, w.logit_cap,
-                            w.cfg.dtype, rows=rows, num_threads=num_threads, window=window, sinks=sinks)
+                            w.cfg.dtype, rows=rows, num_threads=num_threads, window=window, sinks=sinks,
+                            custom_mask=custom_mask, mask_indptr=mask_indptr)

@@ -106,7 +106,9 @@ static int32_t owner_seq(const int32_t* qo_indptr, int32_t bs, int64_t t) {
  * Options of _fwd_kernel_unified (extend_attention.py): a sliding window
  * W > 0 also hides keys j < P + i - W (the query's absolute position may be
  * at most W past the key's); sinks (NULL: none) add exp(sinks[h] - max s) to
- * the denominator of query head h.
+ * the denominator of query head h; a custom mask (NULL: none) replaces the
+ * causal rule: with L = P + E keys, query i sees key j < L iff
+ * custom_mask[mask_indptr[b] + i * L + j] != 0 (a byte matrix per sequence).
  */
 int oracle_extend_attention(int32_t dtype,
                             const void* q, int64_t q_st, int64_t q_sh,
@@ -120,7 +122,8 @@ int oracle_extend_attention(int32_t dtype,
                             int32_t bs, int32_t hq, int32_t hkv, int32_t lq, int32_t lv,
                             double sm_scale, double logit_cap,
                             const int64_t* rows, int64_t n_rows,
-                            double* out, int32_t num_threads, int32_t window, const float* sinks) {
+                            double* out, int32_t num_threads, int32_t window, const float* sinks,
+                            const uint8_t* custom_mask, const int64_t* mask_indptr) {
   if (bs < 0 || hq <= 0 || hkv <= 0 || lq <= 0 || lv <= 0) return ORACLE_EINVAL;
   if (hq % hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_EINVAL;
   const int32_t group = hq / hkv;
@@ -145,8 +148,9 @@ int oracle_extend_attention(int32_t dtype,
 #pragma omp parallel
   {
     double* s = (double*)malloc(sizeof(double) * (size_t)max_keys);
+    char* vis = (char*)malloc((size_t)max_keys);
     double* acc = (double*)malloc(sizeof(double) * (size_t)lv);
-    if (!s || !acc) {
+    if (!s || !vis || !acc) {
 #pragma omp atomic write
       status = ORACLE_ENOMEM;
     } else {
@@ -165,12 +169,17 @@ int oracle_extend_attention(int32_t dtype,
         int64_t i = t - qo_indptr[b];
         int64_t P = kv_indptr[b + 1] - kv_indptr[b];
         int32_t g = h / group;
-        int64_t visible = P + i + 1;
+        int64_t E = qo_indptr[b + 1] - qo_indptr[b];
+        /* visible keys: causal (j <= P + i) or the custom mask, then the window */
+        int64_t visible = custom_mask ? P + E : P + i + 1;
         int64_t first = (window > 0 && P + i - window > 0) ? P + i - window : 0;
+        for (int64_t j = first; j < visible; ++j)
+          vis[j] = custom_mask ? custom_mask[mask_indptr[b] + i * (P + E) + j] != 0 : 1;
 
         /* logits of the visible keys */
         double m = -INFINITY;
         for (int64_t j = first; j < visible; ++j) {
+          if (!vis[j]) continue;
           const void* kbase;
           int64_t koff;
           if (j < P) {
@@ -194,6 +203,7 @@ int oracle_extend_attention(int32_t dtype,
         double den = 0.0;
         for (int32_t d = 0; d < lv; ++d) acc[d] = 0.0;
         for (int64_t j = first; j < visible; ++j) {
+          if (!vis[j]) continue;
           const void* vbase;
           int64_t voff;
           if (j < P) {
@@ -208,10 +218,11 @@ int oracle_extend_attention(int32_t dtype,
           for (int32_t d = 0; d < lv; ++d) acc[d] += wgt * load_elem(vbase, dtype, voff + d);
         }
         if (sinks) den += exp((double)sinks[h] - m);
-        for (int32_t d = 0; d < lv; ++d) o[d] = acc[d] / den;
+        for (int32_t d = 0; d < lv; ++d) o[d] = den > 0.0 ? acc[d] / den : NAN;
       }
     }
     free(s);
+    free(vis);
     free(acc);
   }
   return status;
@@ -228,8 +239,10 @@ int oracle_extend_attention(int32_t dtype,
  * kv_indices[kv_indptr[b] + j].  With P = prefix_lens[b], key j is visible to
  * query i iff j < P (a prefix key) or j - P <= i (a new token at or before the
  * query).  Scale, cap, softmax, window and sinks as in
- * oracle_extend_attention (the window also hides j < P + i - W).  A row
- * with no visible key and no sink gets NaN (the denominator is zero).
+ * oracle_extend_attention (the window also hides j < P + i - W); a custom
+ * mask replaces the causal rule: key j < L is seen iff
+ * custom_mask[mask_indptr[b] + i * L + j] != 0.  A row with no visible key
+ * and no sink gets NaN (the denominator is zero).
  */
 int oracle_extend_attention_unified(int32_t dtype,
                                     const void* q, int64_t q_st, int64_t q_sh,
@@ -241,7 +254,8 @@ int oracle_extend_attention_unified(int32_t dtype,
                                     int32_t bs, int32_t hq, int32_t hkv, int32_t lq, int32_t lv,
                                     double sm_scale, double logit_cap,
                                     const int64_t* rows, int64_t n_rows,
-                                    double* out, int32_t num_threads, int32_t window, const float* sinks) {
+                                    double* out, int32_t num_threads, int32_t window, const float* sinks,
+                                    const uint8_t* custom_mask, const int64_t* mask_indptr) {
   if (bs < 0 || hq <= 0 || hkv <= 0 || lq <= 0 || lv <= 0) return ORACLE_EINVAL;
   if (hq % hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_EINVAL;
   const int32_t group = hq / hkv;
@@ -292,7 +306,8 @@ int oracle_extend_attention_unified(int32_t dtype,
         /* logits of the visible keys */
         double m = -INFINITY;
         for (int64_t j = 0; j < L; ++j) {
-          seen[j] = ((j < P) || (j - P <= i)) && (window <= 0 || j >= P + i - window);
+          seen[j] = (custom_mask ? custom_mask[mask_indptr[b] + i * L + j] != 0 : ((j < P) || (j - P <= i))) &&
+                    (window <= 0 || j >= P + i - window);
           if (!seen[j]) continue;
           int64_t koff = kv_indices[kv_indptr[b] + j] * kp_ss + (int64_t)g * kp_sh;
           double dot = 0.0;

@@ -15,9 +15,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTATIONS = {
-    "mask_drops_diagonal": ("int64_t visible = P + i + 1;", "int64_t visible = P + i;"),
-    "mask_sees_next_token": ("int64_t visible = P + i + 1;",
-                             "int64_t visible = P + i + 1 + (i + 1 < (qo_indptr[b + 1] - qo_indptr[b]));"),
+    "mask_drops_diagonal": ("? P + E : P + i + 1;", "? P + E : P + i;"),
+    "mask_sees_next_token": ("? P + E : P + i + 1;", "? P + E : P + i + 1 + (i + 1 < E);"),
     "kv_head_modulo": ("int32_t g = h / group;", "int32_t g = h % hkv;"),
     "default_scale_from_lv": ("1.0 / sqrt((double)lq)", "1.0 / sqrt((double)lv)"),
     "cap_without_division": ("x = logit_cap * tanh(x / logit_cap);", "x = tanh(x) * logit_cap;"),
@@ -25,10 +24,13 @@ MUTATIONS = {
                          "koff = (qo_indptr[b] + (j - P) + (j > P)) * ke_st"),
     "index_copy_shift": ("unified_kv_indices[u + p_len + o]", "unified_kv_indices[u + p_len + o - (o > 0)]"),
     "first_weight_bias": ("double wgt = exp(s[j] - m);", "double wgt = exp(s[j] - m) * (j == 0 ? 1.0001 : 1.0);"),
-    "unified_drops_diagonal": ("seen[j] = ((j < P) || (j - P <= i))", "seen[j] = ((j < P) || (j - P < i))"),
-    "unified_causal_prefix": ("seen[j] = ((j < P) || (j - P <= i))", "seen[j] = ((j - P <= i))"),
+    "unified_drops_diagonal": ("((j < P) || (j - P <= i)))", "((j < P) || (j - P < i)))"),
+    "unified_causal_prefix": ("((j < P) || (j - P <= i)))", "((j - P <= i)))"),
     "window_one_key_short": ("? P + i - window : 0;", "? P + i - window + 1 : 0;"),
     "unified_window_open_end": ("j >= P + i - window);", "j > P + i - window);"),
+    "mask_row_stride_e": ("custom_mask[mask_indptr[b] + i * (P + E) + j]", "custom_mask[mask_indptr[b] + i * E + j]"),
+    "mask_ignored_past_diagonal": ("int64_t visible = custom_mask ? P + E : P + i + 1;",
+                                   "int64_t visible = P + i + 1;"),
     "sink_without_max": ("if (sinks) den += exp((double)sinks[h] - m);", "if (sinks) den += exp((double)sinks[h]);"),
     "store_k_rows_by_token": ("memcpy((char*)k_pool + (slot * kp_ss", "memcpy((char*)k_pool + (t * kp_ss"),
     "gather_ignores_start": ("int64_t start = kv_start_idx ? kv_start_idx[b] : 0;", "int64_t start = 0;"),

@@ -495,3 +495,78 @@ def test_unified_window_and_sinks_match_two_part():
         got = oracle.extend_attention_unified(w.q, w.k_pool, w.v_pool, w.qo_indptr, indptr, indices, plens,
                                               dtype="bf16", window=window, sinks=sinks)
         np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- custom mask
+# (page extend_attention.py, _fwd_kernel_unified with USE_CUSTOM_MASK: a byte per (query, key)
+# replaces the causal rule; sequence b's [E_b, L_b] matrix starts at mask_indptr[b])
+
+def _mask_arrays(w, rule):
+    """Byte matrices [E_b, P_b + E_b] from rule(b, i, j) -> bool, concatenated, and their offsets."""
+    parts, offs, off = [], [], 0
+    for b in range(w.bs):
+        E = int(w.qo_indptr[b + 1] - w.qo_indptr[b])
+        P = int(w.kv_indptr[b + 1] - w.kv_indptr[b])
+        m = np.array([[rule(b, i, j, P) for j in range(P + E)] for i in range(E)], np.uint8).reshape(E, P + E)
+        offs.append(off)
+        off += m.size
+        parts.append(m.ravel())
+    offs.append(off)
+    return (np.concatenate(parts) if parts else np.zeros(0, np.uint8)), np.array(offs, np.int64)
+
+
+MASK_CASE = dict(dtype="bf16", prefix_lens=[6, 0, 11], extend_lens=[5, 8, 3], hq=4, hkv=2, lq=32, lv=32)
+
+
+def test_causal_pattern_mask_is_no_mask():
+    w = wl.custom(**MASK_CASE)
+    m, mi = _mask_arrays(w, lambda b, i, j, P: j <= P + i)
+    assert np.array_equal(oracle.extend_attention_workload(w, custom_mask=m, mask_indptr=mi),
+                          oracle.extend_attention_workload(w))
+
+
+def test_all_ones_mask_is_full_attention():
+    w = wl.custom(**MASK_CASE)
+    m, mi = _mask_arrays(w, lambda b, i, j, P: True)
+    got = oracle.extend_attention_workload(w, custom_mask=m, mask_indptr=mi)
+    g = w.cfg.hq // w.cfg.hkv
+    outs = []
+    for b in range(w.bs):
+        q0, q1 = w.qo_indptr[b], w.qo_indptr[b + 1]
+        k = torch.from_numpy(_keys_f64(w, b, "k")).transpose(0, 1).repeat_interleave(g, 0)
+        v = torch.from_numpy(_keys_f64(w, b, "v")).transpose(0, 1).repeat_interleave(g, 0)
+        q = _f64(w.q[q0:q1], "bf16").transpose(0, 1)
+        outs.append(torch.nn.functional.scaled_dot_product_attention(q, k, v).transpose(0, 1))
+    np.testing.assert_allclose(got, torch.cat(outs).numpy(), atol=1e-12)
+
+
+def test_zero_query_with_random_mask_gives_masked_mean():
+    w = wl.custom(**MASK_CASE)
+    w.q[:] = 0
+    rng = np.random.default_rng(11)
+    bits = {}
+
+    def rule(b, i, j, P):  # a random pattern that keeps each row's own key
+        return j == P + i or bits.setdefault((b, i, j), rng.random() < 0.4)
+    m, mi = _mask_arrays(w, rule)
+    got = oracle.extend_attention_workload(w, custom_mask=m, mask_indptr=mi)
+    g = w.cfg.hq // w.cfg.hkv
+    for t in range(w.total_q):
+        b = int(np.searchsorted(w.qo_indptr, t, side="right") - 1)
+        i = t - int(w.qo_indptr[b])
+        P = int(w.kv_indptr[b + 1] - w.kv_indptr[b])
+        E = int(w.qo_indptr[b + 1] - w.qo_indptr[b])
+        row = m[mi[b] + i * (P + E):mi[b] + (i + 1) * (P + E)].astype(bool)
+        v = _keys_f64(w, b, "v")[row]
+        np.testing.assert_allclose(got[t], v.mean(axis=0).repeat(g, axis=0), atol=1e-12)
+
+
+def test_unified_custom_mask_matches_two_part():
+    w = wl.custom(**MASK_CASE)
+    rng = np.random.default_rng(12)
+    m, mi = _mask_arrays(w, lambda b, i, j, P: j == P + i or rng.random() < 0.5)
+    want = oracle.extend_attention_workload(w, custom_mask=m, mask_indptr=mi, window=4)
+    indptr, indices, plens = _unified_arrays(w)
+    got = oracle.extend_attention_unified(w.q, w.k_pool, w.v_pool, w.qo_indptr, indptr, indices, plens,
+                                          dtype="bf16", custom_mask=m, mask_indptr=mi, window=4)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
