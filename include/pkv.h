@@ -155,6 +155,12 @@ typedef struct {
   const float* sinks;     /* DEVICE float32[num_q_heads] sink logits, or NULL:
                              exp(sinks[h] - max) joins the softmax denominator
                              of query head h (logits after scale and cap) */
+  const uint8_t* custom_mask; /* DEVICE bytes, or NULL: replaces the causal rule.
+                             Sequence b's keys j < L_b (L_b = P_b + E_b for
+                             extend_attention_fwd, the index span for the
+                             unified entry) are seen by new token i iff
+                             custom_mask[mask_indptr[b] + i * L_b + j] != 0 */
+  const int64_t* mask_indptr; /* DEVICE int64[bs], with custom_mask */
 } pkv_attn_desc_t;
 
 /*

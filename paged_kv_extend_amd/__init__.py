@@ -40,7 +40,8 @@ class AttnDesc(ctypes.Structure):
                    "q_stride_tok", "q_stride_head", "o_stride_tok", "o_stride_head",
                    "ke_stride_tok", "ke_stride_head", "ve_stride_tok", "ve_stride_head",
                    "kp_stride_slot", "kp_stride_head", "vp_stride_slot", "vp_stride_head")] + \
-               [("sliding_window", ctypes.c_int32), ("pad0", ctypes.c_int32), ("sinks", ctypes.c_void_p)]
+               [("sliding_window", ctypes.c_int32), ("pad0", ctypes.c_int32), ("sinks", ctypes.c_void_p),
+                ("custom_mask", ctypes.c_void_p), ("mask_indptr", ctypes.c_void_p)]
 
 
 _lib = None
@@ -193,13 +194,21 @@ def make_desc(q_extend, k_extend, v_extend, o, k_pool, v_pool, bs: int,
     return d
 
 
-def _options(desc: AttnDesc, q_extend: torch.Tensor, sliding_window: int, sinks: Optional[torch.Tensor]) -> None:
+def _options(desc: AttnDesc, q_extend: torch.Tensor, sliding_window: int, sinks: Optional[torch.Tensor],
+             custom_mask: Optional[torch.Tensor] = None, mask_indptr: Optional[torch.Tensor] = None) -> None:
     desc.sliding_window = int(sliding_window) if sliding_window and sliding_window > 0 else 0
     if sinks is not None:
         _want(sinks, "sinks", torch.float32)
         if sinks.shape != (q_extend.shape[1],) or not sinks.is_contiguous():
             raise ValueError("sinks must be a contiguous float32 [num_q_heads] tensor")
         desc.sinks = sinks.data_ptr()
+    if custom_mask is not None:
+        _want(custom_mask, "custom_mask", torch.uint8)
+        if mask_indptr is None:
+            raise ValueError("custom_mask needs mask_indptr")
+        _want(mask_indptr, "mask_indptr", torch.int64)
+        desc.custom_mask = custom_mask.data_ptr()
+        desc.mask_indptr = mask_indptr.data_ptr()
 
 
 def extend_attention_workspace_size(desc: AttnDesc) -> int:
@@ -242,20 +251,22 @@ def extend_attention_fwd(q_extend: torch.Tensor, k_extend: torch.Tensor, v_exten
                          qo_indptr: torch.Tensor, kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
                          sm_scale: Optional[float] = None, logit_cap: float = 0.0,
                          workspace: Optional[torch.Tensor] = None, sliding_window: int = 0,
-                         sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         sinks: Optional[torch.Tensor] = None, custom_mask: Optional[torch.Tensor] = None,
+                         mask_indptr: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Extend attention into ``o`` (see include/pkv.h for the exact semantics).
 
     kv_indptr / kv_indices describe the cached prefix only; the new tokens'
     K/V rows are addressed by qo_indptr.  sm_scale None or 0 means 1/sqrt(lq).
-    sliding_window > 0 and sinks (float32 [num_q_heads] logits) are the
-    options of the unified kernel on the SGLang page.
+    sliding_window > 0, sinks (float32 [num_q_heads] logits) and custom_mask
+    (uint8 bytes, sequence b's [E_b, P_b + E_b] matrix at the int64
+    mask_indptr[b]) are the options of the unified kernel on the SGLang page.
     """
     _want(qo_indptr, "qo_indptr", torch.int32)
     _want(kv_indptr, "kv_indptr", torch.int32)
     _want(kv_indices, "kv_indices", torch.int64)
     bs = qo_indptr.numel() - 1
     desc = make_desc(q_extend, k_extend, v_extend, o, k_pool, v_pool, bs, kv_indices.numel())
-    _options(desc, q_extend, sliding_window, sinks)
+    _options(desc, q_extend, sliding_window, sinks, custom_mask, mask_indptr)
     dev = q_extend.device
     stream = _stream(dev)
     nbytes = extend_attention_workspace_size(desc)
@@ -312,7 +323,8 @@ def extend_attention_fwd_unified(q_extend: torch.Tensor, o: torch.Tensor, k_pool
                                  kv_indices: torch.Tensor, prefix_lens: torch.Tensor,
                                  sm_scale: Optional[float] = None, logit_cap: float = 0.0,
                                  workspace: Optional[torch.Tensor] = None, sliding_window: int = 0,
-                                 sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
+                                 sinks: Optional[torch.Tensor] = None, custom_mask: Optional[torch.Tensor] = None,
+                                 mask_indptr: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Unified one-stage extend attention into ``o``: every key through the
     unified kv_indptr / kv_indices (as build_unified_kv_indices returns them),
     prefix_lens[b] of sequence b's keys prefix keys (see include/pkv.h)."""
@@ -322,7 +334,7 @@ def extend_attention_fwd_unified(q_extend: torch.Tensor, o: torch.Tensor, k_pool
     _want(prefix_lens, "prefix_lens", torch.int32)
     bs = qo_indptr.numel() - 1
     desc = make_desc(q_extend, None, None, o, k_pool, v_pool, bs, kv_indices.numel())
-    _options(desc, q_extend, sliding_window, sinks)
+    _options(desc, q_extend, sliding_window, sinks, custom_mask, mask_indptr)
     dev = q_extend.device
     stream = _stream(dev)
     nbytes = extend_attention_workspace_size(desc)

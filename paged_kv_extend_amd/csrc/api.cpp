@@ -81,7 +81,9 @@ Kernel pick_kernel(int dtype, int lq, int lv, bool v_in_k, pkv::Tiling* t, bool 
   return Kernel::kNone;
 }
 
-bool has_options(const pkv_attn_desc_t& d) { return d.sliding_window > 0 || d.sinks != nullptr; }
+bool has_options(const pkv_attn_desc_t& d) {
+  return d.sliding_window > 0 || d.sinks != nullptr || d.custom_mask != nullptr;
+}
 
 const char* kernel_symbol(Kernel k) {
   switch (k) {
@@ -413,6 +415,7 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   if (unified) k_extend = v_extend = nullptr;  // not read
   if (d.num_prefix_indices > 0 && (!kv_indices || !k_pool || !v_pool))
     return fail(PKV_ERR_INVALID, "kv_indices / k_pool / v_pool is NULL with a non-empty index array");
+  if (d.custom_mask && !d.mask_indptr) return fail(PKV_ERR_INVALID, "custom_mask without mask_indptr");
   const void* ptrs[] = {q_extend, k_extend, v_extend, o, k_pool, v_pool};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(PKV_ERR_UNSUPPORTED, "tensor base pointers must be 16-byte aligned");
@@ -436,6 +439,7 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   pa.kv_indptr = kv_indptr;
   pa.prefix_lens = prefix_lens;
   pa.window = d.sliding_window > 0 ? d.sliding_window : 0;
+  pa.masked = d.custom_mask != nullptr;
   pa.bs = d.bs;
   pa.num_kv_heads = d.num_kv_heads;
   pa.group = group;
@@ -471,6 +475,8 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   a.prefix_lens = prefix_lens;
   a.window = pa.window;
   a.sinks = d.sinks;
+  a.custom_mask = d.custom_mask;
+  a.mask_indptr = d.mask_indptr;
   a.q_st = d.q_stride_tok;
   a.q_sh = d.q_stride_head;
   a.o_st = d.o_stride_tok;

@@ -105,7 +105,9 @@ struct Cfg {
   static_assert(BN % 32 == 0 && BN <= 64 && LQ % 16 == 0 && LV % 32 == 0, "tile shape");
 };
 
-template <bool F32, int LQ, int LV, int BN, bool CAP, int MINB>
+// OPT: a sliding window or a custom mask (which replaces the causal rule) may
+// be set -- a variant of its own
+template <bool F32, int LQ, int LV, int BN, bool CAP, bool OPT, int MINB>
 __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   using C = Cfg<F32, LQ, LV, BN>;
   using T = typename Elem<F32>::T;
@@ -127,7 +129,12 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   const int qi = lane & 31, hi = lane >> 5;
   const int G = a.group;
   const int b = it.b, g = it.g;
-  const SeqKeys sk = seq_keys(a.qo_indptr, a.kv_indptr, a.prefix_lens, b);
+  const bool causal = !OPT || a.custom_mask == nullptr;
+  const SeqKeys sk = seq_keys(a.qo_indptr, a.kv_indptr, a.prefix_lens, b, causal);
+  // last visible key of a row of token i: the diagonal, or every key with a custom mask
+  auto last_key = [&](int i) __attribute__((always_inline)) {
+    return causal ? min(sk.P + i, sk.n_keys - 1) : sk.n_keys - 1;
+  };
   const int q0 = sk.q0, E = sk.E, kvs = sk.kvs, P = sk.P;
   const int R = E * G;
 
@@ -136,18 +143,18 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   const bool valid = r < R;
   const int tok = valid ? r / G : 0;
   const int head = g * G + (valid ? r % G : 0);
-  const int W = a.window;
-  const int lim = valid ? min(P + tok, sk.n_keys - 1) : -1;  // last visible key
+  const int W = OPT ? a.window : 0;
+  const int lim = valid ? last_key(tok) : -1;  // last visible key
   const int lo = (W > 0 && valid) ? P + tok - W : kNoLowerKey;  // first visible key (sliding window)
   // the wave's token range (rows are token-major) and the workgroup's last visible key
   const int rw0 = it.t * BM + wv * 32;
   const bool wave_live = rw0 < R;
   const int tok_lo_w = wave_live ? rw0 / G : 0, tok_hi_w = wave_live ? min(R - 1, rw0 + 31) / G : 0;
-  const int lim_lo_w = min(P + tok_lo_w, sk.n_keys - 1);
-  const int lim_hi_w = min(P + tok_hi_w, sk.n_keys - 1);
+  const int lim_lo_w = last_key(tok_lo_w);
+  const int lim_hi_w = last_key(tok_hi_w);
   const int lo_lo_w = W > 0 ? P + tok_lo_w - W : kNoLowerKey;
   const int lo_hi_w = W > 0 ? P + tok_hi_w - W : kNoLowerKey;
-  const int key_last = min(P + min(R - 1, it.t * BM + BM - 1) / G, sk.n_keys - 1);
+  const int key_last = last_key(min(R - 1, it.t * BM + BM - 1) / G);
 
   const gptr<T> kpool = (gptr<T>)a.k_pool;
   const gptr<T> vpool = (gptr<T>)a.v_pool;
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
 
     const int j0 = kt * BN;
     if (wave_live && j0 <= lim_hi_w && j0 + BN - 1 >= lo_lo_w) {
-      const bool need_mask = j0 + BN - 1 > lim_lo_w || j0 < lo_hi_w;
+      const bool need_mask = j0 + BN - 1 > lim_lo_w || j0 < lo_hi_w || !causal;
 
       // S^T = K Q^T for the tile's 32-key blocks
       f32x16 s[NKB];
@@ -318,13 +325,24 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
             s[kb][rr] = a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
           }
       }
-      if (need_mask) {
+      if (need_mask && causal) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
             s[kb][rr] = (j <= lim && j >= lo) ? s[kb][rr] : -INFINITY;
+          }
+      } else if (need_mask) {
+        // custom mask: this row's bytes, key j at mrow[j] (addressed inside the
+        // branch, so that calls without a mask hold no register for it)
+        const uint8_t* mrow = a.custom_mask + a.mask_indptr[b] + (int64_t)tok * sk.n_keys;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
+            s[kb][rr] = (j <= lim && j >= lo && mrow[j] != 0) ? s[kb][rr] : -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -444,17 +462,24 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
 template <bool F32, int LQ, int LV, int BN, int MINB>
 hipError_t launch_attn_t(const AttnArgs& a, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (a.use_cap)
-    hipLaunchKernelGGL((attn_kernel<F32, LQ, LV, BN, true, MINB>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<F32, LQ, LV, BN, false, MINB>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  const dim3 g((unsigned)grid), t(256);
+  if (a.custom_mask || a.window > 0) {
+    if (a.use_cap)
+      hipLaunchKernelGGL((attn_kernel<F32, LQ, LV, BN, true, true, MINB>), g, t, 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<F32, LQ, LV, BN, false, true, MINB>), g, t, 0, s, a);
+  } else if (a.use_cap) {
+    hipLaunchKernelGGL((attn_kernel<F32, LQ, LV, BN, true, false, MINB>), g, t, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<F32, LQ, LV, BN, false, false, MINB>), g, t, 0, s, a);
+  }
   return hipGetLastError();
 }
 
 template <bool F32, int LQ, int LV, int BN, int MINB>
 int occupancy_t() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_kernel<F32, LQ, LV, BN, false, MINB>, 256, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_kernel<F32, LQ, LV, BN, false, false, MINB>, 256, 0) !=
       hipSuccess)
     return 1;
   return n > 0 ? n : 1;

@@ -133,7 +133,10 @@ __device__ __forceinline__ int swz_v(int r, int c) {
   }
 }
 
-template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, bool CAP, int MINB>
+// OPT: a sliding window or a custom mask (which replaces the causal rule) may
+// be set -- a variant of its own, so that calls without them run code that
+// holds no register for them
+template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, bool CAP, bool OPT, int MINB>
 __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void attn_dl_kernel(AttnArgs a) {
   using C = DlCfg<LQ, LV, BN, VK, RG, SP, NS>;
   using T = uint16_t;
@@ -162,24 +165,27 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   auto o_block = [&](int db) __attribute__((always_inline)) { return C::SPLIT > 1 ? 2 * db + half : db; };
   const int G = a.group;
   const int b = it.b, g = it.g;
-  const SeqKeys sk = seq_keys(a.qo_indptr, a.kv_indptr, a.prefix_lens, b);
+  const bool causal = !OPT || a.custom_mask == nullptr;
+  const SeqKeys sk = seq_keys(a.qo_indptr, a.kv_indptr, a.prefix_lens, b, causal);
   const int q0 = sk.q0, E = sk.E, kvs = sk.kvs, P = sk.P;
   const int R = E * G;
+  // last visible key of a row of token i: the diagonal, or every key with a custom mask
+  auto last_key = [&](int i) __attribute__((always_inline)) { return causal ? min(P + i, sk.n_keys - 1) : sk.n_keys - 1; };
 
   const int r = it.t * BM + rg * 32 + qi;
   const bool valid = r < R;
-  const int W = a.window;
-  const int lim = valid ? min(P + r / G, sk.n_keys - 1) : -1;  // last visible key of this lane's row
+  const int W = OPT ? a.window : 0;
+  const int lim = valid ? last_key(r / G) : -1;  // last visible key of this lane's row
   const int lo = (W > 0 && valid) ? P + r / G - W : kNoLowerKey;  // first visible key (sliding window)
   const int rw0 = it.t * BM + rg * 32;
   const bool wave_live = rw0 < R;
   // the wave's smallest and largest last (lim) and first (lo) visible key
   const int tok_lo_w = wave_live ? rw0 / G : 0, tok_hi_w = wave_live ? min(R - 1, rw0 + 31) / G : 0;
-  const int lim_lo_w = min(P + tok_lo_w, sk.n_keys - 1);
-  const int lim_hi_w = min(P + tok_hi_w, sk.n_keys - 1);
+  const int lim_lo_w = last_key(tok_lo_w);
+  const int lim_hi_w = last_key(tok_hi_w);
   const int lo_lo_w = W > 0 ? P + tok_lo_w - W : kNoLowerKey;
   const int lo_hi_w = W > 0 ? P + tok_hi_w - W : kNoLowerKey;
-  const int key_last = min(P + min(R - 1, it.t * BM + BM - 1) / G, sk.n_keys - 1);
+  const int key_last = last_key(min(R - 1, it.t * BM + BM - 1) / G);
 
   const gptr<T> kpool = (gptr<T>)a.k_pool;
   const gptr<T> vpool = (gptr<T>)a.v_pool;
@@ -435,7 +441,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   // max and lazy rescale; returns the value subtracted in the exponent
   auto softmax_head = [&](int kt, f32x16 (&s)[NKB]) __attribute__((always_inline)) -> float {
     const int j0 = kt * BN;
-    const bool need_mask = j0 + BN - 1 > lim_lo_w || j0 < lo_hi_w;
+    const bool need_mask = j0 + BN - 1 > lim_lo_w || j0 < lo_hi_w || !causal;
     if constexpr (CAP) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -445,13 +451,24 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
           s[kb][rr] = a.cap_out * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f));
         }
     }
-    if (need_mask) {
+    if (need_mask && causal) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
           s[kb][rr] = (j <= lim && j >= lo) ? s[kb][rr] : -INFINITY;
+        }
+    } else if (need_mask) {
+      // custom mask: this row's bytes, key j at mrow[j] (addressed here, inside
+      // the branch, so that calls without a mask hold no register for it)
+      const uint8_t* mrow = a.custom_mask + a.mask_indptr[b] + (int64_t)(valid ? r / G : 0) * sk.n_keys;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int j = j0 + kb * 32 + 8 * (rr / 4) + 4 * hi + (rr % 4);
+          s[kb][rr] = (j <= lim && j >= lo && mrow[j] != 0) ? s[kb][rr] : -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -620,12 +637,17 @@ template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, int MINB>
 hipError_t launch_dl_t(const AttnArgs& a, int64_t grid, hipStream_t s) {
   using C = DlCfg<LQ, LV, BN, VK, RG, SP, NS>;
   if (grid <= 0) return hipSuccess;
-  if (a.use_cap)
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, true, MINB>), dim3((unsigned)grid), dim3(C::NT),
-                       0, s, a);
-  else
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, MINB>), dim3((unsigned)grid), dim3(C::NT),
-                       0, s, a);
+  const dim3 g((unsigned)grid), t(C::NT);
+  if (a.custom_mask || a.window > 0) {
+    if (a.use_cap)
+      hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, true, true, MINB>), g, t, 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, true, MINB>), g, t, 0, s, a);
+  } else if (a.use_cap) {
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, true, false, MINB>), g, t, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, false, MINB>), g, t, 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -633,7 +655,7 @@ template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, int MINB>
 int dl_occupancy_t() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, MINB>),
+          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, false, MINB>),
           DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT, 0) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;

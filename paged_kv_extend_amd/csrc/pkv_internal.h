@@ -78,6 +78,8 @@ struct AttnArgs {
   const int32_t* prefix_lens;
   int32_t window;       // > 0: sliding window (keys j < P + i - window hidden)
   const float* sinks;   // [num_q_heads] sink logits (natural units), or NULL
+  const uint8_t* custom_mask;  // byte per (query, key) replacing the causal rule, or NULL
+  const int64_t* mask_indptr;  // [bs] first byte of sequence b's [E, n_keys] matrix
   int64_t q_st, q_sh, o_st, o_sh, ke_st, ke_sh, ve_st, ve_sh, kp_ss, kp_sh, vp_ss, vp_sh;
   int32_t group;     // query heads per KV head
   int32_t use_cap;   // soft-cap enabled
@@ -98,6 +100,7 @@ struct PlanArgs {
   const int32_t* kv_indptr;
   const int32_t* prefix_lens;  // as in AttnArgs
   int32_t window;              // as in AttnArgs
+  int32_t masked;              // a custom mask: every key of a sequence may be seen
   int32_t bs, num_kv_heads, group, bm, bn;
   int32_t slots;          // workgroups resident at once on the device
   int32_t min_chunk;      // never split below this many KV tiles
@@ -118,7 +121,9 @@ struct PlanArgs {
 //    < span goes through kv_indices, P = prefix_lens[b]; keys at or past P + E
 //    are never visible, so n_idx = n_keys = min(span, P + E), which also keeps
 //    every index read inside the sequence's own span.
-// A query at new-token position i sees key j iff j < n_keys and j <= P + i.
+// A query at new-token position i sees key j iff j < n_keys and j <= P + i
+// (causal), or, with a custom mask (causal == false), iff j < n_keys and its
+// mask byte is set; a unified call then keeps the whole span.
 // "no sliding window": a first visible key below every key
 constexpr int kNoLowerKey = -(1 << 30);
 
@@ -129,7 +134,7 @@ struct SeqKeys {
   int n_keys;  // keys that exist: j < n_keys
 };
 __device__ __forceinline__ SeqKeys seq_keys(const int32_t* qo_indptr, const int32_t* kv_indptr,
-                                            const int32_t* prefix_lens, int b) {
+                                            const int32_t* prefix_lens, int b, bool causal = true) {
   SeqKeys k;
   k.q0 = qo_indptr[b];
   k.E = qo_indptr[b + 1] - k.q0;
@@ -137,7 +142,7 @@ __device__ __forceinline__ SeqKeys seq_keys(const int32_t* qo_indptr, const int3
   const int span = kv_indptr[b + 1] - k.kvs;
   if (prefix_lens) {
     k.P = prefix_lens[b];
-    k.n_idx = k.n_keys = min(span, k.P + k.E);
+    k.n_idx = k.n_keys = causal ? min(span, k.P + k.E) : span;
   } else {
     k.P = span;
     k.n_idx = span;

@@ -178,7 +178,11 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       const int row_hi = min((t + 1) * BM, seq_e[b] * G) - 1;
       // tiles from the first key any row of the item sees (sliding window) to its last
       const int first = a.window > 0 ? max(0, seq_p[b] + (t * BM) / G - a.window) / BN : 0;
-      const int cost = ceil_div(seq_p[b] + row_hi / G + 1, BN) - first;
+      // with a custom mask every key of the sequence may be seen
+      const int keys = !a.masked ? seq_p[b] + row_hi / G + 1
+                                 : (a.prefix_lens ? a.kv_indptr[b + 1] - a.kv_indptr[b] : seq_p[b] + seq_e[b]);
+      // (at least one tile: size classes and chunk ranges assume it)
+      const int cost = max(1, ceil_div(keys, BN) - first);
       cost_of[n] = cost;
       my_total += cost;
       // next item: next tile, next head, or next sequence
