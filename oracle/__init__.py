@@ -11,7 +11,7 @@ rows with OpenMP; this module is its ctypes wrapper.
 Definitions follow the SGLang page "extend_attention.py" (functions
 build_unified_kv_indices, _copy_unified_indices_kernel, _fwd_kernel_unified,
 redundant_attention) and the page "flashinfer_backend.py" (forward_extend,
-call_begin_forward).  Parity is pinned in tests/test_oracle_pins.py.
+call_begin_forward; forward_decode and the decode index updater).  Parity is pinned in tests/test_oracle_pins.py.
 """
 
 from __future__ import annotations
@@ -60,6 +60,9 @@ def _load():
         lib.oracle_extend_attention_unified.argtypes = (
             [i32] + [P, i64, i64] * 3 + [i64, P, P, P, P, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32, i32, P, P, P])
         lib.oracle_extend_attention_unified.restype = ctypes.c_int
+        lib.oracle_decode_attention.argtypes = (
+            [i32] + [P, i64, i64] * 3 + [i64, P, P, i32, i32, i32, i32, i32, f64, f64, P, i32, P, i32, i32, P])
+        lib.oracle_decode_attention.restype = ctypes.c_int
         lib.oracle_store_kv_cache.argtypes = [i32, i64, i32, i32, i32] + [P, i64, i64] * 4 + [i64, P]
         lib.oracle_store_kv_cache.restype = ctypes.c_int
         lib.oracle_gather_kv_indices.argtypes = [P, i64, P, P, P, i32, P, P]
@@ -211,6 +214,40 @@ def extend_attention_unified(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices
     rc = lib.oracle_extend_attention_unified(*args)
     if rc != 0:
         raise ValueError(f"oracle unified attention failed: {rc}")
+    return out[:n]
+
+
+def decode_attention(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale=0.0, logit_cap=0.0, dtype="bf16",
+                     seqs=None, num_threads=0, window=0, sinks=None):
+    """Exact (double) decode attention: row b of q ([bs, hq, lq]) attends to
+    every key of request b through kv_indices (the last window + 1 of them
+    with a sliding window).  Returns float64 [len(seqs) or bs, hq, lv]."""
+    lib = _load()
+    dt = 0 if dtype == "bf16" else 1
+    want = np.uint16 if dt == 0 else np.float32
+    for x in (q, k_pool, v_pool):
+        assert x.dtype == want, (x.dtype, want)
+    kvp = np.ascontiguousarray(kv_indptr, np.int32)
+    kvi = np.ascontiguousarray(kv_indices, np.int64)
+    if kvi.size == 0:
+        kvi = np.zeros(1, np.int64)
+    bs = len(kvp) - 1
+    hq, lq = q.shape[1], q.shape[2]
+    hkv, lv = k_pool.shape[1], v_pool.shape[2]
+    seq_arr = None if seqs is None else np.ascontiguousarray(seqs, np.int32)
+    n = bs if seq_arr is None else len(seq_arr)
+    out = np.zeros((max(n, 1), hq, lv), np.float64)
+    args = [dt]
+    for x in (q, k_pool, v_pool):
+        s0, s1 = _strides(x)
+        args += [_ptr(x) if x.size else 0, s0, s1]
+    sk = _sinks(sinks, hq)
+    args += [k_pool.shape[0], _ptr(kvp), _ptr(kvi), bs, hq, hkv, lq, lv, float(sm_scale), float(logit_cap),
+             _ptr(seq_arr) if seq_arr is not None and n else None, n, _ptr(out), int(num_threads), int(window),
+             _ptr(sk) if sk is not None else None]
+    rc = lib.oracle_decode_attention(*args)
+    if rc != 0:
+        raise ValueError(f"oracle decode attention failed: {rc}")
     return out[:n]
 
 

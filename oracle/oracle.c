@@ -17,6 +17,10 @@
  *    call_begin_forward (the prefix is read through kv_indptr/kv_indices,
  *    the new tokens' K/V share qo_indptr with the queries).
  *
+ *  - decode attention: page "flashinfer_backend.py", forward_decode and the
+ *    decode index updater (one query token per request over its pool keys,
+ *    with the sliding-window key range of update_sliding_window).
+ *
  *  - the steps before attention: the KV-cache store of the new tokens
  *    (page "flashinfer_backend.py", forward_extend, set_kv_buffer) and the
  *    prefix index gather from the request-to-token table (the same page,
@@ -335,6 +339,103 @@ int oracle_extend_attention_unified(int32_t dtype,
     }
     free(s);
     free(seen);
+    free(acc);
+  }
+  return status;
+}
+
+/*
+ * Decode attention (flashinfer_backend.py, forward_decode; the decode index
+ * updater's update_single_wrapper and update_sliding_window): one query
+ * token per request, whose K/V the caller has already stored in the pool,
+ * attends to every key of its request, read through kv_indices.
+ *
+ * Request b has n = kv_indptr[b+1] - kv_indptr[b] keys, key j being pool slot
+ * kv_indices[kv_indptr[b] + j]; its query is row b of q.  With a sliding
+ * window W > 0 only the last min(n, W + 1) keys are kept (keys j >= n - 1 - W),
+ * as the sliding-window updater shortens paged_kernel_lens and moves
+ * kv_start_idx.  Scale, cap and softmax as in oracle_extend_attention; a sink
+ * adds exp(sink - m) to the denominator.  A request with no key gets zeros.
+ *
+ * seqs (n_seqs entries, or NULL for all bs requests) selects the requests
+ * computed; out is [n_seqs][hq][lv] in double.
+ */
+int oracle_decode_attention(int32_t dtype,
+                            const void* q, int64_t q_st, int64_t q_sh,
+                            const void* k_pool, int64_t kp_ss, int64_t kp_sh,
+                            const void* v_pool, int64_t vp_ss, int64_t vp_sh,
+                            int64_t pool_slots, const int32_t* kv_indptr, const int64_t* kv_indices,
+                            int32_t bs, int32_t hq, int32_t hkv, int32_t lq, int32_t lv,
+                            double sm_scale, double logit_cap, const int32_t* seqs, int32_t n_seqs,
+                            double* out, int32_t num_threads, int32_t window, const float* sinks) {
+  if (bs < 0 || hq <= 0 || hkv <= 0 || lq <= 0 || lv <= 0) return ORACLE_EINVAL;
+  if (hq % hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_EINVAL;
+  if (seqs == NULL) n_seqs = bs;
+  const int32_t group = hq / hkv;
+  const double scale = sm_scale != 0.0 ? sm_scale : 1.0 / sqrt((double)lq);
+
+  int64_t max_keys = 1;
+  for (int32_t r = 0; r < n_seqs; ++r) {
+    int32_t b = seqs ? seqs[r] : r;
+    if (b < 0 || b >= bs) return ORACLE_EINVAL;
+    int64_t n = (int64_t)(kv_indptr[b + 1] - kv_indptr[b]);
+    if (n > max_keys) max_keys = n;
+    for (int64_t j = 0; j < n; ++j) {
+      int64_t slot = kv_indices[kv_indptr[b] + j];
+      if (slot < 0 || slot >= pool_slots) return ORACLE_ERANGE;
+    }
+  }
+
+  int status = ORACLE_OK;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#endif
+#pragma omp parallel
+  {
+    double* logit = (double*)malloc(sizeof(double) * (size_t)max_keys);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)lv);
+    if (!logit || !acc) {
+#pragma omp atomic write
+      status = ORACLE_ENOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t w = 0; w < (int64_t)n_seqs * hq; ++w) {
+        int32_t r = (int32_t)(w / hq);
+        int32_t h = (int32_t)(w % hq);
+        int32_t b = seqs ? seqs[r] : r;
+        int32_t g = h / group;
+        int64_t n = kv_indptr[b + 1] - kv_indptr[b];
+        int64_t first = (window > 0 && n - 1 - window > 0) ? n - 1 - window : 0;
+        double* o = out + ((int64_t)r * hq + h) * (int64_t)lv;
+
+        double m = -INFINITY;
+        for (int64_t j = first; j < n; ++j) {
+          int64_t koff = kv_indices[kv_indptr[b] + j] * kp_ss + (int64_t)g * kp_sh;
+          double dot = 0.0;
+          for (int32_t d = 0; d < lq; ++d)
+            dot += load_elem(q, dtype, (int64_t)b * q_st + (int64_t)h * q_sh + d) * load_elem(k_pool, dtype, koff + d);
+          double x = dot * scale;
+          if (logit_cap > 0.0) x = logit_cap * tanh(x / logit_cap);
+          logit[j] = x;
+          if (x > m) m = x;
+        }
+        for (int32_t d = 0; d < lv; ++d) acc[d] = 0.0;
+        if (first >= n) {
+          for (int32_t d = 0; d < lv; ++d) o[d] = 0.0;
+          continue;
+        }
+        double den = 0.0;
+        for (int64_t j = first; j < n; ++j) {
+          int64_t voff = kv_indices[kv_indptr[b] + j] * vp_ss + (int64_t)g * vp_sh;
+          double e = exp(logit[j] - m);
+          den += e;
+          for (int32_t d = 0; d < lv; ++d) acc[d] += e * load_elem(v_pool, dtype, voff + d);
+        }
+        if (sinks) den += exp((double)sinks[h] - m);
+        for (int32_t d = 0; d < lv; ++d) o[d] = acc[d] / den;
+      }
+    }
+    free(logit);
     free(acc);
   }
   return status;

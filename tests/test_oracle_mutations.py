@@ -36,6 +36,13 @@ MUTATIONS = {
     "gather_ignores_start": ("int64_t start = kv_start_idx ? kv_start_idx[b] : 0;", "int64_t start = 0;"),
     "gather_indptr_skips_first": ("kv_indptr[b + 1] = kv_indptr[b] + kv_lens[b];",
                                   "kv_indptr[b + 1] = kv_indptr[b] + kv_lens[b] + (b == 0);"),
+    "decode_window_one_key_short": ("? n - 1 - window : 0;", "? n - window : 0;"),
+    "decode_query_row_of_output": ("(int64_t)b * q_st + (int64_t)h * q_sh + d)",
+                                   "(int64_t)r * q_st + (int64_t)h * q_sh + d)"),
+    "decode_empty_request_nan": ("for (int32_t d = 0; d < lv; ++d) o[d] = 0.0;",
+                                 "for (int32_t d = 0; d < lv; ++d) o[d] = NAN;"),
+    "decode_kv_head_modulo": ("int32_t g = h / group;\n        int64_t n = kv_indptr",
+                              "int32_t g = h % hkv;\n        int64_t n = kv_indptr"),
     "unified_batch_index_base": ("int64_t koff = kv_indices[kv_indptr[b] + j] * kp_ss",
                                  "int64_t koff = kv_indices[kv_indptr[0] + j] * kp_ss"),
 }

@@ -570,3 +570,105 @@ def test_unified_custom_mask_matches_two_part():
     got = oracle.extend_attention_unified(w.q, w.k_pool, w.v_pool, w.qo_indptr, indptr, indices, plens,
                                           dtype="bf16", custom_mask=m, mask_indptr=mi, window=4)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- decode
+# (page flashinfer_backend.py, forward_decode: one query token per request over
+# its pool keys; update_sliding_window keeps the last window + 1 keys)
+
+def _decode(d, **kw):
+    return oracle.decode_attention(d.q, d.k_pool, d.v_pool, d.kv_indptr, d.kv_indices, d.sm_scale,
+                                   d.logit_cap, d.cfg.dtype, **kw)
+
+
+def _decode_sdpa(d, keep=None, scale=None):
+    """Library attention of each request's query over its gathered keys
+    (the last `keep` of them when given)."""
+    c = d.cfg
+    g = c.hq // c.hkv
+    out = np.zeros((d.bs, c.hq, c.lv))
+    for b in range(d.bs):
+        k0, k1 = int(d.kv_indptr[b]), int(d.kv_indptr[b + 1])
+        if keep is not None:
+            k0 = max(k0, k1 - keep)
+        if k1 == k0:
+            continue
+        slots = d.kv_indices[k0:k1]
+        k = _f64(d.k_pool[slots], c.dtype).transpose(0, 1).repeat_interleave(g, 0)  # [Hq, n, Lq]
+        v = _f64(d.v_pool[slots], c.dtype).transpose(0, 1).repeat_interleave(g, 0)
+        q = _f64(d.q[b:b + 1], c.dtype).transpose(0, 1)  # [Hq, 1, Lq]
+        sc = scale if scale is not None else (c.sm_scale or 1.0 / math.sqrt(c.lq))
+        out[b] = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=sc)[:, 0].numpy()
+    return out
+
+
+DECODE_CASES = [
+    dict(key_lens=[37, 1, 200, 64], dtype="bf16", hq=32, hkv=8, lq=128, lv=128),
+    dict(key_lens=[5, 90], dtype="fp32", hq=4, hkv=4, lq=64, lv=64, sm_scale=0.2),
+    dict(key_lens=[33, 17, 3], dtype="bf16", hq=16, hkv=1, lq=576, lv=512, v_aliases_k=True, std=0.5),
+    dict(key_lens=[12, 0, 40], dtype="bf16", hq=6, hkv=2, lq=192, lv=128),
+    dict(key_lens=[70], dtype="bf16", hq=8, hkv=2, lq=256, lv=256, sm_scale=-0.05),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"{c['dtype']}-{c['lq']}x{c['lv']}-h{c['hq']}/{c['hkv']}")
+def test_decode_matches_library_attention(case):
+    d = wl.decode_custom(**case)
+    np.testing.assert_allclose(_decode(d), _decode_sdpa(d), rtol=0, atol=1e-12)
+
+
+def test_decode_is_unified_extend_of_one_new_token():
+    # a decode step is the unified extend of E = 1 whose prefix is every earlier key
+    d = wl.decode_custom([25, 1, 60, 9], hq=8, hkv=2, lq=64, lv=64, logit_cap=3.0)
+    sinks = np.array([0.5, -1.0, 2.0, 0.0, 1.5, -3.0, 0.25, 1.0], np.float32)
+    qo = np.arange(d.bs + 1, dtype=np.int32)
+    plens = (d.key_lens - 1).astype(np.int32)
+    for window in (0, 4, 30):
+        got = _decode(d, window=window, sinks=sinks)
+        want = oracle.extend_attention_unified(d.q, d.k_pool, d.v_pool, qo, d.kv_indptr, d.kv_indices, plens,
+                                               d.sm_scale, d.logit_cap, "bf16", window=window, sinks=sinks)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [1, 7, 63, 500])
+def test_decode_window_is_attention_over_the_last_keys(window):
+    d = wl.decode_custom([1, 8, 64, 150], hq=4, hkv=2, lq=64, lv=64)
+    np.testing.assert_allclose(_decode(d, window=window), _decode_sdpa(d, keep=window + 1), rtol=0, atol=1e-12)
+
+
+def test_decode_single_key_returns_its_value():
+    d = wl.decode_custom([1, 1], dtype="fp32", hq=4, hkv=2, lq=64, lv=48)
+    got = _decode(d)
+    for b in range(2):
+        v = d.v_pool[d.kv_indices[b]].astype(np.float64)  # [Hkv, Lv]
+        np.testing.assert_array_equal(got[b], v.repeat(2, axis=0))
+
+
+def test_decode_request_without_keys_is_zero():
+    d = wl.decode_custom([4, 0, 3], hq=4, hkv=2, lq=64, lv=64)
+    sinks = np.array([1.0, 0.0, -1.0, 2.0], np.float32)
+    for s in (None, sinks):
+        got = _decode(d, sinks=s)
+        assert np.array_equal(got[1], np.zeros_like(got[1]))
+        assert np.isfinite(got).all()
+
+
+def test_decode_sink_closed_form_with_zero_query():
+    # all logits 0: out = sum_j V_j / (n + e^sink)
+    d = wl.decode_custom([6, 31], hq=4, hkv=1, lq=64, lv=64)
+    d.q[:] = 0
+    sinks = np.array([-1.0, 0.0, 0.7, 4.0], np.float32)
+    got = _decode(d, sinks=sinks)
+    for b in range(d.bs):
+        slots = d.kv_indices[d.kv_indptr[b]:d.kv_indptr[b + 1]]
+        v = wl.as_f32(d.v_pool[slots], "bf16").astype(np.float64)[:, 0]  # [n, Lv]
+        for h in range(4):
+            want = v.sum(axis=0) / (len(slots) + math.exp(float(sinks[h])))
+            np.testing.assert_allclose(got[b, h], want, atol=1e-12)
+
+
+def test_decode_selected_requests_equal_full_batch():
+    d = wl.decode_custom([9, 14, 2, 30, 5], hq=4, hkv=2, lq=64, lv=64)
+    full = _decode(d)
+    sel = [3, 0, 4]
+    np.testing.assert_array_equal(_decode(d, seqs=sel), full[sel])

@@ -291,6 +291,141 @@ def index_case(rng: np.random.Generator, bs: int, max_p: int = 300, max_e: int =
                 extend_kv_indices=extend_kv_indices, bs=bs)
 
 
+# ----------------------------------------------------------------------------- decode batches
+# One query token per request over its pool keys (the new token's K/V already
+# stored).  Seeds are 1100 + k.
+
+@dataclasses.dataclass
+class DecodeConfig:
+    name: str
+    dtype: str
+    bs: int
+    hq: int
+    hkv: int
+    lq: int
+    lv: int
+    std: float
+    sm_scale: float
+    logit_cap: float
+    seed: int
+    key_lens: Callable[[np.random.Generator, int], np.ndarray]
+    v_aliases_k: bool = False
+    description: str = ""
+
+
+DECODE_CONFIGS = {
+    "decode_llama8b": DecodeConfig(
+        "decode_llama8b", "bf16", bs=64, hq=32, hkv=8, lq=128, lv=128, std=1.0, sm_scale=0.0, logit_cap=0.0,
+        seed=1101, key_lens=_uniform(2048, 6144),
+        description="Llama-3-8B-shaped decode: bs 64, 32/8 heads, D 128, keys~U[2048,6144]"),
+    "decode_long": DecodeConfig(
+        "decode_long", "bf16", bs=8, hq=32, hkv=8, lq=128, lv=128, std=1.0, sm_scale=0.0, logit_cap=0.0,
+        seed=1102, key_lens=_fixed([32768] * 8),
+        description="long-context decode: bs 8, 32/8 heads, D 128, 32768 keys each"),
+    "decode_mla": DecodeConfig(
+        "decode_mla", "bf16", bs=32, hq=16, hkv=1, lq=576, lv=512, std=0.5, sm_scale=0.0, logit_cap=0.0,
+        seed=1103, key_lens=_uniform(1024, 8192), v_aliases_k=True,
+        description="MLA-shaped decode: bs 32, 16/1 heads, Lq 576, Lv 512 = K[:, :512], keys~U[1024,8192]"),
+}
+
+
+@dataclasses.dataclass
+class DecodeBatch:
+    cfg: DecodeConfig
+    key_lens: np.ndarray   # int32 [bs]
+    kv_indptr: np.ndarray  # int32 [bs + 1]
+    kv_indices: np.ndarray  # int64, distinct pool slots
+    q: np.ndarray          # [bs, hq, lq]
+    k_pool: np.ndarray     # [pool_slots, hkv, lq]; unused slots hold NaN
+    v_pool: np.ndarray     # [pool_slots, hkv, lv] (a view into k_pool when V lies inside K)
+
+    @property
+    def bs(self) -> int:
+        return int(self.key_lens.shape[0])
+
+    @property
+    def num_keys(self) -> int:
+        return int(self.kv_indptr[-1])
+
+    @property
+    def sm_scale(self) -> float:
+        return self.cfg.sm_scale
+
+    @property
+    def logit_cap(self) -> float:
+        return self.cfg.logit_cap
+
+    def algorithmic_bytes(self) -> float:
+        """Bytes a decode pass must move: every key's K (and V unless inside K)
+        row per KV head, its slot index, the queries and the outputs."""
+        c = self.cfg
+        el = 2 if c.dtype == "bf16" else 4
+        row = c.lq + (0 if c.v_aliases_k else c.lv)
+        return float(self.num_keys * (c.hkv * row * el + 8) + self.bs * c.hq * (c.lq + c.lv) * el)
+
+
+def decode_batch(cfg: DecodeConfig, key_lens: Optional[Sequence[int]] = None, pool_slots: Optional[int] = None,
+                 rng: Optional[np.random.Generator] = None) -> DecodeBatch:
+    """Draw one decode batch for cfg (key lengths may be overridden)."""
+    if rng is None:
+        rng = np.random.default_rng(cfg.seed)
+    n = cfg.key_lens(rng, cfg.bs) if key_lens is None else np.asarray(key_lens, np.int64)
+    n = n.astype(np.int64)
+    bs = n.shape[0]
+    total = int(n.sum())
+    slots = pool_slots if pool_slots is not None else total + 37
+    if total > slots:
+        raise ValueError(f"{cfg.name}: {total} keys do not fit {slots} slots")
+    kv_indices = rng.permutation(slots)[:total].astype(np.int64)
+    kv_indptr = np.zeros(bs + 1, np.int32)
+    kv_indptr[1:] = np.cumsum(n)
+    dt = cfg.dtype
+    q = _draw(rng, (bs, cfg.hq, cfg.lq), cfg.std, dt)
+    np_dtype = np.uint16 if dt == "bf16" else np.float32
+    fill = BF16_NAN if dt == "bf16" else np.float32(np.nan)
+    k_pool = np.full((slots, cfg.hkv, cfg.lq), fill, dtype=np_dtype)
+    k_pool[kv_indices] = _draw(rng, (total, cfg.hkv, cfg.lq), cfg.std, dt)
+    if cfg.v_aliases_k:
+        v_pool = k_pool[..., :cfg.lv]
+    else:
+        v_pool = np.full((slots, cfg.hkv, cfg.lv), fill, dtype=np_dtype)
+        v_pool[kv_indices] = _draw(rng, (total, cfg.hkv, cfg.lv), cfg.std, dt)
+    return DecodeBatch(cfg, n.astype(np.int32), kv_indptr, kv_indices, q, k_pool, v_pool)
+
+
+def decode_custom(key_lens=(16,), dtype="bf16", hq=4, hkv=2, lq=64, lv=64, std=1.0, sm_scale=0.0, logit_cap=0.0,
+                  seed=11, v_aliases_k=False, pool_slots=None) -> DecodeBatch:
+    """A test-shape decode batch with explicit key counts."""
+    n = np.asarray(key_lens, np.int64)
+    cfg = DecodeConfig("decode_custom", dtype, bs=len(n), hq=hq, hkv=hkv, lq=lq, lv=lv, std=std,
+                       sm_scale=sm_scale, logit_cap=logit_cap, seed=seed, key_lens=_fixed(n),
+                       v_aliases_k=v_aliases_k)
+    return decode_batch(cfg, pool_slots=pool_slots)
+
+
+def decode_get(name: str, **kw) -> DecodeBatch:
+    return decode_batch(DECODE_CONFIGS[name], **kw)
+
+
+def decode_to_torch(d: DecodeBatch, device="cuda"):
+    """Device tensors of a decode batch (bf16 bit patterns become torch.bfloat16)."""
+    import torch
+
+    def t(x):
+        a = torch.from_numpy(np.ascontiguousarray(x))
+        if d.cfg.dtype == "bf16":
+            a = a.view(torch.bfloat16)
+        return a.to(device)
+
+    c = d.cfg
+    out = dict(q=t(d.q), k_pool=t(d.k_pool))
+    out["v_pool"] = out["k_pool"][..., :c.lv] if c.v_aliases_k else t(d.v_pool)
+    out["kv_indptr"] = torch.from_numpy(d.kv_indptr.astype(np.int32)).to(device)
+    out["kv_indices"] = torch.from_numpy(d.kv_indices.astype(np.int64)).to(device)
+    out["o"] = torch.empty((d.bs, c.hq, c.lv), dtype=out["q"].dtype, device=device)
+    return out
+
+
 def to_torch(w: Workload, device="cuda"):
     """Device tensors of a workload (bf16 bit patterns become torch.bfloat16)."""
     import torch
