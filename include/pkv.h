@@ -277,6 +277,52 @@ int extend_attention_fwd_unified(const void* q_extend, void* o, const void* k_po
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention: one new token per request over its pool keys.
+ * Page "flashinfer_backend.py": forward_decode (each request's single query
+ * token attends to every key its decode indices list, the new token's own
+ * K/V already stored in the pool) and the decode index updater (kv_indptr /
+ * kv_indices per request; with a sliding window only the last window + 1
+ * keys).  Scale, soft-cap and sinks as in page "extend_attention.py",
+ * _fwd_kernel_unified.  This equals extend_attention_fwd_unified with one new
+ * token per request whose prefix is every earlier key; a kernel of its own
+ * serves it, splitting each request's keys over many workgroups.
+ *
+ * For request b (n_b = kv_indptr[b+1] - kv_indptr[b] keys), query head h and
+ * KV head g = h / (num_q_heads / num_kv_heads):
+ *   key j in [f_b, n_b): k_pool[kv_indices[kv_indptr[b] + j], g], v_pool likewise,
+ *       f_b = max(0, n_b - 1 - sliding_window) with a window, else 0
+ *   s_j = scale * <q[b, h], K_j>, scale = sm_scale, or 1/sqrt(lq) when 0;
+ *   if logit_cap > 0: s_j = logit_cap * tanh(s_j / logit_cap)
+ *   o[b, h] = sum_j e^{s_j - m} V_j / (sum_j e^{s_j - m} + e^{sinks[h] - m})
+ *   (the sink term only with desc->sinks); o[b, h] = 0 when n_b == 0.
+ *
+ * Arguments (device pointers unless noted):
+ *  q          [bs, num_q_heads, lq]  strides (desc->q_stride_tok, q_stride_head)
+ *  o          out [bs, num_q_heads, lv]  strides (o_stride_tok, o_stride_head);
+ *             every row of every request is written.
+ *  k_pool, v_pool: as in pkv_attn_desc_t; v_pool may be the first lv columns
+ *             of k_pool (same base and strides; required for lq 576 / lv 512
+ *             unless v_pool is a pool of its own).
+ *  kv_indptr  int32[bs+1], non-decreasing; kv_indptr[bs] - kv_indptr[0] ==
+ *             desc->num_prefix_indices (the length of kv_indices).
+ *  kv_indices int64[num_prefix_indices], each in [0, pool_slots).
+ *  sm_scale, logit_cap: host floats as for extend_attention_fwd.
+ *  desc       host pointer: dtype must be PKV_BF16; (lq, lv) one of (64, 64),
+ *             (128, 128), (256, 256), (192, 128), (288, 256), (576, 512);
+ *             sliding_window and sinks are honoured, custom_mask must be NULL;
+ *             total_q_tokens and the k/v_extend strides are not used.
+ *  workspace  device buffer of >= decode_attention_workspace_size(desc)
+ *             bytes, 256-byte aligned, no initialisation needed; calls that
+ *             overlap in time must use different workspaces.
+ *  stream     hipStream_t.
+ * The result is bitwise reproducible run to run on the same device.
+ */
+size_t decode_attention_workspace_size(const pkv_attn_desc_t* desc);
+int decode_attention_fwd(const void* q, void* o, const void* k_pool, const void* v_pool, const int32_t* kv_indptr,
+                         const int64_t* kv_indices, float sm_scale, float logit_cap, const pkv_attn_desc_t* desc,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Process-wide kernel preference for later extend_attention_fwd calls, for
  * tests and benchmarks: "auto" (the default: the fastest measured kernel that
  * serves the shape), "r64" (64 query rows per wave; bf16, lq == lv == 128), "dl"
@@ -303,7 +349,8 @@ const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc, const void
 
 /*
  * Measurement hook (not needed for results).  pkv_profile_enable(1) clears
- * the record and makes every later extend_attention_fwd call record a HIP
+ * the record and makes every later extend_attention_fwd,
+ * extend_attention_fwd_unified or decode_attention_fwd call record a HIP
  * event pair on its stream around its attention kernel; 0 stops recording.
  * pkv_profile_read waits for the recorded events and returns the summed
  * attention-kernel time in milliseconds and the number of calls.  The

@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_fwd_unified",
-           "extend_attention_workspace_size", "store_kv_cache", "gather_kv_indices",
+           "extend_attention_workspace_size", "decode_attention_fwd", "decode_attention_workspace_size", "store_kv_cache", "gather_kv_indices",
            "extend_attention_kernel_name", "extend_attention_prefer_kernel",
            "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "LIB_PATH", "PkvError"]
 
@@ -66,6 +66,11 @@ def library() -> ctypes.CDLL:
     lib.extend_attention_fwd_unified.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
                                                  ctypes.POINTER(AttnDesc), P, ctypes.c_size_t, P]
     lib.extend_attention_fwd_unified.restype = ctypes.c_int
+    lib.decode_attention_workspace_size.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.decode_attention_workspace_size.restype = ctypes.c_size_t
+    lib.decode_attention_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
+                                         ctypes.POINTER(AttnDesc), P, ctypes.c_size_t, P]
+    lib.decode_attention_fwd.restype = ctypes.c_int
     lib.store_kv_cache.argtypes = [P, P, P, P, P, ctypes.POINTER(AttnDesc), P]
     lib.store_kv_cache.restype = ctypes.c_int
     lib.gather_kv_indices.argtypes = [P, i64, P, P, P, i32, P, P, i64, P]
@@ -343,6 +348,40 @@ def extend_attention_fwd_unified(q_extend: torch.Tensor, o: torch.Tensor, k_pool
     rc = library().extend_attention_fwd_unified(
         _ptr(q_extend), _ptr(o), _ptr(k_pool), _ptr(v_pool), _ptr(qo_indptr), _ptr(kv_indptr),
         _ptr(kv_indices), _ptr(prefix_lens), float(sm_scale or 0.0), float(logit_cap), ctypes.byref(desc),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    _check(rc)
+    return o
+
+
+def decode_attention_workspace_size(desc: AttnDesc) -> int:
+    n = library().decode_attention_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        raise PkvError(-1, last_error())
+    return int(n)
+
+
+def decode_attention_fwd(q: torch.Tensor, o: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                         kv_indptr: torch.Tensor, kv_indices: torch.Tensor, sm_scale: Optional[float] = None,
+                         logit_cap: float = 0.0, workspace: Optional[torch.Tensor] = None, sliding_window: int = 0,
+                         sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention into ``o`` ([bs, num_q_heads, lv]): the query row q[b]
+    attends to request b's keys kv_indices[kv_indptr[b]:kv_indptr[b+1]] (the
+    last sliding_window + 1 of them with a window); see include/pkv.h."""
+    _want(kv_indptr, "kv_indptr", torch.int32)
+    _want(kv_indices, "kv_indices", torch.int64)
+    bs = kv_indptr.numel() - 1
+    if q.dim() != 3 or q.shape[0] != bs or o.dim() != 3 or o.shape[0] != bs:
+        raise ValueError("q and o must be [bs, num_q_heads, dim] with bs = len(kv_indptr) - 1")
+    desc = make_desc(q, None, None, o, k_pool, v_pool, bs, kv_indices.numel())
+    _options(desc, q, sliding_window, sinks)
+    dev = q.device
+    stream = _stream(dev)
+    nbytes = decode_attention_workspace_size(desc)
+    if workspace is None:
+        workspace = _workspace(dev, stream, nbytes)
+    rc = library().decode_attention_fwd(
+        _ptr(q), _ptr(o), _ptr(k_pool), _ptr(v_pool), _ptr(kv_indptr), _ptr(kv_indices),
+        float(sm_scale or 0.0), float(logit_cap), ctypes.byref(desc),
         _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
     _check(rc)
     return o

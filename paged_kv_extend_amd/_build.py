@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = ["api.cpp", "index_build.hip", "kv_cache.hip", "plan.hip", "attention.hip", "attention_dl.hip",
-           "attention_r64.hip"]
+           "attention_r64.hip", "decode.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          # no packed fp32 instructions from the compiler

@@ -541,3 +541,156 @@ int extend_attention_fwd_unified(const void* q_extend, void* o, const void* k_po
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- decode
+namespace {
+
+// Workgroups the decode launch aims at (MI355X: 256 CUs, one decode workgroup
+// per CU at a time, eight rounds), a function of the sizes only so that the
+// workspace size query and the call agree on any device.
+constexpr int64_t kDecodeTargetWgs = 2048;
+constexpr int64_t kDecodeMinChunk = 128;
+constexpr int64_t kDecodeMaxChunk = 16384;
+constexpr int64_t kMaxGridY = 65535;
+
+struct DecodeSizes {
+  int hblocks, gh_count;
+  int64_t chunk, chunks;
+  size_t vis, arrived, part_ml, part_acc, total;  // workspace offsets and size
+};
+
+DecodeSizes decode_sizes(const pkv_attn_desc_t& d) {
+  DecodeSizes z;
+  const int group = d.num_q_heads / d.num_kv_heads;
+  z.hblocks = (group + 15) / 16;
+  z.gh_count = d.num_kv_heads * z.hblocks;
+  int64_t vis = d.num_prefix_indices;  // visible keys over all requests, at most
+  if (d.sliding_window > 0) vis = std::min(vis, (int64_t)d.bs * ((int64_t)d.sliding_window + 1));
+  int64_t chunk = (vis * z.gh_count + kDecodeTargetWgs - 1) / kDecodeTargetWgs;
+  chunk = std::max(chunk, (vis + kMaxGridY - 1) / kMaxGridY);
+  chunk = std::min(std::max(chunk, kDecodeMinChunk), std::max(kDecodeMaxChunk, (vis + kMaxGridY - 1) / kMaxGridY));
+  chunk = (chunk + 63) / 64 * 64;
+  z.chunk = chunk;
+  z.chunks = (vis + chunk - 1) / chunk;
+  const int64_t rows = 2 * z.chunks * z.gh_count * 16;  // two partial pieces per chunk
+  size_t off = 0;
+  z.vis = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)(d.bs + 1), 256);
+  z.arrived = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)d.bs * z.gh_count, 256);
+  z.part_ml = off;
+  off = align_up(off + sizeof(float) * 2 * (size_t)rows, 256);
+  z.part_acc = off;
+  off = align_up(off + sizeof(float) * (size_t)rows * d.lv, 256);
+  z.total = off;
+  return z;
+}
+
+int check_decode_desc(const pkv_attn_desc_t* d) {
+  if (!d) return fail(PKV_ERR_INVALID, "desc is NULL");
+  if (d->dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "decode attention serves bf16 only (dtype %d)", d->dtype);
+  if (d->bs < 0) return fail(PKV_ERR_INVALID, "bs %d < 0", d->bs);
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID, "head counts must be positive (%d, %d)", d->num_q_heads, d->num_kv_heads);
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
+                d->num_kv_heads);
+  int waves = 0;
+  if (!pkv::decode_supported(d->dtype, d->lq, d->lv, false, &waves) &&
+      !pkv::decode_supported(d->dtype, d->lq, d->lv, true, &waves))
+    return fail(PKV_ERR_UNSUPPORTED, "head dims (lq %d, lv %d) not supported for decode", d->lq, d->lv);
+  if (d->custom_mask) return fail(PKV_ERR_UNSUPPORTED, "decode attention takes no custom mask");
+  if (d->num_prefix_indices < 0 || d->pool_slots < 0)
+    return fail(PKV_ERR_INVALID, "negative size (num_prefix_indices %lld, pool_slots %lld)",
+                (long long)d->num_prefix_indices, (long long)d->pool_slots);
+  if (d->num_prefix_indices >= (1ll << 31)) return fail(PKV_ERR_UNSUPPORTED, "more than 2^31 - 1 keys");
+  if (d->num_prefix_indices > 0 && d->pool_slots <= 0)
+    return fail(PKV_ERR_INVALID, "keys given but pool_slots is %lld", (long long)d->pool_slots);
+  const int64_t strides[] = {d->q_stride_tok, d->q_stride_head, d->o_stride_tok, d->o_stride_head,
+                             d->kp_stride_slot, d->kp_stride_head, d->vp_stride_slot, d->vp_stride_head};
+  for (int64_t s : strides)
+    if (s < 0 || s % 8 != 0) return fail(PKV_ERR_UNSUPPORTED, "strides must be non-negative multiples of 8 elements");
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t decode_attention_workspace_size(const pkv_attn_desc_t* desc) {
+  if (check_decode_desc(desc) != PKV_OK) return 0;
+  g_err[0] = '\0';
+  return decode_sizes(*desc).total;
+}
+
+int decode_attention_fwd(const void* q, void* o, const void* k_pool, const void* v_pool, const int32_t* kv_indptr,
+                         const int64_t* kv_indices, float sm_scale, float logit_cap, const pkv_attn_desc_t* desc,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_decode_desc(desc);
+  if (rc != PKV_OK) return rc;
+  const pkv_attn_desc_t& d = *desc;
+  if (!std::isfinite(sm_scale) || std::isnan(logit_cap))
+    return fail(PKV_ERR_INVALID, "sm_scale must be finite and logit_cap not NaN");
+  if (d.bs == 0) return ok();
+  if (!kv_indptr || !q || !o) return fail(PKV_ERR_INVALID, "kv_indptr / q / o is NULL");
+  if (d.num_prefix_indices > 0 && (!kv_indices || !k_pool || !v_pool))
+    return fail(PKV_ERR_INVALID, "kv_indices / k_pool / v_pool is NULL with a non-empty index array");
+  const void* ptrs[] = {q, o, k_pool, v_pool};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(PKV_ERR_UNSUPPORTED, "tensor base pointers must be 16-byte aligned");
+  // V inside K: the variant that reads V out of the K tile when there is one;
+  // the general variant reads the same rows twice otherwise
+  int waves = 0;
+  bool vk = v_inside_k(d, nullptr, nullptr, k_pool, v_pool);
+  if (vk && !pkv::decode_supported(d.dtype, d.lq, d.lv, true, &waves)) vk = false;
+  if (!pkv::decode_supported(d.dtype, d.lq, d.lv, vk, &waves))
+    return fail(PKV_ERR_UNSUPPORTED, "head dims (lq %d, lv %d) not supported for decode", d.lq, d.lv);
+  const DecodeSizes z = decode_sizes(d);
+  if (!workspace || workspace_bytes < z.total)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                z.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  const double scale = sm_scale != 0.0f ? (double)sm_scale : 1.0 / sqrt((double)d.lq);
+  const double log2e = 1.4426950408889634;
+  pkv::DecodeArgs a;
+  a.q = q;
+  a.o = o;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.sinks = d.sinks;
+  a.q_st = d.q_stride_tok;
+  a.q_sh = d.q_stride_head;
+  a.o_st = d.o_stride_tok;
+  a.o_sh = d.o_stride_head;
+  a.kp_ss = d.kp_stride_slot * 2;
+  a.kp_sh = d.kp_stride_head * 2;
+  a.vp_ss = d.vp_stride_slot * 2;
+  a.vp_sh = d.vp_stride_head * 2;
+  a.bs = d.bs;
+  a.group = d.num_q_heads / d.num_kv_heads;
+  a.hblocks = z.hblocks;
+  a.lv = d.lv;
+  a.gh_count = z.gh_count;
+  a.chunk = (int32_t)z.chunk;
+  a.window = d.sliding_window > 0 ? d.sliding_window : 0;
+  a.use_cap = logit_cap > 0.0f;
+  a.scale_log2 = (float)(scale * log2e);
+  a.cap_in = a.use_cap ? (float)(scale / logit_cap) : 0.0f;
+  a.cap_out = a.use_cap ? (float)(logit_cap * log2e) : 0.0f;
+  a.vis = reinterpret_cast<int32_t*>(ws + z.vis);
+  a.arrived = reinterpret_cast<int32_t*>(ws + z.arrived);
+  a.part_ml = reinterpret_cast<float*>(ws + z.part_ml);
+  a.part_acc = reinterpret_cast<float*>(ws + z.part_acc);
+  const auto ev = profile_slot();
+  hipError_t e = pkv::launch_decode(d.lq, d.lv, vk, a, z.chunks, reinterpret_cast<hipStream_t>(stream), ev.first,
+                                    ev.second);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -188,6 +188,37 @@ hipError_t launch_index_build(const int32_t* prefix_kv_indptr, const int64_t* pr
                               const int64_t* extend_kv_indices, int32_t bs,
                               int32_t* unified_kv_indptr, int64_t* unified_kv_indices,
                               int32_t* prefix_lens, hipStream_t s);
+// Decode attention (one query token per request over its pool keys).
+struct DecodeArgs {
+  const void* q;     // [bs, num_q_heads, lq], strides (q_st, q_sh) elements
+  void* o;           // [bs, num_q_heads, lv], strides (o_st, o_sh) elements
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* kv_indptr;   // [bs + 1]
+  const int64_t* kv_indices;  // pool slot of each key
+  const float* sinks;         // [num_q_heads] sink logits (natural units), or NULL
+  int64_t q_st, q_sh, o_st, o_sh;
+  int64_t kp_ss, kp_sh, vp_ss, vp_sh;  // BYTES
+  int32_t bs, group, hblocks, lv;
+  int32_t gh_count;  // num_kv_heads * hblocks: the x extent of the grid
+  int32_t chunk;     // keys per chunk (a multiple of 64)
+  int32_t window;    // > 0: only the last window + 1 keys of a request are seen
+  int32_t use_cap;
+  float scale_log2;  // scale * log2(e)
+  float cap_in;      // scale / cap
+  float cap_out;     // cap * log2(e)
+  int32_t* vis;      // [bs + 1] first visible key of request b among all requests' visible keys
+  int32_t* arrived;  // [bs * gh_count] chunks of a split request whose state is written
+  float* part_ml;    // [2 * chunks][gh_count][16][2]: max (base-2 units), sum of weights
+  float* part_acc;   // [2 * chunks][gh_count][16][lv]
+};
+// (dtype, lq, lv, V inside K) served by the decode kernel; waves per workgroup.
+bool decode_supported(int dtype, int lq, int lv, bool v_in_k, int* waves);
+// Plan launch, then the attention launch over `chunks` chunks of a.chunk keys;
+// non-null events are recorded on s around the attention launch.
+hipError_t launch_decode(int lq, int lv, bool v_in_k, const DecodeArgs& a, int64_t chunks, hipStream_t s,
+                         hipEvent_t before, hipEvent_t after);
+
 // Workgroups of the attention kernel resident per CU (from the occupancy API).
 int attention_blocks_per_cu(int dtype, int lq, int lv);
 // The direct-to-LDS kernel (bf16, head dims 64, 128, 256, and 576/512 when V is

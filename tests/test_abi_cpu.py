@@ -181,3 +181,60 @@ def test_store_and_gather_argument_errors_without_device():
     assert lib.gather_kv_indices(p, 64, p, p, None, 3, None, p, 10, None) == -1
     assert lib.gather_kv_indices(None, 64, p, p, None, 3, p, p, 10, None) == -1
     assert lib.gather_kv_indices(p, 64, p, p, None, 3, p, None, 10, None) == -1
+
+
+def decode_desc(**kw):
+    base = dict(bs=4, total_q_tokens=4, q_stride_tok=32 * 128, o_stride_tok=32 * 128, num_prefix_indices=5000)
+    base.update(kw)
+    return desc(**base)
+
+
+def call_decode(d, ws_bytes=1 << 30, ptr=4096, ws=4096, k_pool=4096, v_pool=4096):
+    lib = pkv.library()
+    return lib.decode_attention_fwd(ptr, ptr, k_pool, v_pool, ptr, ptr, 0.0, 0.0,
+                                    ctypes.byref(d) if d is not None else None, ws, ws_bytes, None)
+
+
+def test_decode_workspace_size_grows_with_keys():
+    small = pkv.decode_attention_workspace_size(decode_desc())
+    big = pkv.decode_attention_workspace_size(decode_desc(num_prefix_indices=5_000_000, bs=64))
+    assert 0 < small < big and small % 256 == 0
+    # a sliding window bounds the keys a call can see, and with them the partial states
+    windowed = pkv.decode_attention_workspace_size(decode_desc(num_prefix_indices=5_000_000, bs=64,
+                                                               sliding_window=127))
+    assert windowed < big
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(dtype=1), "bf16"),
+    (dict(lq=80, lv=80), "not supported"),
+    (dict(num_q_heads=30), "multiple"),
+    (dict(bs=-1), "bs"),
+    (dict(kp_stride_slot=1001), "stride"),
+    (dict(num_prefix_indices=-1), "negative"),
+    (dict(num_prefix_indices=1 << 31), "2^31"),
+    (dict(custom_mask=4096, mask_indptr=4096), "custom mask"),
+])
+def test_decode_workspace_size_rejects(kw, needle):
+    lib = pkv.library()
+    assert lib.decode_attention_workspace_size(ctypes.byref(decode_desc(**kw))) == 0
+    assert needle in pkv.last_error()
+
+
+def test_decode_argument_errors_without_device():
+    assert call_decode(None) == -1
+    assert call_decode(decode_desc(dtype=1, lq=64, lv=64)) == -2
+    assert call_decode(decode_desc(), ws_bytes=16) == -3
+    assert call_decode(decode_desc(), ws=4096 + 64) == -3
+    assert call_decode(decode_desc(), ptr=4100) == -2
+    assert call_decode(decode_desc(bs=0)) == 0
+    mla = decode_desc(lq=576, lv=512, num_kv_heads=1, q_stride_tok=32 * 576, q_stride_head=576,
+                      o_stride_tok=32 * 512, o_stride_head=512, kp_stride_slot=576, kp_stride_head=576,
+                      vp_stride_slot=512, vp_stride_head=512)
+    # lq 576 / lv 512 with V in a pool of its own has a kernel; so does V inside K
+    assert pkv.decode_attention_workspace_size(mla) > 0
+    lib = pkv.library()
+    assert lib.decode_attention_fwd(4096, None, 4096, 4096, 4096, 4096, 0.0, 0.0, ctypes.byref(decode_desc()),
+                                    4096, 1 << 30, None) == -1
+    assert lib.decode_attention_fwd(4096, 4096, 4096, 4096, 4096, 4096, float("inf"), 0.0,
+                                    ctypes.byref(decode_desc()), 4096, 1 << 30, None) == -1
