@@ -43,9 +43,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel", default="auto", help="attention kernel preference: auto, r64, dl, attn")
-    ap.add_argument("--op", default="attention", choices=["attention", "store", "gather"],
+    ap.add_argument("--op", default="attention", choices=["attention", "store", "gather", "decode"],
                     help="attention: the hot path; store / gather: the KV-cache store of the new tokens or the "
-                         "request-to-token index gather of the same batch, reported in GB/s against HBM")
+                         "request-to-token index gather of the same batch, reported in GB/s against HBM; "
+                         "decode: decode attention on a decode batch (--workload decode_llama8b, decode_long, "
+                         "decode_mla), GB/s against HBM")
     ap.add_argument("--path", default="two-part", choices=["two-part", "unified"],
                     help="two-part: prefix through kv_indices, new tokens from k/v_extend (the index build "
                          "runs beside it); unified: attention reads every key through the index build's output")
@@ -112,6 +114,8 @@ def main():
     torch.cuda.init()
     pkv.extend_attention_prefer_kernel(args.kernel)
     dev = torch.device("cuda", 0)
+    if args.op == "decode":
+        return bench_decode(args, dev, torch, pkv)
     w = wl.get(args.workload)
     if args.op != "attention":
         return bench_copy_op(args, w, dev, torch, pkv)
@@ -269,6 +273,79 @@ def bench_copy_op(args, w, dev, torch, pkv):
         "config": {"workload": c.name, "op": args.op, "bytes_per_step": int(nbytes), "input_copies_rotated": copies},
         "roofline": {"bound": "hbm", "kernel": what, "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(gbs / 8000.0, 4), "traffic": None}}), flush=True)
+    return 0
+
+
+def bench_decode(args, dev, torch, pkv):
+    """Decode attention over one decode batch per step, input copies rotated."""
+    import workloads as wl
+
+    name = args.workload if args.workload in wl.DECODE_CONFIGS else "decode_llama8b"
+    d = wl.decode_get(name)
+    c = d.cfg
+    nbytes = d.algorithmic_bytes()
+    flops = float(d.key_lens.astype(np.int64).sum()) * c.hq * 2.0 * (c.lq + c.lv)
+    copies = args.copies or max(1, min(16, int(np.ceil(512e6 / nbytes))))
+    sets = []
+    for _ in range(copies):
+        t = wl.decode_to_torch(d, dev)
+        desc = pkv.make_desc(t["q"], None, None, t["o"], t["k_pool"], t["v_pool"], d.bs, d.num_keys)
+        t["ws"] = torch.empty(pkv.decode_attention_workspace_size(desc), dtype=torch.uint8, device=dev)
+        sets.append(t)
+
+    def step(i):
+        t = sets[i % copies]
+        pkv.decode_attention_fwd(t["q"], t["o"], t["k_pool"], t["v_pool"], t["kv_indptr"], t["kv_indices"],
+                                 sm_scale=d.sm_scale, logit_cap=d.logit_cap, workspace=t["ws"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pkv.profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    pkv.profile_enable(False)
+    kern_ms, calls = pkv.profile_read()
+    ms_kernel = kern_ms / max(calls, 1)
+    ms = start.elapsed_time(stop) / args.steps
+    gbs_kernel = nbytes / (ms_kernel * 1e-3) / 1e9
+    line = {
+        "metric": "decode attention GB/s (algorithmic HBM bytes), 1 GPU", "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": name, "description": c.description, "bs": d.bs, "keys": d.num_keys,
+                   "algorithmic_mb": round(nbytes / 1e6, 2), "gflop": round(flops / 1e9, 3),
+                   "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(gbs_kernel, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
+                     "traffic": None, "ms_per_launch": round(ms_kernel, 4),
+                     "tflops": round(flops / (ms_kernel * 1e-3) / 1e12, 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        per_req = d.key_lens.astype(np.float64) * (c.hkv * (c.lq + (0 if c.v_aliases_k else c.lv)) * 2 + 8)
+        rng = np.random.default_rng(123)
+        order = rng.permutation(d.bs)
+        t0 = time.perf_counter()
+        oracle.decode_attention(d.q, d.k_pool, d.v_pool, d.kv_indptr, d.kv_indices, d.sm_scale, d.logit_cap,
+                                c.dtype, seqs=order[:1])
+        dt1 = max(time.perf_counter() - t0, 1e-6)
+        n = int(min(d.bs, max(1, args.cpu_seconds / dt1)))
+        t0 = time.perf_counter()
+        oracle.decode_attention(d.q, d.k_pool, d.v_pool, d.kv_indptr, d.kv_indices, d.sm_scale, d.logit_cap,
+                                c.dtype, seqs=order[:n])
+        dt = time.perf_counter() - t0
+        b = float(per_req[order[:n]].sum())
+        line["cpu_baseline"] = {"value": round(b / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+                                "kind": "oracle",
+                                "sample": f"{n} of {d.bs} requests (all heads), {b / 1e6:.0f} MB of K/V in {dt:.1f} s, "
+                                          "fp64 C loops with OpenMP"}
+    print(json.dumps(line), flush=True)
     return 0
 
 

@@ -307,7 +307,7 @@ int extend_attention_fwd_unified(const void* q_extend, void* o, const void* k_po
  *             desc->num_prefix_indices (the length of kv_indices).
  *  kv_indices int64[num_prefix_indices], each in [0, pool_slots).
  *  sm_scale, logit_cap: host floats as for extend_attention_fwd.
- *  desc       host pointer: dtype must be PKV_BF16; (lq, lv) one of (64, 64),
+ *  desc       host pointer: dtype must be PKV_BF16; bs <= 65535; (lq, lv) one of (64, 64),
  *             (128, 128), (256, 256), (192, 128), (288, 256), (576, 512);
  *             sliding_window and sinks are honoured, custom_mask must be NULL;
  *             total_q_tokens and the k/v_extend strides are not used.

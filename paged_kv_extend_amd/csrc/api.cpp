@@ -545,10 +545,12 @@ int extend_attention_fwd_unified(const void* q_extend, void* o, const void* k_po
 // ---------------------------------------------------------------- decode
 namespace {
 
-// Workgroups the decode launch aims at (MI355X: 256 CUs, one decode workgroup
-// per CU at a time, eight rounds), a function of the sizes only so that the
-// workspace size query and the call agree on any device.
-constexpr int64_t kDecodeTargetWgs = 2048;
+// Workgroups the decode launch aims at: MI355X has 256 CUs and a decode
+// workgroup fills one (its LDS ring), so one round of equal chunks streams
+// longest with the fewest pipeline fills and partial states (measured best
+// against 512 .. 2048).  A function of the sizes only, so that the workspace
+// size query and the call agree on any device.
+constexpr int64_t kDecodeTargetWgs = 256;
 constexpr int64_t kDecodeMinChunk = 128;
 constexpr int64_t kDecodeMaxChunk = 16384;
 constexpr int64_t kMaxGridY = 65535;
@@ -556,7 +558,7 @@ constexpr int64_t kMaxGridY = 65535;
 struct DecodeSizes {
   int hblocks, gh_count;
   int64_t chunk, chunks;
-  size_t vis, arrived, part_ml, part_acc, total;  // workspace offsets and size
+  size_t vis, part_ml, part_acc, total;  // workspace offsets and size
 };
 
 DecodeSizes decode_sizes(const pkv_attn_desc_t& d) {
@@ -576,8 +578,6 @@ DecodeSizes decode_sizes(const pkv_attn_desc_t& d) {
   size_t off = 0;
   z.vis = off;
   off = align_up(off + sizeof(int32_t) * (size_t)(d.bs + 1), 256);
-  z.arrived = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)d.bs * z.gh_count, 256);
   z.part_ml = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)rows, 256);
   z.part_acc = off;
@@ -604,6 +604,7 @@ int check_decode_desc(const pkv_attn_desc_t* d) {
     return fail(PKV_ERR_INVALID, "negative size (num_prefix_indices %lld, pool_slots %lld)",
                 (long long)d->num_prefix_indices, (long long)d->pool_slots);
   if (d->num_prefix_indices >= (1ll << 31)) return fail(PKV_ERR_UNSUPPORTED, "more than 2^31 - 1 keys");
+  if (d->bs > 65535) return fail(PKV_ERR_UNSUPPORTED, "decode batch of %d requests exceeds 65535", d->bs);
   if (d->num_prefix_indices > 0 && d->pool_slots <= 0)
     return fail(PKV_ERR_INVALID, "keys given but pool_slots is %lld", (long long)d->pool_slots);
   const int64_t strides[] = {d->q_stride_tok, d->q_stride_head, d->o_stride_tok, d->o_stride_head,
@@ -683,7 +684,6 @@ int decode_attention_fwd(const void* q, void* o, const void* k_pool, const void*
   a.cap_in = a.use_cap ? (float)(scale / logit_cap) : 0.0f;
   a.cap_out = a.use_cap ? (float)(logit_cap * log2e) : 0.0f;
   a.vis = reinterpret_cast<int32_t*>(ws + z.vis);
-  a.arrived = reinterpret_cast<int32_t*>(ws + z.arrived);
   a.part_ml = reinterpret_cast<float*>(ws + z.part_ml);
   a.part_acc = reinterpret_cast<float*>(ws + z.part_acc);
   const auto ev = profile_slot();

@@ -13,8 +13,7 @@
 // (2 (lq + lv) G flops per key and KV head), so the kernel is built to keep
 // HBM busy:
 //  * A plan launch (one workgroup) writes each request's first visible key in
-//    the concatenation of all requests' visible keys and clears the merge
-//    counters.  The attention launch cuts that concatenation into chunks of a
+//    the concatenation of all requests' visible keys.  The attention launch cuts that concatenation into chunks of a
 //    fixed number of keys: grid (KV head x head block, chunk), thousands of
 //    workgroups whatever the length mix, and a request longer than a chunk
 //    spreads over several.
@@ -31,8 +30,11 @@
 //    keys of one head, so a head's max and sum take two lane exchanges.
 //  * The four waves' states are merged through LDS; a request wholly inside
 //    the chunk is normalised and written out, otherwise the chunk writes its
-//    unnormalised state and the workgroup that brings a request's chunk count
-//    to its total merges all of them in chunk order (deterministic).
+//    unnormalised state, and a merge launch (a workgroup per request and head
+//    block, many in parallel) combines a request's chunks in chunk order
+//    (deterministic).  Keeping the merge out of the attention launch spares
+//    its workgroups the fences and counters, and a long request's many
+//    partial states are read by a whole workgroup instead of one straggler.
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -121,17 +123,6 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
     __syncthreads();
   }
   if (tid == 0) a.vis[a.bs] = carry;
-  const int64_t counters = (int64_t)a.bs * a.gh_count;
-  for (int64_t i = tid; i < counters; i += 1024) a.arrived[i] = 0;
-  // requests with no key: the output is zero (there is nothing to average)
-  const int hq = a.gh_count / a.hblocks * a.group;
-  for (int b = 0; b < a.bs; ++b) {
-    if (a.kv_indptr[b + 1] != a.kv_indptr[b]) continue;
-    for (int i = tid; i < hq * a.lv; i += 1024) {
-      const int h = i / a.lv, d = i % a.lv;
-      reinterpret_cast<__bf16*>(a.o)[(int64_t)b * a.o_st + (int64_t)h * a.o_sh + d] = (__bf16)0.0f;
-    }
-  }
 }
 
 // Partial-state slot of request b's piece of chunk c: every chunk holds at
@@ -148,7 +139,6 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
   constexpr int NDB = LV / 16;  // 16-column output blocks
   constexpr int NKK = LQ / 32;  // 32-dim slices of a K row
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
-  __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -221,19 +211,32 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
       auto issue_tile = [&](int t) {
         const int64_t* sl = reinterpret_cast<const int64_t*>(ring + (t % C::NSI) * C::SLOT_BYTES);
         char* st = wbase + (t % NS) * C::STAGE;
-#pragma unroll
-        for (int i = 0; i < C::K_LOADS; ++i) {
+        auto ksrc = [&](int i) {
           const unsigned f = 64u * i + lane, r = f / C::CK, p = f % C::CK;
-          const int64_t slot = sl[r];
-          const char* src = kbase + slot * a.kp_ss + (p ^ swz_k<C::CK>(r)) * 16u;
-          load_lds_16((gptr<void>)src, lds_addr(st + 1024 * i));
-        }
-#pragma unroll
-        for (int i = 0; i < C::V_LOADS; ++i) {
+          return kbase + sl[r] * a.kp_ss + (p ^ swz_k<C::CK>(r)) * 16u;
+        };
+        auto vsrc = [&](int i) {
           const unsigned f = 64u * i + lane, r = f / C::CV, p = f % C::CV;
-          const int64_t slot = sl[r];
-          const char* src = vbase + slot * a.vp_ss + (p ^ swz_v<C::CV>(r)) * 16u;
-          load_lds_16((gptr<void>)src, lds_addr(st + C::K_BYTES + 1024 * i));
+          return vbase + sl[r] * a.vp_ss + (p ^ swz_v<C::CV>(r)) * 16u;
+        };
+        if constexpr (C::K_LOADS + C::V_LOADS <= 18) {
+          // every row address first (one wait for the slot reads), then the loads
+          const char* ks[C::K_LOADS];
+          const char* vs[C::V_LOADS > 0 ? C::V_LOADS : 1];
+#pragma unroll
+          for (int i = 0; i < C::K_LOADS; ++i) ks[i] = ksrc(i);
+#pragma unroll
+          for (int i = 0; i < C::V_LOADS; ++i) vs[i] = vsrc(i);
+#pragma unroll
+          for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ks[i], lds_addr(st + 1024 * i));
+#pragma unroll
+          for (int i = 0; i < C::V_LOADS; ++i) load_lds_16((gptr<void>)vs[i], lds_addr(st + C::K_BYTES + 1024 * i));
+        } else {
+          // (too many loads to hold every address in registers)
+#pragma unroll
+          for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ksrc(i), lds_addr(st + 1024 * i));
+#pragma unroll
+          for (int i = 0; i < C::V_LOADS; ++i) load_lds_16((gptr<void>)vsrc(i), lds_addr(st + C::K_BYTES + 1024 * i));
         }
       };
 
@@ -280,17 +283,25 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
           mx = fmaxf(mx, x[i]);
         }
         mx = xor_max(xor_max(mx, 16), 32);
-        const float m_new = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - m_new);  // 0 on the first tile (m = -inf)
-        m = m_new;
+        // the reference max m is raised (and the state rescaled) only when a
+        // head's tile max exceeds it by more than 2^8: weights stay <= 2^8
+        const bool raise = mx > m + kRescaleSlack;  // always on the first tile (m = -inf)
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float m_new = raise ? mx : m;
+          const float alpha = fast_exp2(m - m_new);  // 1 for heads that keep m, 0 from m = -inf
+          lsum *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[db] = acc[db] * alpha;
+          m = m_new;
+        }
         bf16x4 pb;
         float psum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pb[i] = (__bf16)fast_exp2(x[i] - m_new);
+          pb[i] = (__bf16)fast_exp2(x[i] - m);
           psum += (float)pb[i];  // the sum adds the rounded weights that multiply V
         }
-        lsum = lsum * alpha + psum;
+        lsum += psum;
         const i16x4 pbi = __builtin_bit_cast(i16x4, pb);
         // O^T += V^T P^T: lane (in its group of 16) t16 reads row 4 j4 + t16 / 4 at
         // column 16 db + 4 (t16 % 4) and receives column 16 db + t16 of rows 4 j4 ..
@@ -306,7 +317,6 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
             addr = st + C::K_BYTES + vr * (C::CV * 16) + (vc ^ swz_v<C::CV>(vr)) * 16u + half8;
           }
           const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr<i16x4>)(addr));
-          acc[db] = acc[db] * alpha;
           acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pbi, acc[db], 0, 0, 0);
         }
       }
@@ -368,61 +378,79 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
       }
     }
 
-    if (!single) {
-      // count this chunk in; the workgroup that completes request b merges it.
-      // Release: the partial writes are visible device-wide before the count;
-      // acquire: the last one reads the others' after seeing the full count.
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) last_flag = atomicAdd(a.arrived + (int64_t)b * a.gh_count + gh, 1) == c1 - c0;
-      __syncthreads();
-      if (last_flag) {
-        __threadfence();
-        for (int idx = tid; idx < 16 * V4; idx += C::NT) {
-          const int row = idx / V4, d = 4 * (idx % V4);
-          if (hb * 16 + row >= G) continue;
-          float M = -INFINITY;
-          for (int cc = c0; cc <= c1; ++cc) {
-            const int64_t prow = (piece_slot(cc, v0, a.chunk) * a.gh_count + gh) * 16 + row;
-            M = fmaxf(M, a.part_ml[prow * 2]);
-          }
-          float L = 0.0f;
-          float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-          for (int cc = c0; cc <= c1; ++cc) {
-            const int64_t prow = (piece_slot(cc, v0, a.chunk) * a.gh_count + gh) * 16 + row;
-            const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
-            const float wt = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
-            L += ml.y * wt;
-            const float4 v = *reinterpret_cast<const float4*>(a.part_acc + prow * LV + d);
-            o.x += v.x * wt;
-            o.y += v.y * wt;
-            o.z += v.z * wt;
-            o.w += v.w * wt;
-          }
-          const int h = g * G + hb * 16 + row;
-          if (a.sinks) L += fast_exp2(a.sinks[h] * kLog2e - M);
-          const float inv = 1.0f / L;
-          bf16x4 ov;
-          ov[0] = (__bf16)(o.x * inv);
-          ov[1] = (__bf16)(o.y * inv);
-          ov[2] = (__bf16)(o.z * inv);
-          ov[3] = (__bf16)(o.w * inv);
-          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + (int64_t)b * a.o_st + (int64_t)h * a.o_sh + d) =
-              ov;
-        }
-      }
-    }
     barrier_fence();  // the merge area is the next piece's stages
   }
 }
 
+// Requests whose keys span several chunks: one workgroup per (head block,
+// 64-column slice, request) combines the chunks' states in chunk order
+// (deterministic):
+//   M = max_c m_c,  L = sum_c l_c 2^(m_c - M),  o = sum_c acc_c 2^(m_c - M) / L
+// plus the sink term.  Thread = (head row, 4 columns); the chunk loops are
+// unrolled so that several partial rows are in flight per thread.  A request
+// with no visible key gets a zero output here (there is nothing to average).
+constexpr int kMergeCols = 64;
+
+template <int LV>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int SLICES = LV / kMergeCols;
+  const int gh = blockIdx.x / SLICES, slice = blockIdx.x % SLICES, b = blockIdx.y;
+  const int g = gh / a.hblocks, hb = gh % a.hblocks, G = a.group;
+  const int row = threadIdx.x / (kMergeCols / 4), d = slice * kMergeCols + 4 * (threadIdx.x % (kMergeCols / 4));
+  if (hb * 16 + row >= G) return;
+  const int h = g * G + hb * 16 + row;
+  bf16x4* out = reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + (int64_t)b * a.o_st + (int64_t)h * a.o_sh + d);
+  const int v0 = a.vis[b], v1 = a.vis[b + 1];
+  if (v1 <= v0) {
+    *out = bf16x4{(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+    return;
+  }
+  const int c0 = v0 / a.chunk, c1 = (v1 - 1) / a.chunk;
+  if (c0 == c1) return;  // written by its only chunk
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int cc = c0; cc <= c1; ++cc) {
+    const int64_t prow = (piece_slot(cc, v0, a.chunk) * a.gh_count + gh) * 16 + row;
+    M = fmaxf(M, a.part_ml[prow * 2]);
+  }
+  float L = 0.0f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int cc = c0; cc <= c1; ++cc) {
+    const int64_t prow = (piece_slot(cc, v0, a.chunk) * a.gh_count + gh) * 16 + row;
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
+    const float wt = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
+    L += ml.y * wt;
+    const float4 v = *reinterpret_cast<const float4*>(a.part_acc + prow * LV + d);
+    o.x += v.x * wt;
+    o.y += v.y * wt;
+    o.z += v.z * wt;
+    o.w += v.w * wt;
+  }
+  if (a.sinks) L += fast_exp2(a.sinks[h] * kLog2e - M);
+  const float inv = 1.0f / L;
+  bf16x4 ov;
+  ov[0] = (__bf16)(o.x * inv);
+  ov[1] = (__bf16)(o.y * inv);
+  ov[2] = (__bf16)(o.z * inv);
+  ov[3] = (__bf16)(o.w * inv);
+  *out = ov;
+}
+
 template <int LQ, int LV, bool VK, int NW, int NS>
 hipError_t launch_decode_t(const DecodeArgs& a, int64_t chunks, hipStream_t s) {
-  const dim3 grid((unsigned)a.gh_count, (unsigned)chunks), block(DecCfg<LQ, LV, VK, NW, NS>::NT);
-  if (a.use_cap)
-    hipLaunchKernelGGL((decode_kernel<LQ, LV, VK, NW, NS, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<LQ, LV, VK, NW, NS, false>), grid, block, 0, s, a);
+  if (chunks > 0) {  // (no visible key at all: only the zero outputs of the merge launch)
+    const dim3 grid((unsigned)a.gh_count, (unsigned)chunks), block(DecCfg<LQ, LV, VK, NW, NS>::NT);
+    if (a.use_cap)
+      hipLaunchKernelGGL((decode_kernel<LQ, LV, VK, NW, NS, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<LQ, LV, VK, NW, NS, false>), grid, block, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  static_assert(LV % kMergeCols == 0, "merge slices");
+  hipLaunchKernelGGL(decode_merge_kernel<LV>, dim3((unsigned)(a.gh_count * (LV / kMergeCols)), (unsigned)a.bs),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -454,7 +482,7 @@ hipError_t launch_decode(int lq, int lv, bool v_in_k, const DecodeArgs& a, int64
                          hipEvent_t before, hipEvent_t after) {
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || chunks <= 0) return e;
+  if (e != hipSuccess) return e;
   if (before && (e = hipEventRecord(before, s)) != hipSuccess) return e;
   e = hipErrorInvalidValue;
 #define PKV_DL(Q, V, VK, NW, NS) \

@@ -208,14 +208,13 @@ struct DecodeArgs {
   float cap_in;      // scale / cap
   float cap_out;     // cap * log2(e)
   int32_t* vis;      // [bs + 1] first visible key of request b among all requests' visible keys
-  int32_t* arrived;  // [bs * gh_count] chunks of a split request whose state is written
   float* part_ml;    // [2 * chunks][gh_count][16][2]: max (base-2 units), sum of weights
   float* part_acc;   // [2 * chunks][gh_count][16][lv]
 };
 // (dtype, lq, lv, V inside K) served by the decode kernel; waves per workgroup.
 bool decode_supported(int dtype, int lq, int lv, bool v_in_k, int* waves);
-// Plan launch, then the attention launch over `chunks` chunks of a.chunk keys;
-// non-null events are recorded on s around the attention launch.
+// Plan launch, then the attention launch over `chunks` chunks of a.chunk keys
+// and the merge launch; non-null events are recorded on s around the last two.
 hipError_t launch_decode(int lq, int lv, bool v_in_k, const DecodeArgs& a, int64_t chunks, hipStream_t s,
                          hipEvent_t before, hipEvent_t after);
 
