@@ -26,7 +26,7 @@
 namespace pkv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBuckets = 256;
 constexpr int kMaxXcd = 8;
