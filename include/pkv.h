@@ -351,7 +351,8 @@ const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc, const void
  * Measurement hook (not needed for results).  pkv_profile_enable(1) clears
  * the record and makes every later extend_attention_fwd,
  * extend_attention_fwd_unified or decode_attention_fwd call record a HIP
- * event pair on its stream around its attention kernel; 0 stops recording.
+ * event pair on its stream around its attention kernel (for decode, its
+ * attention and merge launches); 0 stops recording.
  * pkv_profile_read waits for the recorded events and returns the summed
  * attention-kernel time in milliseconds and the number of calls.  The
  * record is process-wide and holds at most 4096 calls.

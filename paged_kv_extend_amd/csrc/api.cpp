@@ -39,6 +39,12 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kMinChunkTiles = 8;           // never split an item below this many KV tiles
 constexpr size_t kPartialBytes = 64u << 20;  // budget for split partial states
+// Items are cut into chunks of at most 1/kSplitRounds of the average work per
+// resident workgroup.  Finer cuts even out the CUs on paper (llama8b's
+// heaviest-first makespan is 13 % above the mean unsplit), but every extra
+// chunk reloads its Q rows and writes and merges 128 KB of fp32 state: on
+// one MI355X, 2 and 4 rounds made llama8b 10 % and 50 % slower.
+constexpr int kSplitRounds = 1;
 constexpr int kXcds = 8;                     // MI355X: 8 XCDs, workgroups dealt round-robin
 
 // V is the first lv columns of K (same base pointers and strides), as in the
@@ -447,6 +453,7 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   pa.bn = t.bn;
   pa.slots = resident_slots(d.dtype, d.lq, d.lv, vk, has_options(d));
   pa.min_chunk = kMinChunkTiles;
+  pa.rounds = kSplitRounds;
   pa.xcds = kXcds;
   pa.max_work = pb.max_work;
   pa.max_items = pb.max_items;
@@ -511,6 +518,9 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   }
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   if (ev.second) (void)hipEventRecord(ev.second, s);
+  // the chunks of split items, merged after the launch that wrote them
+  e = pkv::launch_split_merge(d.dtype, d.lv, pa.bm, a, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -455,7 +455,6 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
       }
     }
     if (hi == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref, l_tot);
-    finish_split<F32, LV>(a, it.merge, BM);
   }
 }
 
@@ -497,6 +496,22 @@ int occupancy_t() {
   X(true, 128, 128, 32, 1)
 
 }  // namespace
+
+hipError_t launch_split_merge(int dtype, int lv, int bm, const AttnArgs& a, hipStream_t s) {
+  const dim3 g(512), t(256);  // a grid stride over (merge record, row block) tasks
+  if (dtype == 1) {
+    if (lv == 64) hipLaunchKernelGGL((split_merge_kernel<true, 64>), g, t, 0, s, a, bm);
+    else if (lv == 128) hipLaunchKernelGGL((split_merge_kernel<true, 128>), g, t, 0, s, a, bm);
+    else return hipErrorInvalidValue;
+  } else {
+    if (lv == 64) hipLaunchKernelGGL((split_merge_kernel<false, 64>), g, t, 0, s, a, bm);
+    else if (lv == 128) hipLaunchKernelGGL((split_merge_kernel<false, 128>), g, t, 0, s, a, bm);
+    else if (lv == 256) hipLaunchKernelGGL((split_merge_kernel<false, 256>), g, t, 0, s, a, bm);
+    else if (lv == 512) hipLaunchKernelGGL((split_merge_kernel<false, 512>), g, t, 0, s, a, bm);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 bool attn_tiling(int dtype, int lq, int lv, Tiling* t) {
   const bool f32 = dtype == 1;

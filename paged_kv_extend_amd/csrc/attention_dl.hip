@@ -31,7 +31,6 @@
 //    "cpu_graph_runner.py", qkv_proj_with_rope: v = k.narrow(-1, 0, lv)), only
 //    the K tile is loaded and the V^T operand is read from it.
 #include "device_common.h"
-#include "merge_tile.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -629,7 +628,6 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
       }
     }
     if (hi == 0 && half == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref, l_tot);
-    finish_split<false, LV>(a, it.merge, BM);
   }
 }
 

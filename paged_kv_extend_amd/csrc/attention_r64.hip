@@ -23,7 +23,6 @@
 //    16 bytes per lane) with the XOR chunk swizzles that keep the MFMA operand
 //    reads and the transposing V reads free of bank conflicts.
 #include "device_common.h"
-#include "merge_tile.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -498,7 +497,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (hi == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref[rs], l_tot);
     }
   }
-  if (it.part >= 0) finish_split<false, D>(a, it.merge, BM);
 }
 
 template <int D, int BN>

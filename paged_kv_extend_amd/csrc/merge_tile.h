@@ -1,10 +1,15 @@
-// Merge of the chunks of a split item, fused into the attention kernels: the
-// workgroup that writes the last chunk's partial state combines all of them.
-//
-// In chunk order (deterministic, whichever chunk finishes last):
+// Merge of the chunks of split items, a launch of its own after the attention
+// launch.  In chunk order (deterministic):
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s acc_s 2^(m_s - M) / L
 // the log-sum-exp state merge (page "flashinfer_backend.py", forward_extend:
-// merge_state of the ragged and paged partial outputs).
+// merge_state of the ragged and paged partial outputs), plus the sink term.
+//
+// The attention launch only writes each chunk's partial state: on MI355X each
+// XCD has an L2 of its own, so a chunk that published its state to a merging
+// workgroup on another XCD inside the launch would need a device-scope
+// release (an L2 write-back) per chunk; the launch boundary orders the writes
+// for free.  A chunk's workgroup is then done as soon as its writes are
+// issued, and the merges run spread over every CU.
 #pragma once
 
 #include "device_common.h"
@@ -12,21 +17,29 @@
 
 namespace pkv {
 
-// Rows of split item mi from its partial states into o; thread = (row, 4 columns).
+// Work of the merge launch: (merge record, block of rows) tasks, strided over
+// the grid; thread = (row of the block, 4 columns).
 template <bool F32, int LV>
-__device__ void merge_tile(const AttnArgs& a, const MergeItem& mi, int bm, int tid, int nthreads) {
+__global__ __launch_bounds__(256) void split_merge_kernel(AttnArgs a, int bm) {
+  constexpr int V4 = LV / 4;          // float4 columns per row
+  constexpr int RPB = 256 / V4;       // rows per task
+  static_assert(256 % V4 == 0, "columns per thread block");
+  const int blocks = (bm + RPB - 1) / RPB;
+  const int tasks = a.hdr->num_merge * blocks;
+  const int row_in = threadIdx.x / V4, d = 4 * (threadIdx.x % V4);
   const int G = a.group;
-  const int q0 = a.qo_indptr[mi.b], E = a.qo_indptr[mi.b + 1] - q0;
-  const int R = E * G;
-  constexpr int V4 = LV / 4;
-  for (int idx = tid; idx < bm * V4; idx += nthreads) {
-    const int row = idx / V4, d = (idx % V4) * 4;
+  for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const MergeItem mi = a.merge[task / blocks];
+    const int row = (task % blocks) * RPB + row_in;
+    const int q0 = a.qo_indptr[mi.b], E = a.qo_indptr[mi.b + 1] - q0;
     const int r = mi.t * bm + row;
-    if (r >= R) continue;
+    if (row >= bm || r >= E * G) continue;
     float M = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < mi.n; ++s) M = fmaxf(M, a.part_ml[((int64_t)(mi.part_base + s) * bm + row) * 2]);
     float L = 0.0f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int s = 0; s < mi.n; ++s) {
       const int64_t prow = (int64_t)(mi.part_base + s) * bm + row;
       const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
@@ -54,26 +67,6 @@ __device__ void merge_tile(const AttnArgs& a, const MergeItem& mi, int bm, int t
       *reinterpret_cast<bf16x4*>(reinterpret_cast<uint16_t*>(a.o) + off) = ov;
     }
   }
-}
-
-// Called by every thread of a workgroup after it wrote the partial state of
-// one chunk of split item a.merge[merge_index]: the chunks count themselves
-// in, and the workgroup that brings the count to n merges them.  Release:
-// each workgroup's partial writes are visible device-wide before its count;
-// acquire: the last one reads the others' after seeing the full count.
-template <bool F32, int LV>
-__device__ void finish_split(const AttnArgs& a, int merge_index, int bm) {
-  __shared__ int last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int n = a.merge[merge_index].n;
-    last = atomicAdd(&a.merge[merge_index].arrived, 1) == n - 1;
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  merge_tile<F32, LV>(a, a.merge[merge_index], bm, threadIdx.x, blockDim.x);
 }
 
 }  // namespace pkv

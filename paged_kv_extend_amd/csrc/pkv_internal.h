@@ -24,7 +24,7 @@ struct WorkItem {
 // A split item whose chunks occupy partial slots [part_base, part_base + n).
 struct MergeItem {
   int32_t b, g, t, part_base, n;
-  int32_t arrived;  // chunks whose partial state is written (zeroed by the planner)
+  int32_t pad2;
   int32_t pad0, pad1;
 };
 
@@ -104,6 +104,7 @@ struct PlanArgs {
   int32_t bs, num_kv_heads, group, bm, bn;
   int32_t slots;          // workgroups resident at once on the device
   int32_t min_chunk;      // never split below this many KV tiles
+  int32_t rounds;         // chunk limit = average work per resident workgroup / rounds
   int32_t xcds;           // XCDs to spread work over (workgroup i runs on XCD i mod xcds)
   int64_t max_items, part_budget, max_merge;
   int64_t max_work;       // grid size: slots available for work items
@@ -156,6 +157,8 @@ bool attn_tiling(int dtype, int lq, int lv, Tiling* t);
 hipError_t launch_attention(int dtype, int lq, int lv, const AttnArgs& a, int64_t grid,
                             hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+// Merge of the chunks of split items (after the attention launch; bm = rows per item).
+hipError_t launch_split_merge(int dtype, int lv, int bm, const AttnArgs& a, hipStream_t s);
 // KV-cache store: byte strides; ck / cv = 16-byte chunks of a K / V row
 // (cv = 0 when V lies inside K and is stored with it); rows = tokens * hkv.
 struct StoreArgs {

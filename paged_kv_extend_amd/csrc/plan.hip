@@ -198,9 +198,11 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   }
   const int64_t total = block_sum(my_total, sh);
 
-  // 3. chunk limit: one average share per resident workgroup, grown until the
-  //    split chunks fit the partial-state budget
-  int64_t chunk = (total + a.slots - 1) / a.slots;
+  // 3. chunk limit: a 1/rounds share of the average work per resident
+  //    workgroup (so that heaviest-first placement can even out the CUs),
+  //    grown until the split chunks fit the partial-state budget
+  const int64_t shares = (int64_t)a.slots * (a.rounds > 0 ? a.rounds : 1);
+  int64_t chunk = (total + shares - 1) / shares;
   if (chunk < a.min_chunk) chunk = a.min_chunk;
   for (;;) {
     int64_t parts = 0;
@@ -259,14 +261,16 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     for (int i = 0; i < kMaxXcd - 1; ++i) x += (i < X - 1 && mid2 >= bnd2[i]) ? 1 : 0;
     return x;
   };
-  // tile range of chunk s of k over c tiles
+  // tile range of chunk s of k over c tiles: full chunks of `chunk` tiles and
+  // the remainder last (chunks of mixed sizes let the heaviest-first
+  // placement fill the last round, where equal pieces would quantise it)
   auto chunk_range = [&](int c, int s, int k, int& k0, int& k1) {
     if (k == 1) {
       k0 = 0;
       k1 = c;
     } else {
-      k0 = (int)((int64_t)c * s / k);
-      k1 = (int)((int64_t)c * (s + 1) / k);
+      k0 = (int)(s * chunk);
+      k1 = min(c, (int)((s + 1) * chunk));
     }
   };
   constexpr int kPer = kMaxXcd * kBuckets / kThreads;  // counters per thread in the scan
@@ -357,7 +361,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
         m.t = itt;
         m.part_base = pbase;
         m.n = k;
-        m.arrived = 0;
+        m.pad2 = 0;
         m.pad0 = m.pad1 = 0;
         a.merge[midx] = m;
       }
