@@ -303,9 +303,12 @@ int extend_attention_fwd_unified(const void* q_extend, void* o, const void* k_po
  *  k_pool, v_pool: as in pkv_attn_desc_t; v_pool may be the first lv columns
  *             of k_pool (same base and strides; required for lq 576 / lv 512
  *             unless v_pool is a pool of its own).
- *  kv_indptr  int32[bs+1], non-decreasing; kv_indptr[bs] - kv_indptr[0] ==
- *             desc->num_prefix_indices (the length of kv_indices).
- *  kv_indices int64[num_prefix_indices], each in [0, pool_slots).
+ *  kv_indptr  int32[bs+1], non-decreasing, need not start at 0;
+ *             desc->num_prefix_indices >= kv_indptr[bs] - kv_indptr[0] (the
+ *             keys of the batch; a larger value only enlarges the launch and
+ *             the workspace, a smaller one leaves keys unread).
+ *  kv_indices int64, read at [kv_indptr[0], kv_indptr[bs]), each in
+ *             [0, pool_slots).
  *  sm_scale, logit_cap: host floats as for extend_attention_fwd.
  *  desc       host pointer: dtype must be PKV_BF16; bs <= 65535; (lq, lv) one of (64, 64),
  *             (128, 128), (256, 256), (192, 128), (288, 256), (576, 512);

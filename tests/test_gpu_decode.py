@@ -132,3 +132,51 @@ def test_decode_full_size(name):
     assert np.isfinite(got).all()
     # every request at full size (the oracle finishes these in seconds)
     check(got, oracle_decode(d), "bf16", f"{name} full")
+
+
+def test_decode_many_requests_and_offset_indptr():
+    # more requests than one pass of the plan launch's scan (1024), and an
+    # index array that starts past the first entry of kv_indices
+    rng = np.random.default_rng(41)
+    lens = rng.integers(0, 40, 2500)
+    d = wl.decode_custom(lens.tolist(), hq=8, hkv=2, lq=64, lv=64, seed=41)
+    want = oracle_decode(d)
+    dev = wl.decode_to_torch(d)
+    pad = 5
+    dev["kv_indices"] = torch.cat([torch.zeros(pad, dtype=torch.int64, device="cuda"), dev["kv_indices"]])
+    dev["kv_indptr"] = dev["kv_indptr"] + pad
+    pkv.decode_attention_fwd(dev["q"], dev["o"], dev["k_pool"], dev["v_pool"], dev["kv_indptr"],
+                             dev["kv_indices"][:].contiguous())
+    torch.cuda.synchronize()
+    check(out_f64(dev), want, "bf16", "2500 requests, offset indptr")
+
+
+def test_decode_graph_replay():
+    # the decode launches record no memset, so a captured call replays as run
+    d = wl.decode_custom([300, 7, 1200, 0, 64], hq=16, hkv=4, lq=128, lv=128, seed=43)
+    dev = wl.decode_to_torch(d)
+    desc = pkv.make_desc(dev["q"], None, None, dev["o"], dev["k_pool"], dev["v_pool"], d.bs, d.num_keys)
+    ws = torch.empty(pkv.decode_attention_workspace_size(desc), dtype=torch.uint8, device="cuda")
+
+    def call():
+        pkv.decode_attention_fwd(dev["q"], dev["o"], dev["k_pool"], dev["v_pool"], dev["kv_indptr"],
+                                 dev["kv_indices"], workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = dev["o"].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        dev["o"].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dev["o"], eager)
+        call()  # eager work between the replays
+        torch.cuda.synchronize()
