@@ -102,7 +102,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
     int v = 0;
     if (b < a.bs) {
       const int n = a.kv_indptr[b + 1] - a.kv_indptr[b];
-      v = (a.window > 0 && n > a.window + 1) ? a.window + 1 : n;
+      v = (a.window > 0 && n - 1 > a.window) ? a.window + 1 : n;  // (no overflow at any window)
     }
     int x = v;  // inclusive scan over the wave
 #pragma unroll

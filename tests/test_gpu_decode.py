@@ -180,3 +180,10 @@ def test_decode_graph_replay():
         assert torch.equal(dev["o"], eager)
         call()  # eager work between the replays
         torch.cuda.synchronize()
+
+
+def test_decode_widest_window_is_no_window():
+    d = wl.decode_custom([5, 300, 0, 2000], hq=8, hkv=2, lq=128, lv=128, seed=47)
+    plain = run_decode(d)["o"].clone()
+    widest = run_decode(d, window=2**31 - 1)["o"]
+    assert torch.equal(plain, widest)
