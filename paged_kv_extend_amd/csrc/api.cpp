@@ -685,7 +685,6 @@ int decode_attention_fwd(const void* q, void* o, const void* k_pool, const void*
   a.bs = d.bs;
   a.group = d.num_q_heads / d.num_kv_heads;
   a.hblocks = z.hblocks;
-  a.lv = d.lv;
   a.gh_count = z.gh_count;
   a.chunk = (int32_t)z.chunk;
   a.window = d.sliding_window > 0 ? d.sliding_window : 0;

@@ -202,7 +202,7 @@ struct DecodeArgs {
   const float* sinks;         // [num_q_heads] sink logits (natural units), or NULL
   int64_t q_st, q_sh, o_st, o_sh;
   int64_t kp_ss, kp_sh, vp_ss, vp_sh;  // BYTES
-  int32_t bs, group, hblocks, lv;
+  int32_t bs, group, hblocks;
   int32_t gh_count;  // num_kv_heads * hblocks: the x extent of the grid
   int32_t chunk;     // keys per chunk (a multiple of 64)
   int32_t window;    // > 0: only the last window + 1 keys of a request are seen
