@@ -53,6 +53,8 @@ def parse():
                          "runs beside it); unified: attention reads every key through the index build's output")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attention_traffic.json"),
                     help="HBM bytes per attention launch measured with rocprofv3 counters")
+    ap.add_argument("--decode-traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"),
+                    help="HBM bytes per decode call (attention + merge launches) measured with rocprofv3 counters")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -313,6 +315,12 @@ def bench_decode(args, dev, torch, pkv):
     ms_kernel = kern_ms / max(calls, 1)
     ms = start.elapsed_time(stop) / args.steps
     gbs_kernel = nbytes / (ms_kernel * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.decode_traffic_json):
+        with open(args.decode_traffic_json) as f:
+            tj = json.load(f)
+        if tj.get("workload") == name and tj.get("kernel_source_sha") == kernel_source_sha(DECODE_SOURCES):
+            traffic = tj.get("bytes_per_launch")
     line = {
         "metric": "decode attention GB/s (algorithmic HBM bytes), 1 GPU", "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -322,7 +330,7 @@ def bench_decode(args, dev, torch, pkv):
                    "input_copies_rotated": copies},
         "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(gbs_kernel, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
-                     "traffic": None, "ms_per_launch": round(ms_kernel, 4),
+                     "traffic": traffic, "ms_per_launch": round(ms_kernel, 4),
                      "tflops": round(flops / (ms_kernel * 1e-3) / 1e12, 2)},
     }
     if not args.no_cpu_baseline:
@@ -349,12 +357,16 @@ def bench_decode(args, dev, torch, pkv):
     return 0
 
 
-def kernel_source_sha():
+ATTENTION_SOURCES = ("device_common.h", "pkv_internal.h", "attention.hip", "attention_dl.hip", "attention_r64.hip",
+                     "plan.hip")
+DECODE_SOURCES = ("device_common.h", "pkv_internal.h", "decode.hip")
+
+
+def kernel_source_sha(files=ATTENTION_SOURCES):
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("device_common.h", "pkv_internal.h", "attention.hip", "attention_dl.hip", "attention_r64.hip",
-              "plan.hip"):
+    for f in files:
         with open(os.path.join(ROOT, "paged_kv_extend_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
