@@ -13,11 +13,11 @@
 // (2 (lq + lv) G flops per key and KV head), so the kernel is built to keep
 // HBM busy:
 //  * A plan launch (one workgroup) writes each request's first visible key in
-//    the concatenation of all requests' visible keys.  The attention launch cuts that concatenation into chunks of a
-//    fixed number of keys: grid (KV head x head block, chunk), thousands of
-//    workgroups whatever the length mix, and a request longer than a chunk
-//    spreads over several.
-//  * Inside a workgroup each of the four waves streams its own contiguous
+//    the concatenation of all requests' visible keys.  The attention launch
+//    cuts that concatenation into equal chunks of keys: grid (KV head x head
+//    block, chunk), sized on the host to about one workgroup per CU whatever
+//    the length mix; a request longer than a chunk spreads over several.
+//  * Inside a workgroup each of the (usually four) waves streams its own contiguous
 //    share of the chunk's keys, 16 keys per tile, through a ring of LDS stages
 //    filled by global-to-LDS loads (16 bytes per lane, whole rows per group of
 //    lanes).  The slots of later tiles come into LDS the same way, far enough
@@ -30,9 +30,10 @@
 //    keys of one head, so a head's max and sum take two lane exchanges.
 //  * The four waves' states are merged through LDS; a request wholly inside
 //    the chunk is normalised and written out, otherwise the chunk writes its
-//    unnormalised state, and a merge launch (a workgroup per request and head
-//    block, many in parallel) combines a request's chunks in chunk order
-//    (deterministic).  Keeping the merge out of the attention launch spares
+//    unnormalised state, and a merge launch (a workgroup per request, head
+//    block and 64-column slice, many in parallel) combines a request's chunks
+//    in chunk order (deterministic) and writes zeros for requests without
+//    keys.  Keeping the merge out of the attention launch spares
 //    its workgroups the fences and counters, and a long request's many
 //    partial states are read by a whole workgroup instead of one straggler.
 #include "device_common.h"
