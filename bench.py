@@ -166,8 +166,11 @@ def main():
     ms_per_step = start.elapsed_time(stop) / args.steps
     ms_attn = attn_ms_total / max(calls, 1)
 
-    achieved = flops / (ms_attn * 1e-3) / 1e12
     peak = PEAK[w.cfg.dtype]
+    # the kernel's bound: products above the ridge (peak flop/s over HBM
+    # bytes/s), HBM below it (short extends over long prefixes)
+    hbm_bound = flops / algo_bytes < peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    achieved = flops / (ms_attn * 1e-3) / 1e12
     traffic = None
     if os.path.exists(args.traffic_json):
         with open(args.traffic_json) as f:
@@ -194,10 +197,15 @@ def main():
                    "causal_gflop": round(flops / 1e9, 3), "algorithmic_mb": round(algo_bytes / 1e6, 2),
                    "input_copies_rotated": copies, "wall_s_timed": round(wall, 3), "path": args.path},
         "mfma_frac_step": round(flops / (ms_per_step * 1e-3) / 1e12 / peak, 4),
-        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "ms_per_launch": round(ms_attn, 4),
-                     "hbm_gbs_algorithmic": round(algo_bytes / (ms_attn * 1e-3) / 1e9, 1)},
+        "roofline": ({"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2),
+                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                      "traffic": traffic, "ms_per_launch": round(ms_attn, 4),
+                      "hbm_gbs_algorithmic": round(algo_bytes / (ms_attn * 1e-3) / 1e9, 1)} if not hbm_bound else
+                     {"bound": "hbm", "kernel": kernel, "achieved": round(algo_bytes / (ms_attn * 1e-3) / 1e9, 1),
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(algo_bytes / (ms_attn * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "traffic": traffic, "ms_per_launch": round(ms_attn, 4),
+                      "tflops": round(achieved, 2)}),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -154,7 +154,7 @@ def test_every_kernel_on_one_batch(kernel):
 
 # ---- full sizes, sampled rows, same launch path as the benchmark
 
-@pytest.mark.parametrize("name", wl.CONFIG_ORDER)
+@pytest.mark.parametrize("name", wl.CONFIG_ORDER + wl.AUX_CONFIGS)
 def test_parity_full_size_sampled(name):
     w = wl.get(name)
     rows = sample_rows(w)

@@ -128,6 +128,16 @@ CONFIGS = {
 
 CONFIG_ORDER = ["tiny_fp32", "llama8b", "long_prefix", "mla", "skewed_cap"]
 
+# Auxiliary: the long-prefix batch with 16 new tokens per sequence, the shape
+# where extend attention is bound by HBM rather than by the products
+# (~111 flop per algorithmic byte against the MI355X ridge of ~312).
+CONFIGS["long_prefix_e16"] = Config(
+    "long_prefix_e16", "bf16", bs=4, hq=28, hkv=4, lq=128, lv=128, pool_slots=131072, std=1.0,
+    sm_scale=0.0, logit_cap=0.0, seed=1006,
+    prefix_lens=_fixed([16384] * 4), extend_lens=_fixed([16] * 4),
+    description="long prefix, short extend (HBM-bound): bs 4, 28/4 heads, D 128, P 16384, E 16")
+AUX_CONFIGS = ["long_prefix_e16"]
+
 
 @dataclasses.dataclass
 class Workload:
