@@ -93,7 +93,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(sharding is described in DESIGN.md, not run).", file=sys.stderr)
+              "(the path runs on one GPU; sharding across GPUs is not built).", file=sys.stderr)
         return 2
 
     import torch
