@@ -310,10 +310,15 @@ int extend_attention_fwd_unified(const void* q_extend, void* o, const void* k_po
  *  kv_indices int64, read at [kv_indptr[0], kv_indptr[bs]), each in
  *             [0, pool_slots).
  *  sm_scale, logit_cap: host floats as for extend_attention_fwd.
- *  desc       host pointer: dtype must be PKV_BF16; bs <= 65535; (lq, lv) one of (64, 64),
- *             (128, 128), (256, 256), (192, 128), (288, 256), (576, 512);
- *             sliding_window and sinks are honoured, custom_mask must be NULL;
- *             total_q_tokens and the k/v_extend strides are not used.
+ *  desc       host pointer: bs <= 65535; sliding_window and sinks are
+ *             honoured, custom_mask must be NULL; total_q_tokens and the
+ *             k/v_extend strides are not used.  The decode kernels serve
+ *             PKV_BF16 with (lq, lv) one of (64, 64), (128, 128), (256, 256),
+ *             (192, 128), (288, 256), (576, 512); any other batch that
+ *             extend_attention_fwd_unified serves (PKV_FP32, other head
+ *             dims) runs as that call with one new token per request whose
+ *             prefix is every earlier key, under the same rule as above and
+ *             the extend limits on dtype, head dims and strides.
  *  workspace  device buffer of >= decode_attention_workspace_size(desc)
  *             bytes, 256-byte aligned, no initialisation needed; calls that
  *             overlap in time must use different workspaces.

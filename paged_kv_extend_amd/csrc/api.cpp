@@ -596,19 +596,37 @@ DecodeSizes decode_sizes(const pkv_attn_desc_t& d) {
   return z;
 }
 
+// Whether a decode kernel variant serves the batch (bf16, listed head dims).
+bool decode_kernel_serves(const pkv_attn_desc_t& d) {
+  int waves = 0;
+  return pkv::decode_supported(d.dtype, d.lq, d.lv, false, &waves) ||
+         pkv::decode_supported(d.dtype, d.lq, d.lv, true, &waves);
+}
+
+// A decode batch that no decode kernel serves (fp32, other head dims) runs as
+// the unified extend of one new token per request whose prefix is every
+// earlier key, all of them read through kv_indices.
+pkv_attn_desc_t decode_as_extend(const pkv_attn_desc_t& d) {
+  pkv_attn_desc_t e = d;
+  e.total_q_tokens = d.bs;
+  e.ke_stride_tok = e.ke_stride_head = e.ve_stride_tok = e.ve_stride_head = 0;
+  return e;
+}
+
+// Bytes before the extend workspace on that route: qo_indptr[bs + 1] and
+// prefix_lens[bs].
+size_t decode_rows_bytes(const pkv_attn_desc_t& d) {
+  return align_up(sizeof(int32_t) * (size_t)(2 * (int64_t)d.bs + 1), 256);
+}
+
 int check_decode_desc(const pkv_attn_desc_t* d) {
   if (!d) return fail(PKV_ERR_INVALID, "desc is NULL");
-  if (d->dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "decode attention serves bf16 only (dtype %d)", d->dtype);
   if (d->bs < 0) return fail(PKV_ERR_INVALID, "bs %d < 0", d->bs);
   if (d->num_q_heads <= 0 || d->num_kv_heads <= 0)
     return fail(PKV_ERR_INVALID, "head counts must be positive (%d, %d)", d->num_q_heads, d->num_kv_heads);
   if (d->num_q_heads % d->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
                 d->num_kv_heads);
-  int waves = 0;
-  if (!pkv::decode_supported(d->dtype, d->lq, d->lv, false, &waves) &&
-      !pkv::decode_supported(d->dtype, d->lq, d->lv, true, &waves))
-    return fail(PKV_ERR_UNSUPPORTED, "head dims (lq %d, lv %d) not supported for decode", d->lq, d->lv);
   if (d->custom_mask) return fail(PKV_ERR_UNSUPPORTED, "decode attention takes no custom mask");
   if (d->num_prefix_indices < 0 || d->pool_slots < 0)
     return fail(PKV_ERR_INVALID, "negative size (num_prefix_indices %lld, pool_slots %lld)",
@@ -617,6 +635,12 @@ int check_decode_desc(const pkv_attn_desc_t* d) {
   if (d->bs > 65535) return fail(PKV_ERR_UNSUPPORTED, "decode batch of %d requests exceeds 65535", d->bs);
   if (d->num_prefix_indices > 0 && d->pool_slots <= 0)
     return fail(PKV_ERR_INVALID, "keys given but pool_slots is %lld", (long long)d->pool_slots);
+  if (!decode_kernel_serves(*d)) {
+    // the extend kernels' own limits (dtype, head dims, strides) apply
+    pkv::Tiling t;
+    const pkv_attn_desc_t e = decode_as_extend(*d);
+    return check_desc(&e, &t);
+  }
   const int64_t strides[] = {d->q_stride_tok, d->q_stride_head, d->o_stride_tok, d->o_stride_head,
                              d->kp_stride_slot, d->kp_stride_head, d->vp_stride_slot, d->vp_stride_head};
   for (int64_t s : strides)
@@ -631,6 +655,10 @@ extern "C" {
 size_t decode_attention_workspace_size(const pkv_attn_desc_t* desc) {
   if (check_decode_desc(desc) != PKV_OK) return 0;
   g_err[0] = '\0';
+  if (!decode_kernel_serves(*desc)) {
+    const pkv_attn_desc_t e = decode_as_extend(*desc);
+    return decode_rows_bytes(*desc) + extend_attention_workspace_size(&e);
+  }
   return decode_sizes(*desc).total;
 }
 
@@ -649,6 +677,31 @@ int decode_attention_fwd(const void* q, void* o, const void* k_pool, const void*
   const void* ptrs[] = {q, o, k_pool, v_pool};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(PKV_ERR_UNSUPPORTED, "tensor base pointers must be 16-byte aligned");
+  if (!decode_kernel_serves(d)) {
+    const pkv_attn_desc_t e = decode_as_extend(d);
+    const size_t rows = decode_rows_bytes(d);
+    const size_t need = rows + extend_attention_workspace_size(&e);
+    g_err[0] = '\0';
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                  need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    int32_t* qo_indptr = static_cast<int32_t*>(workspace);
+    int32_t* prefix_lens = qo_indptr + d.bs + 1;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e1 = pkv::launch_decode_rows(kv_indptr, d.bs, qo_indptr, prefix_lens, s);
+    if (e1 != hipSuccess) return fail(PKV_ERR_HIP, "decode rows launch: %s", hipGetErrorString(e1));
+    rc = attention_call(q, nullptr, nullptr, o, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, prefix_lens,
+                        sm_scale, logit_cap, &e, static_cast<char*>(workspace) + rows, workspace_bytes - rows,
+                        stream);
+    if (rc != PKV_OK) return rc;
+    // a request without keys has no visible key: its output row is zero
+    e1 = pkv::launch_decode_zero_empty(kv_indptr, d.bs, d.num_q_heads, d.lv, d.dtype == PKV_FP32 ? 4 : 2, o,
+                                       d.o_stride_tok, d.o_stride_head, s);
+    if (e1 != hipSuccess) return fail(PKV_ERR_HIP, "decode zero launch: %s", hipGetErrorString(e1));
+    return ok();
+  }
   // V inside K: the variant that reads V out of the K tile when there is one;
   // the general variant reads the same rows twice otherwise
   int waves = 0;

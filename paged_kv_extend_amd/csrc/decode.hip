@@ -465,7 +465,44 @@ hipError_t launch_decode_t(const DecodeArgs& a, int64_t chunks, hipStream_t s) {
   X(576, 512, true, 4, 2)        \
   X(576, 512, false, 2, 2)
 
+// fp32 decode runs as the unified extend of one new token per request whose
+// prefix is every earlier key: these two kernels write its row arrays and
+// give requests without keys their zero output afterwards.
+__global__ __launch_bounds__(256) void decode_rows_kernel(const int32_t* kv_indptr, int32_t bs, int32_t* qo_indptr,
+                                                           int32_t* prefix_lens) {
+  for (int b = blockIdx.x * 256 + threadIdx.x; b <= bs; b += gridDim.x * 256) {
+    qo_indptr[b] = b;
+    if (b < bs) prefix_lens[b] = max(kv_indptr[b + 1] - kv_indptr[b] - 1, 0);
+  }
+}
+__global__ __launch_bounds__(256) void decode_zero_empty_kernel(const int32_t* kv_indptr, int32_t hq, int32_t lv,
+                                                                 int32_t elem_bytes, char* o, int64_t o_st,
+                                                                 int64_t o_sh) {
+  const int b = blockIdx.x;
+  if (kv_indptr[b + 1] != kv_indptr[b]) return;
+  for (int i = threadIdx.x; i < hq * lv; i += 256) {
+    char* e = o + ((int64_t)b * o_st + (int64_t)(i / lv) * o_sh + i % lv) * elem_bytes;
+    if (elem_bytes == 4) *reinterpret_cast<float*>(e) = 0.0f;
+    else *reinterpret_cast<uint16_t*>(e) = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_decode_rows(const int32_t* kv_indptr, int32_t bs, int32_t* qo_indptr, int32_t* prefix_lens,
+                              hipStream_t s) {
+  const unsigned grid = (unsigned)((bs + 1 + 255) / 256 < 1024 ? (bs + 1 + 255) / 256 : 1024);
+  hipLaunchKernelGGL(decode_rows_kernel, dim3(grid), dim3(256), 0, s, kv_indptr, bs, qo_indptr, prefix_lens);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_zero_empty(const int32_t* kv_indptr, int32_t bs, int32_t hq, int32_t lv, int32_t elem_bytes,
+                                    void* o, int64_t o_st, int64_t o_sh, hipStream_t s) {
+  if (bs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_zero_empty_kernel, dim3((unsigned)bs), dim3(256), 0, s, kv_indptr, hq, lv, elem_bytes,
+                     static_cast<char*>(o), o_st, o_sh);
+  return hipGetLastError();
+}
 
 bool decode_supported(int dtype, int lq, int lv, bool v_in_k, int* waves) {
   if (dtype != 0) return false;

@@ -216,6 +216,12 @@ struct DecodeArgs {
 };
 // (dtype, lq, lv, V inside K) served by the decode kernel; waves per workgroup.
 bool decode_supported(int dtype, int lq, int lv, bool v_in_k, int* waves);
+// fp32 decode through the unified extend: row arrays (qo_indptr[b] = b,
+// prefix_lens[b] = keys - 1) and, afterwards, zero outputs of keyless requests.
+hipError_t launch_decode_rows(const int32_t* kv_indptr, int32_t bs, int32_t* qo_indptr, int32_t* prefix_lens,
+                              hipStream_t s);
+hipError_t launch_decode_zero_empty(const int32_t* kv_indptr, int32_t bs, int32_t hq, int32_t lv, int32_t elem_bytes,
+                                    void* o, int64_t o_st, int64_t o_sh, hipStream_t s);
 // Plan launch, then the attention launch over `chunks` chunks of a.chunk keys
 // and the merge launch; non-null events are recorded on s around the last two.
 hipError_t launch_decode(int lq, int lv, bool v_in_k, const DecodeArgs& a, int64_t chunks, hipStream_t s,

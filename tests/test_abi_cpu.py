@@ -206,8 +206,10 @@ def test_decode_workspace_size_grows_with_keys():
 
 
 @pytest.mark.parametrize("kw,needle", [
-    (dict(dtype=1), "bf16"),
+    (dict(dtype=2), "dtype"),
     (dict(lq=80, lv=80), "not supported"),
+    (dict(dtype=1, lq=256, lv=256), "not supported"),  # fp32 extend kernels serve 64 and 128 only
+    (dict(dtype=1, kp_stride_slot=1002), "stride"),
     (dict(num_q_heads=30), "multiple"),
     (dict(bs=-1), "bs"),
     (dict(kp_stride_slot=1001), "stride"),
@@ -223,7 +225,13 @@ def test_decode_workspace_size_rejects(kw, needle):
 
 def test_decode_argument_errors_without_device():
     assert call_decode(None) == -1
-    assert call_decode(decode_desc(dtype=1, lq=64, lv=64)) == -2
+    assert call_decode(decode_desc(dtype=1, lq=80, lv=80)) == -2
+    # fp32 runs as a unified extend: its workspace is the extend workspace plus the row arrays
+    f32 = decode_desc(dtype=1)
+    ext = decode_desc(dtype=1, total_q_tokens=4)
+    assert pkv.decode_attention_workspace_size(f32) >= pkv.extend_attention_workspace_size(ext) + 256
+    assert call_decode(f32, ws_bytes=pkv.decode_attention_workspace_size(f32) - 256) == -3
+    assert call_decode(f32, ws=4096 + 64) == -3
     assert call_decode(decode_desc(), ws_bytes=16) == -3
     assert call_decode(decode_desc(), ws=4096 + 64) == -3
     assert call_decode(decode_desc(), ptr=4100) == -2

@@ -187,3 +187,19 @@ def test_decode_widest_window_is_no_window():
     plain = run_decode(d)["o"].clone()
     widest = run_decode(d, window=2**31 - 1)["o"]
     assert torch.equal(plain, widest)
+
+
+# fp32 batches run as the unified extend of one new token per request
+@pytest.mark.parametrize("dims", [64, 128])
+@pytest.mark.parametrize("opt", ["plain", "window+sinks+cap"])
+def test_decode_fp32(dims, opt):
+    kw = dict(hq=8, hkv=2, lq=dims, lv=dims, dtype="fp32")
+    window, sinks = 0, None
+    if opt != "plain":
+        window, kw["logit_cap"] = 37, 5.0
+        sinks = np.linspace(1.0, -1.0, 8).astype(np.float32)
+    d = wl.decode_custom(LENS, seed=53, **kw)
+    dev = wl.decode_to_torch(d)
+    dev["o"].fill_(float("nan"))  # rows of keyless requests are written too
+    run_decode(d, dev, window=window, sinks=sinks)
+    check(out_f64(dev), oracle_decode(d, window=window, sinks=sinks), "fp32", f"fp32 {dims} {opt}")
