@@ -116,3 +116,59 @@ def test_unified_full_size_sampled(name):
     got = out_f64(dev)
     assert np.isfinite(got).all(), "non-finite outputs"
     check(got[rows], oracle_unified(w, *arrays, rows=rows), w.cfg.dtype, f"{name}-unified-sampled")
+
+
+def test_graph_replay_index_build_and_both_entries():
+    # the index build, a two-part call with split chunks (one long prefix)
+    # and a unified call over the built arrays, captured in one HIP graph:
+    # their launches record no memset, so every replay equals the eager run
+    w = wl.custom(dtype="bf16", prefix_lens=[20000, 300, 0, 77], extend_lens=[3, 200, 64, 1], hq=8, hkv=2,
+                  lq=128, lv=128, seed=71)
+    dev = wl.to_torch(w)
+    n_u = dev["kv_indices"].numel() + dev["extend_kv_indices"].numel()
+    uni = (torch.empty(w.bs + 1, dtype=torch.int32, device="cuda"),
+           torch.empty(n_u, dtype=torch.int64, device="cuda"),
+           torch.empty(w.bs, dtype=torch.int32, device="cuda"))
+    o2 = torch.empty_like(dev["o"])
+    d1 = pkv.make_desc(dev["q"], dev["k_ext"], dev["v_ext"], dev["o"], dev["k_pool"], dev["v_pool"], w.bs,
+                       dev["kv_indices"].numel())
+    d2 = pkv.make_desc(dev["q"], None, None, o2, dev["k_pool"], dev["v_pool"], w.bs, n_u)
+    nbytes = max(pkv.extend_attention_workspace_size(d1), pkv.extend_attention_workspace_size(d2))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def call():
+        pkv.build_unified_kv_indices(dev["kv_indptr"], dev["kv_indices"], dev["extend_start_loc"],
+                                     dev["extend_seq_lens"], dev["extend_kv_indices"], w.bs, out=uni)
+        pkv.extend_attention_fwd(dev["q"], dev["k_ext"], dev["v_ext"], dev["o"], dev["k_pool"], dev["v_pool"],
+                                 dev["qo_indptr"], dev["kv_indptr"], dev["kv_indices"], sm_scale=w.sm_scale,
+                                 workspace=ws)
+        pkv.extend_attention_fwd_unified(dev["q"], o2, dev["k_pool"], dev["v_pool"], dev["qo_indptr"], uni[0],
+                                         uni[1], uni[2], sm_scale=w.sm_scale, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = (dev["o"].clone(), o2.clone(), uni[0].clone(), uni[1][:int(uni[0][-1])].clone(), uni[2].clone())
+    check(eager[0].float().cpu().numpy().astype(np.float64), oracle.extend_attention_workload(w), "bf16",
+          "graph batch, eager")
+    assert torch.equal(eager[0], eager[1]), "unified and two-part calls differ"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        dev["o"].fill_(float("nan"))
+        o2.fill_(float("nan"))
+        uni[0].fill_(-1)
+        uni[1].fill_(-1)
+        uni[2].fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (dev["o"], o2, uni[0], uni[1][:int(eager[2][-1])], uni[2])
+        for g, e in zip(got, eager):
+            assert torch.equal(g, e), "a graph replay differs from the eager run"
+        call()  # eager work between the replays
+        torch.cuda.synchronize()
