@@ -200,26 +200,16 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
 
   // 3. chunk limit: a 1/rounds share of the average work per resident
   //    workgroup (so that heaviest-first placement can even out the CUs),
-  //    grown until the split chunks fit the partial-state budget
+  //    grown until the split chunks fit the partial-state budget; and
+  // 4. with the limit that fits, in the same block scan: partial-slot and
+  //    merge-record offsets of split items, running cost, number of chunks
   const int64_t shares = (int64_t)a.slots * (a.rounds > 0 ? a.rounds : 1);
   int64_t chunk = (total + shares - 1) / shares;
   if (chunk < a.min_chunk) chunk = a.min_chunk;
-  for (;;) {
-    int64_t parts = 0;
-    for (int n = n0; n < n1; ++n) {
-      const int c = cost_of[n];
-      if (c > chunk) parts += (c + chunk - 1) / chunk;
-    }
-    parts = block_sum(parts, sh);
-    if (parts <= a.part_budget) break;
-    chunk *= 2;
-  }
-  auto pieces = [&](int c) { return c > chunk ? (int)((c + chunk - 1) / chunk) : 1; };
-
-  // 4. partial-slot and merge-record offsets of split items, running cost,
-  //    and the number of chunks
+  // (c > chunk: both fit 32 bits, and a 32-bit divide is much shorter than a 64-bit one)
+  auto pieces = [&](int c) { return c > chunk ? (int)((uint32_t)(c - 1) / (uint32_t)chunk) + 1 : 1; };
   int mcarry, n_chunks;
-  {
+  for (;;) {
     int v[4] = {0, 0, 0, 0}, ex[4];
     int64_t tot[4];
     for (int n = n0; n < n1; ++n) {
@@ -230,6 +220,10 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       v[3] += k;
     }
     block_excl_scan<4>(v, ex, tot, sh);
+    if (tot[0] > a.part_budget) {
+      chunk *= 2;
+      continue;
+    }
     for (int n = n0; n < n1; ++n) {
       const int c = cost_of[n], k = pieces(c);
       // partial bases < part_budget <= 4096 and merge indices < part_budget fit 16 bits each
@@ -241,6 +235,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     }
     mcarry = (int)tot[1];
     n_chunks = (int)tot[3];
+    break;
   }
 
   // 5. XCD bin of every chunk (midpoint rule), then heaviest first inside a bin
@@ -252,8 +247,13 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   // XCD of a chunk: which of X equal-cost ranges holds its midpoint (twice the
   // midpoint against twice the range ends; integer compares only)
   int64_t bnd2[kMaxXcd];
+  {
+    // (x+1) total / X with one 64-bit divide: (x+1)(q X + r) / X = (x+1) q + (x+1) r / X
+    const int64_t q = total / X;
+    const int rem = (int)(total - q * X);
 #pragma unroll
-  for (int x = 0; x < kMaxXcd; ++x) bnd2[x] = 2 * ((x + 1) * total / X);
+    for (int x = 0; x < kMaxXcd; ++x) bnd2[x] = 2 * ((x + 1) * q + ((x + 1) * rem) / X);
+  }
   auto bin_of = [&](int n, int k0, int k1) {
     const int64_t mid2 = 2 * (int64_t)cum_cost[n] + k0 + k1;
     int x = 0;
