@@ -126,10 +126,14 @@ int gather_kv_indices(const int32_t* req_to_token, int64_t req_to_token_stride, 
  *
  * v_pool / v_extend may be views into k_pool / k_extend (the MLA layout on
  * page "cpu_graph_runner.py", qkv_proj_with_rope: V is the first lv columns
- * of the joint latent+rope K row).  Supported (lq, lv): (64,64), (128,128),
- * (256,256), (192,128), (288,256), (576,512) for bf16; (64,64), (128,128)
- * for fp32.  Strides must be multiples of 8 elements (bf16) or 4 (fp32) and
- * base pointers 16-byte aligned.
+ * of the joint latent+rope K row).  Supported (lq, lv): (64,64), (80,80),
+ * (96,96), (112,112), (128,128), (160,160), (192,192), (256,256), (192,128),
+ * (288,256), (576,512) for bf16; (64,64), (128,128) for fp32.  Plain head
+ * dims between the served tile widths run in the next wider tile with the
+ * extra columns zero (page "extend_attention.py",
+ * _get_block_sizes_for_extend_attention: the head dim is padded to a power
+ * of two and the columns past Lq masked).  Strides must be multiples of 8
+ * elements (bf16) or 4 (fp32) and base pointers 16-byte aligned.
  */
 typedef struct {
   int32_t dtype; /* PKV_BF16 or PKV_FP32: q, k/v extend, pools and o share it */
@@ -343,6 +347,22 @@ int decode_attention_fwd(const void* q, void* o, const void* k_pool, const void*
  * with calls in flight on other host threads.
  */
 int extend_attention_prefer_kernel(const char* name);
+
+/*
+ * Process-wide split granularity of later extend calls, for tests and
+ * benchmarks.  The planner cuts a work item (sequence, KV head, row tile)
+ * whose key range is longer than 1/rounds of the average work per resident
+ * workgroup into chunks of keys, never shorter than min_chunk_tiles key
+ * tiles; each chunk writes a partial softmax state (m, l, acc) and a merge
+ * launch combines them in chunk order (page "flashinfer_backend.py",
+ * forward_extend: the ragged and paged parts merged with merge_state).  The
+ * result is the same softmax at any granularity, up to rounding.  0 keeps a
+ * default (1 round, 8 tiles).  Chunks past the workspace's partial-state
+ * budget are not made: the limit grows until the split fits.  Returns PKV_OK,
+ * or PKV_ERR_INVALID for rounds outside 0..64 or min_chunk_tiles outside
+ * 0..2^20.  Not synchronised with calls in flight on other host threads.
+ */
+int extend_attention_set_split(int rounds, int min_chunk_tiles);
 
 /*
  * Name of the attention kernel symbol that serves a call with `desc` and these

@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_fwd_unified",
            "extend_attention_workspace_size", "decode_attention_fwd", "decode_attention_workspace_size", "store_kv_cache", "gather_kv_indices",
-           "extend_attention_kernel_name", "extend_attention_prefer_kernel",
+           "extend_attention_kernel_name", "extend_attention_prefer_kernel", "extend_attention_set_split",
            "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "LIB_PATH", "PkvError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -83,6 +83,8 @@ def library() -> ctypes.CDLL:
     lib.extend_attention_kernel_name.restype = ctypes.c_char_p
     lib.extend_attention_prefer_kernel.argtypes = [ctypes.c_char_p]
     lib.extend_attention_prefer_kernel.restype = ctypes.c_int
+    lib.extend_attention_set_split.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.extend_attention_set_split.restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.restype = ctypes.c_char_p
     _lib = lib
@@ -239,6 +241,13 @@ def extend_attention_prefer_kernel(name: str) -> None:
     _check(library().extend_attention_prefer_kernel(name.encode()))
 
 
+def extend_attention_set_split(rounds: int = 0, min_chunk_tiles: int = 0) -> None:
+    """Process-wide split granularity (tests, benchmarks): items longer than 1/rounds of the
+    average work per resident workgroup are cut into key chunks of at least min_chunk_tiles
+    tiles, merged afterwards; 0 keeps a default."""
+    _check(library().extend_attention_set_split(int(rounds), int(min_chunk_tiles)))
+
+
 _ws_cache = {}
 
 
@@ -301,7 +310,10 @@ def gather_kv_indices(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor
                       kv_start_idx: Optional[torch.Tensor] = None, capacity: Optional[int] = None,
                       out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Prefix indices of a batch from the request-to-token table: (kv_indptr int32, kv_indices int64).
-    capacity defaults to the sum of kv_lens (read from the device, a host sync)."""
+
+    capacity (the length of kv_indices, at least the sum of kv_lens) comes from
+    the caller, or from ``out`` when it is given: the binding never reads the
+    device, so the call stays free of host syncs and can be captured."""
     _want(req_to_token, "req_to_token", torch.int32)
     _want(req_pool_indices, "req_pool_indices", torch.int64)
     _want(kv_lens, "kv_lens", torch.int32)
@@ -312,7 +324,10 @@ def gather_kv_indices(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor
     bs = kv_lens.numel()
     dev = req_to_token.device
     if capacity is None:
-        capacity = int(kv_lens.sum().item()) if bs else 0
+        if out is None:
+            raise ValueError("gather_kv_indices needs capacity (or out): the sum of kv_lens is not read "
+                             "from the device")
+        capacity = out[1].numel()
     if out is None:
         out = (torch.empty(bs + 1, dtype=torch.int32, device=dev),
                torch.empty(max(capacity, 1), dtype=torch.int64, device=dev))

@@ -1,7 +1,7 @@
 // C ABI of libpkv.so: host-side argument checks, workspace sizing and the
-// stream-ordered launch sequence (plan, then attention, whose last chunk of
-// a split item merges it).  Checks use only host-visible sizes, so no call
-// reads device memory or waits for the device.
+// stream-ordered launch sequence of an extend call (plan, attention, then a
+// merge launch that combines the chunks of split items).  Checks use only
+// host-visible sizes, so no call reads device memory or waits for the device.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -64,6 +64,9 @@ bool v_inside_k(const pkv_attn_desc_t& d, const void* k_extend, const void* v_ex
 enum class Kernel { kNone, kR64, kDl, kAttn };
 
 std::atomic<int> g_prefer{0};  // Kernel preferred by extend_attention_prefer_kernel, 0 = automatic
+// Split granularity set by extend_attention_set_split (0: the defaults above)
+std::atomic<int> g_split_rounds{0};
+std::atomic<int> g_min_chunk{0};
 
 // Tiling of kernel k for the shape, or false when k does not serve it.
 bool kernel_tiling(Kernel k, int dtype, int lq, int lv, bool v_in_k, pkv::Tiling* t) {
@@ -380,6 +383,15 @@ int extend_attention_prefer_kernel(const char* name) {
   return fail(PKV_ERR_INVALID, "unknown kernel \"%s\" (auto, r64, dl, attn)", name);
 }
 
+int extend_attention_set_split(int rounds, int min_chunk_tiles) {
+  if (rounds < 0 || rounds > 64 || min_chunk_tiles < 0 || min_chunk_tiles > (1 << 20))
+    return fail(PKV_ERR_INVALID, "split rounds %d (0..64) or minimum chunk %d tiles (0..2^20) out of range", rounds,
+                min_chunk_tiles);
+  g_split_rounds.store(rounds, std::memory_order_relaxed);
+  g_min_chunk.store(min_chunk_tiles, std::memory_order_relaxed);
+  return ok();
+}
+
 size_t extend_attention_workspace_size(const pkv_attn_desc_t* desc) {
   pkv::Tiling t;
   if (check_desc(desc, &t) != PKV_OK) return 0;
@@ -452,8 +464,10 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   pa.bm = t.bm;
   pa.bn = t.bn;
   pa.slots = resident_slots(d.dtype, d.lq, d.lv, vk, has_options(d));
-  pa.min_chunk = kMinChunkTiles;
-  pa.rounds = kSplitRounds;
+  const int forced_rounds = g_split_rounds.load(std::memory_order_relaxed);
+  const int forced_min = g_min_chunk.load(std::memory_order_relaxed);
+  pa.min_chunk = forced_min > 0 ? forced_min : kMinChunkTiles;
+  pa.rounds = forced_rounds > 0 ? forced_rounds : kSplitRounds;
   pa.xcds = kXcds;
   pa.max_work = pb.max_work;
   pa.max_items = pb.max_items;

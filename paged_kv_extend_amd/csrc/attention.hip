@@ -499,15 +499,16 @@ int occupancy_t() {
 
 hipError_t launch_split_merge(int dtype, int lv, int bm, const AttnArgs& a, hipStream_t s) {
   const dim3 g(512), t(256);  // a grid stride over (merge record, row block) tasks
+  if (lv <= 0 || lv % 4 != 0) return hipErrorInvalidValue;
   if (dtype == 1) {
-    if (lv == 64) hipLaunchKernelGGL((split_merge_kernel<true, 64>), g, t, 0, s, a, bm);
-    else if (lv == 128) hipLaunchKernelGGL((split_merge_kernel<true, 128>), g, t, 0, s, a, bm);
+    if (lv <= 64) hipLaunchKernelGGL((split_merge_kernel<true, 64>), g, t, 0, s, a, bm, lv);
+    else if (lv <= 128) hipLaunchKernelGGL((split_merge_kernel<true, 128>), g, t, 0, s, a, bm, lv);
     else return hipErrorInvalidValue;
   } else {
-    if (lv == 64) hipLaunchKernelGGL((split_merge_kernel<false, 64>), g, t, 0, s, a, bm);
-    else if (lv == 128) hipLaunchKernelGGL((split_merge_kernel<false, 128>), g, t, 0, s, a, bm);
-    else if (lv == 256) hipLaunchKernelGGL((split_merge_kernel<false, 256>), g, t, 0, s, a, bm);
-    else if (lv == 512) hipLaunchKernelGGL((split_merge_kernel<false, 512>), g, t, 0, s, a, bm);
+    if (lv <= 64) hipLaunchKernelGGL((split_merge_kernel<false, 64>), g, t, 0, s, a, bm, lv);
+    else if (lv <= 128) hipLaunchKernelGGL((split_merge_kernel<false, 128>), g, t, 0, s, a, bm, lv);
+    else if (lv <= 256) hipLaunchKernelGGL((split_merge_kernel<false, 256>), g, t, 0, s, a, bm, lv);
+    else if (lv <= 512) hipLaunchKernelGGL((split_merge_kernel<false, 512>), g, t, 0, s, a, bm, lv);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

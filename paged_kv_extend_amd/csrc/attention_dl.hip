@@ -36,8 +36,21 @@
 namespace pkv {
 namespace {
 
-template <int LQ, int LV, int BN, bool VK, int RG_, int SPLIT_, int NS_>
+template <int LQ, int LV, int BN, bool VK, int RG_, int SPLIT_, int NS_, int DR_ = 0>
 struct DlCfg {
+  // Plain head dims that are not a served tile width (80, 96, 112 in the
+  // 128-wide tile, 160 and 192 in the 256-wide one): the tile keeps its width
+  // and the columns from DR on hold zeros -- Q's in registers, K's and V's
+  // loaded from the zero row -- so the products over them add nothing; the
+  // contraction stops at the last real 16-column step and only output
+  // blocks holding real columns are computed and stored (the page's
+  // extend kernels pad the head dim to a power of two and mask the columns
+  // past Lq the same way: page "extend_attention.py",
+  // _get_block_sizes_for_extend_attention and the offs_d < Lq masks).
+  static constexpr int LQR = DR_ ? DR_ : LQ;  // real Q/K dims
+  static constexpr int LVR = DR_ ? DR_ : LV;  // real V/O dims
+  static constexpr int CKR = LQR / 8;         // real 16-byte chunks of a K row
+  static constexpr int CVR = LVR / 8;
   // Waves per row group.  When one wave cannot hold both its Q^T operand
   // (LQ / 4 registers) and its O^T accumulator (LV / 2 registers), two waves
   // share a row group: each holds half of the Q dims and half of the O
@@ -60,6 +73,10 @@ struct DlCfg {
   static constexpr int CK = LQ / 8;      // 16-byte chunks per K row
   static constexpr int CV = LV / 8;
   static constexpr int NDB_ALL = LV / 32;  // 32-column output blocks
+  // contraction steps and output blocks a wave computes: the split variants
+  // interleave the halves inside 8-chunk groups and compute every step
+  static constexpr int NQ = SPLIT == 1 ? (CKR + 1) / 2 : QD / 16;
+  static constexpr int NDB = SPLIT == 1 ? (LVR + 31) / 32 : VD / 32;
   static constexpr bool WIDE = CK == 72;  // 576-element rows: swizzle inside 8-chunk groups
   // rows sharing one 256-byte window of the 64 LDS banks
   static constexpr int RPK = CK >= 16 ? 1 : 16 / CK;
@@ -100,6 +117,7 @@ struct DlCfg {
   static_assert(QD % 16 == 0 && VD % 32 == 0, "split");
   static_assert(SPLIT == 1 || (SPLIT == 2 && CK % 8 == 0 && NDB_ALL % 2 == 0), "split: halves interleave in 8-chunk groups");
   static_assert(BN % 32 == 0 && BN <= 128, "key tile");
+  static_assert(DR_ == 0 || (!VK && LQ == LV && DR_ < LQ && DR_ % 16 == 0), "padded plain head dims");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r.  K: the 32 rows read at
@@ -135,14 +153,14 @@ __device__ __forceinline__ int swz_v(int r, int c) {
 // OPT: a sliding window or a custom mask (which replaces the causal rule) may
 // be set -- a variant of its own, so that calls without them run code that
 // holds no register for them
-template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, bool CAP, bool OPT, int MINB>
-__global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void attn_dl_kernel(AttnArgs a) {
-  using C = DlCfg<LQ, LV, BN, VK, RG, SP, NS>;
+template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, int DR, bool CAP, bool OPT, int MINB>
+__global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) void attn_dl_kernel(AttnArgs a) {
+  using C = DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>;
   using T = uint16_t;
   constexpr int BM = C::BM;
   constexpr int NKB = BN / 32;
-  constexpr int NQ = C::QD / 16;
-  constexpr int NDB = C::VD / 32;
+  constexpr int NQ = C::NQ;
+  constexpr int NDB = C::NDB;
 
   __shared__ __attribute__((aligned(1024))) char lds[NS * C::STAGE_BYTES + C::XCH_BYTES];
   __shared__ gptr<T> kptr[NS][BN];  // row pointer tables, slot kt % NS
@@ -202,7 +220,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) {
       const int ch = qk_chunk(ks) + hi;
-      const u32x4 v = valid ? *(gptr<u32x4>)(qrow + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 v = valid && ch < C::CKR ? *(gptr<u32x4>)(qrow + ch * 8) : u32x4{0u, 0u, 0u, 0u};
       qr[ks] = __builtin_bit_cast(bf16x8, v ^ flip);
     }
   }
@@ -281,7 +299,8 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
         for (int i = 0; i < C::K_LOADS; ++i) {
           const unsigned off = (unsigned)kchunk(i, vw) * 1024u + (unsigned)lane * 16u;
           const unsigned row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
-          ksrc[q][i] = kptr[kt % NS][row] + (unsigned)swz_k<C>(row, p) * 8u;
+          const unsigned c = (unsigned)swz_k<C>(row, p);
+          ksrc[q][i] = C::CKR < C::CK && c >= (unsigned)C::CKR ? zrow : kptr[kt % NS][row] + c * 8u;
         }
       }
       if (do_v) {
@@ -289,7 +308,8 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
         for (int i = 0; i < C::V_LOADS; ++i) {
           const unsigned off = (unsigned)vchunk(i, vw) * 1024u + (unsigned)lane * 16u;
           const unsigned row = off / (LV * 2), p = (off % (LV * 2)) / 16;
-          vsrc[q][i] = vptr[kt % NS][row] + (unsigned)swz_v<C>(row, p) * 8u;
+          const unsigned c = (unsigned)swz_v<C>(row, p);
+          vsrc[q][i] = C::CVR < C::CV && c >= (unsigned)C::CVR ? zrow : vptr[kt % NS][row] + c * 8u;
         }
       }
     }
@@ -622,6 +642,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = o_block(db) * 32 + 8 * g4 + 4 * hi;
+        if (C::LVR < LV && d >= C::LVR) continue;  // padded columns
         bf16x4 ov;
         ov[0] = (__bf16)(acc[db][4 * g4] * inv);
         ov[1] = (__bf16)(acc[db][4 * g4 + 1] * inv);
@@ -632,12 +653,13 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
     }
   } else {
     const int64_t prow = (int64_t)it.part * BM + rg * 32 + qi;
-    float* pa = a.part_acc + prow * LV;
+    float* pa = a.part_acc + prow * C::LVR;  // rows of the real width
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = o_block(db) * 32 + 8 * g4 + 4 * hi;
+        if (C::LVR < LV && d >= C::LVR) continue;
         *reinterpret_cast<float4*>(pa + d) =
             make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
       }
@@ -646,51 +668,61 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT), MINB) void
   }
 }
 
-template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, int MINB>
+template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, int DR, int MINB>
 hipError_t launch_dl_t(const AttnArgs& a, int64_t grid, hipStream_t s) {
-  using C = DlCfg<LQ, LV, BN, VK, RG, SP, NS>;
+  using C = DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>;
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), t(C::NT);
   if (a.custom_mask || a.window > 0) {
     if (a.use_cap)
-      hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, true, true, MINB>), g, t, 0, s, a);
+      hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, DR, true, true, MINB>), g, t, 0, s, a);
     else
-      hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, true, MINB>), g, t, 0, s, a);
+      hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, DR, false, true, MINB>), g, t, 0, s, a);
   } else if (a.use_cap) {
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, true, false, MINB>), g, t, 0, s, a);
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, DR, true, false, MINB>), g, t, 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, false, MINB>), g, t, 0, s, a);
+    hipLaunchKernelGGL((attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, DR, false, false, MINB>), g, t, 0, s, a);
   }
   return hipGetLastError();
 }
 
-template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, int MINB>
+template <int LQ, int LV, int BN, bool VK, int RG, int SP, int NS, int DR, int MINB>
 int dl_occupancy_t() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, false, false, MINB>),
-          DlCfg<LQ, LV, BN, VK, RG, SP, NS>::NT, 0) != hipSuccess)
+          &n, reinterpret_cast<const void*>(&attn_dl_kernel<LQ, LV, BN, VK, RG, SP, NS, DR, false, false, MINB>),
+          DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT, 0) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
 }
 
 // bf16 variants served here: (lq, lv, key tile, V inside K, 32-row groups,
-// waves per row group, LDS stages, workgroups per CU)
-#define PKV_DL_VARIANTS(X)                \
-  X(64, 64, 64, false, 4, 1, 4, 2)        \
-  X(128, 128, 128, false, 8, 1, 2, 1)     \
-  X(256, 256, 32, false, 4, 2, 3, 1)      \
-  X(576, 512, 32, true, 4, 2, 3, 1)
+// waves per row group, LDS stages, real plain head dim in a wider tile or 0,
+// workgroups per CU)
+#define PKV_DL_VARIANTS(X)                   \
+  X(64, 64, 64, false, 4, 1, 4, 0, 2)        \
+  X(128, 128, 128, false, 8, 1, 2, 0, 1)     \
+  X(256, 256, 32, false, 4, 2, 3, 0, 1)      \
+  X(576, 512, 32, true, 4, 2, 3, 0, 1)       \
+  X(128, 128, 128, false, 8, 1, 2, 80, 1)    \
+  X(128, 128, 128, false, 8, 1, 2, 96, 1)    \
+  X(128, 128, 128, false, 8, 1, 2, 112, 1)   \
+  X(256, 256, 32, false, 4, 2, 3, 160, 1)    \
+  X(256, 256, 32, false, 4, 2, 3, 192, 1)
+
+// head dims a variant serves: its tile's, or the real plain dim it pads
+#define PKV_DL_MATCH(Q, V, VK, DR) \
+  (lq == ((DR) ? (DR) : (Q)) && lv == ((DR) ? (DR) : (V)) && (!(VK) || v_in_k))
 
 }  // namespace
 
 bool dl_tiling(int dtype, int lq, int lv, bool v_in_k, Tiling* t) {
   if (dtype != 0) return false;
-#define PKV_DT(Q, V, N, VK, RG, SP, NS, M)              \
-  if (lq == Q && lv == V && (!VK || v_in_k)) {          \
-    t->bm = DlCfg<Q, V, N, VK, RG, SP, NS>::BM;         \
+#define PKV_DT(Q, V, N, VK, RG, SP, NS, DR, M)          \
+  if (PKV_DL_MATCH(Q, V, VK, DR)) {                     \
+    t->bm = DlCfg<Q, V, N, VK, RG, SP, NS, DR>::BM;     \
     t->bn = N;                                          \
-    t->threads = DlCfg<Q, V, N, VK, RG, SP, NS>::NT;    \
+    t->threads = DlCfg<Q, V, N, VK, RG, SP, NS, DR>::NT; \
     return true;                                        \
   }
   PKV_DL_VARIANTS(PKV_DT)
@@ -699,16 +731,16 @@ bool dl_tiling(int dtype, int lq, int lv, bool v_in_k, Tiling* t) {
 }
 
 hipError_t launch_dl(int lq, int lv, bool v_in_k, const AttnArgs& a, int64_t grid, hipStream_t s) {
-#define PKV_DLL(Q, V, N, VK, RG, SP, NS, M) \
-  if (lq == Q && lv == V && (!VK || v_in_k)) return launch_dl_t<Q, V, N, VK, RG, SP, NS, M>(a, grid, s);
+#define PKV_DLL(Q, V, N, VK, RG, SP, NS, DR, M) \
+  if (PKV_DL_MATCH(Q, V, VK, DR)) return launch_dl_t<Q, V, N, VK, RG, SP, NS, DR, M>(a, grid, s);
   PKV_DL_VARIANTS(PKV_DLL)
 #undef PKV_DLL
   return hipErrorInvalidValue;
 }
 
 int dl_blocks_per_cu(int lq, int lv, bool v_in_k) {
-#define PKV_DLO(Q, V, N, VK, RG, SP, NS, M) \
-  if (lq == Q && lv == V && (!VK || v_in_k)) return dl_occupancy_t<Q, V, N, VK, RG, SP, NS, M>();
+#define PKV_DLO(Q, V, N, VK, RG, SP, NS, DR, M) \
+  if (PKV_DL_MATCH(Q, V, VK, DR)) return dl_occupancy_t<Q, V, N, VK, RG, SP, NS, DR, M>();
   PKV_DL_VARIANTS(PKV_DLO)
 #undef PKV_DLO
   return 1;

@@ -18,10 +18,12 @@
 namespace pkv {
 
 // Work of the merge launch: (merge record, block of rows) tasks, strided over
-// the grid; thread = (row of the block, 4 columns).
-template <bool F32, int LV>
-__global__ __launch_bounds__(256) void split_merge_kernel(AttnArgs a, int bm) {
-  constexpr int V4 = LV / 4;          // float4 columns per row
+// the grid; thread = (row of the block, 4 columns).  Rows hold lv columns
+// (partial accumulators are lv floats apart); LVP, a power of two >= lv,
+// sets the threads per row, and threads past lv idle.
+template <bool F32, int LVP>
+__global__ __launch_bounds__(256) void split_merge_kernel(AttnArgs a, int bm, int lv) {
+  constexpr int V4 = LVP / 4;         // float4 columns per row
   constexpr int RPB = 256 / V4;       // rows per task
   static_assert(256 % V4 == 0, "columns per thread block");
   const int blocks = (bm + RPB - 1) / RPB;
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(AttnArgs a, int bm) {
     const int row = (task % blocks) * RPB + row_in;
     const int q0 = a.qo_indptr[mi.b], E = a.qo_indptr[mi.b + 1] - q0;
     const int r = mi.t * bm + row;
-    if (row >= bm || r >= E * G) continue;
+    if (row >= bm || r >= E * G || d >= lv) continue;
     float M = -INFINITY;
 #pragma unroll 8
     for (int s = 0; s < mi.n; ++s) M = fmaxf(M, a.part_ml[((int64_t)(mi.part_base + s) * bm + row) * 2]);
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(AttnArgs a, int bm) {
       const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
       const float w = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
       L += ml.y * w;
-      const float4 v = *reinterpret_cast<const float4*>(a.part_acc + prow * LV + d);
+      const float4 v = *reinterpret_cast<const float4*>(a.part_acc + prow * lv + d);
       o.x += v.x * w;
       o.y += v.y * w;
       o.z += v.z * w;

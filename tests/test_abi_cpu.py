@@ -45,7 +45,12 @@ def test_kernel_name_per_variant():
     assert kernel_name(mla) == "attn_kernel"
     assert kernel_name(mla, 4096, 4096, 12288, 12288) == "attn_dl_kernel"
     assert kernel_name(desc(dtype=1, lq=64, lv=64)) == "attn_kernel"
-    assert kernel_name(desc(lq=80, lv=80)) is None
+    # plain head dims between the tile widths run in a wider tile of the direct-load kernel
+    for dim in (80, 96, 112, 160, 192):
+        assert kernel_name(desc(lq=dim, lv=dim)) == "attn_dl_kernel", dim
+    assert kernel_name(desc(lq=72, lv=72)) is None
+    assert kernel_name(desc(lq=80, lv=64)) is None
+    assert kernel_name(desc(dtype=1, lq=96, lv=96)) is None
 
 
 def test_kernel_preference():
@@ -62,6 +67,14 @@ def test_kernel_preference():
     finally:
         pkv.extend_attention_prefer_kernel("auto")
     assert kernel_name(desc()) == "attn_dl_kernel"
+
+
+def test_split_setting_is_checked():
+    for bad in ((-1, 0), (65, 0), (0, -2), (0, 1 << 21)):
+        with pytest.raises(pkv.PkvError):
+            pkv.extend_attention_set_split(*bad)
+    pkv.extend_attention_set_split(4, 1)
+    pkv.extend_attention_set_split(0, 0)
 
 
 def test_workspace_covers_every_kernel():
@@ -99,7 +112,9 @@ def test_workspace_size_valid_and_grows():
 
 @pytest.mark.parametrize("kw,needle", [
     (dict(num_q_heads=30), "multiple"),
-    (dict(lq=96, lv=96), "not supported"),
+    (dict(lq=72, lv=72), "not supported"),
+    (dict(lq=96, lv=80), "not supported"),
+    (dict(dtype=1, lq=96, lv=96), "not supported"),
     (dict(dtype=5), "dtype"),
     (dict(bs=-1), "bs"),
     (dict(q_stride_head=100), "stride"),
@@ -120,7 +135,7 @@ def call_fwd(d, ws_bytes=1 << 30, ptr=4096, ws=4096):
 
 def test_fwd_argument_errors_without_device():
     assert call_fwd(None) == pkv.PkvError(-1, "").code == -1
-    assert call_fwd(desc(lq=80, lv=80)) == -2
+    assert call_fwd(desc(lq=72, lv=72)) == -2
     assert call_fwd(desc(num_kv_heads=7)) == -1
     assert call_fwd(desc(), ws_bytes=16) == -3
     assert "workspace" in pkv.last_error()
@@ -176,7 +191,7 @@ def test_store_and_gather_argument_errors_without_device():
     assert lib.store_kv_cache(p, p, p, None, p, ctypes.byref(d), None) == -1
     assert lib.store_kv_cache(p, p, p, p, p, ctypes.byref(desc(total_q_tokens=0)), None) == 0
     assert lib.store_kv_cache(p + 4, p, p, p, p, ctypes.byref(d), None) == -2
-    assert lib.store_kv_cache(p, p, p, p, p, ctypes.byref(desc(lq=80, lv=80)), None) == -2
+    assert lib.store_kv_cache(p, p, p, p, p, ctypes.byref(desc(lq=72, lv=72)), None) == -2
     assert lib.gather_kv_indices(p, 64, p, p, None, -1, p, p, 10, None) == -1
     assert lib.gather_kv_indices(p, 64, p, p, None, 3, None, p, 10, None) == -1
     assert lib.gather_kv_indices(None, 64, p, p, None, 3, p, p, 10, None) == -1
@@ -207,7 +222,7 @@ def test_decode_workspace_size_grows_with_keys():
 
 @pytest.mark.parametrize("kw,needle", [
     (dict(dtype=2), "dtype"),
-    (dict(lq=80, lv=80), "not supported"),
+    (dict(lq=72, lv=72), "not supported"),
     (dict(dtype=1, lq=256, lv=256), "not supported"),  # fp32 extend kernels serve 64 and 128 only
     (dict(dtype=1, kp_stride_slot=1002), "stride"),
     (dict(num_q_heads=30), "multiple"),

@@ -70,6 +70,17 @@ EDGE = [
          v_aliases_k=True, std=0.5, sm_scale=-0.06),
     dict(name="mla-v-apart", dtype="bf16", prefix_lens=[33, 0], extend_lens=[10, 40], hq=8, hkv=1, lq=576, lv=512,
          std=0.5),
+    # plain head dims between the tile widths (zero columns in the next wider
+    # tile): several key tiles, ragged row tiles, a soft-cap and a negative scale
+    dict(name="d80", dtype="bf16", prefix_lens=[300, 0, 41], extend_lens=[70, 129, 3], hq=8, hkv=2, lq=80, lv=80),
+    dict(name="d96", dtype="bf16", prefix_lens=[260, 7], extend_lens=[90, 200], hq=12, hkv=4, lq=96, lv=96),
+    dict(name="d96-cap", dtype="bf16", prefix_lens=[500, 0], extend_lens=[33, 64], hq=4, hkv=1, lq=96, lv=96,
+         logit_cap=5.0),
+    dict(name="d112-neg", dtype="bf16", prefix_lens=[129, 400], extend_lens=[17, 60], hq=6, hkv=2, lq=112, lv=112,
+         sm_scale=-0.08),
+    dict(name="d160", dtype="bf16", prefix_lens=[200, 3], extend_lens=[45, 100], hq=8, hkv=4, lq=160, lv=160),
+    dict(name="d192-cap", dtype="bf16", prefix_lens=[90, 0], extend_lens=[30, 77], hq=4, hkv=2, lq=192, lv=192,
+         logit_cap=20.0),
 ]
 
 

@@ -203,3 +203,14 @@ def test_decode_fp32(dims, opt):
     dev["o"].fill_(float("nan"))  # rows of keyless requests are written too
     run_decode(d, dev, window=window, sinks=sinks)
     check(out_f64(dev), oracle_decode(d, window=window, sinks=sinks), "fp32", f"fp32 {dims} {opt}")
+
+
+# bf16 head dims without a decode kernel variant run through the extend route
+# too (the plain dims the extend kernels pad to a wider tile)
+@pytest.mark.parametrize("dims", [80, 96, 160])
+def test_decode_plain_dims_through_extend(dims):
+    d = wl.decode_custom(LENS, seed=59, hq=8, hkv=2, lq=dims, lv=dims)
+    dev = wl.decode_to_torch(d)
+    dev["o"].fill_(float("nan"))
+    run_decode(d, dev)
+    check(out_f64(dev), oracle_decode(d), "bf16", f"bf16 {dims} via extend")

@@ -78,6 +78,11 @@ EDGE = [
          lv=128, sm_scale=0.05),
     dict(name="e1-decode", dtype="bf16", prefix_lens=[500, 0, 31], extend_lens=[1, 1, 1], hq=8, hkv=2, lq=128,
          lv=128),
+    dict(name="d80", dtype="bf16", prefix_lens=[300, 0, 41], extend_lens=[70, 129, 3], hq=8, hkv=2, lq=80, lv=80),
+    dict(name="d96", dtype="bf16", prefix_lens=[260, 7], extend_lens=[90, 200], hq=12, hkv=4, lq=96, lv=96),
+    dict(name="d112", dtype="bf16", prefix_lens=[129, 400], extend_lens=[17, 60], hq=6, hkv=2, lq=112, lv=112),
+    dict(name="d160-cap", dtype="bf16", prefix_lens=[200, 3], extend_lens=[45, 100], hq=8, hkv=4, lq=160, lv=160,
+         logit_cap=10.0),
 ]
 
 

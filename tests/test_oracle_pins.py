@@ -184,6 +184,53 @@ def test_saturated_soft_cap_closed_form():
     np.testing.assert_allclose(got[0, 0], want, atol=1e-14)
 
 
+def _softcap_example():
+    with open(os.path.join(GOLDEN, "softcap_worked_example.json")) as f:
+        ex = json.load(f)
+    # pool slots 3 and 1 hold the two prefix keys, slot 4 the new token's key
+    # (the unified and decode forms read it there); other slots hold NaN
+    pool_k = np.full((6, 1, 2), np.nan, np.float32)
+    pool_v = np.full((6, 1, 4), np.nan, np.float32)
+    for slot, d, v in zip([3, 1, 4], ex["dots"], ex["v"]):
+        pool_k[slot, 0] = [d, 0.0]
+        pool_v[slot, 0] = v
+    q = np.array(ex["q"], np.float32).reshape(1, 1, 2)
+    return ex, q, pool_k, pool_v
+
+
+def _check_softcap_output(ex, out):
+    out = np.asarray(out).reshape(-1)
+    np.testing.assert_allclose(out, ex["expected_output"], rtol=0, atol=1e-14)
+    w = out[:3]
+    np.testing.assert_allclose(w, ex["expected_weights"], rtol=0, atol=1e-14)
+    # the logits themselves, up to the softmax's shift: log(w_j / w_0) = s_j - s_0
+    cap = np.asarray(ex["expected_capped_logits"])
+    np.testing.assert_allclose(np.log(w / w[0]), cap - cap[0], rtol=0, atol=1e-13)
+
+
+def test_softcap_worked_example_two_part():
+    ex, q, pool_k, pool_v = _softcap_example()
+    k_ext = pool_k[4:5].copy()
+    v_ext = pool_v[4:5].copy()
+    out = oracle.extend_attention(q, k_ext, v_ext, pool_k, pool_v, [0, 1], [0, 2], [3, 1],
+                                  sm_scale=ex["sm_scale"], logit_cap=ex["logit_cap"], dtype="fp32")
+    _check_softcap_output(ex, out)
+
+
+def test_softcap_worked_example_unified():
+    ex, q, pool_k, pool_v = _softcap_example()
+    out = oracle.extend_attention_unified(q, pool_k, pool_v, [0, 1], [0, 3], [3, 1, 4], [2],
+                                          sm_scale=ex["sm_scale"], logit_cap=ex["logit_cap"], dtype="fp32")
+    _check_softcap_output(ex, out)
+
+
+def test_softcap_worked_example_decode():
+    ex, q, pool_k, pool_v = _softcap_example()
+    out = oracle.decode_attention(q, pool_k, pool_v, [0, 3], [3, 1, 4],
+                                  sm_scale=ex["sm_scale"], logit_cap=ex["logit_cap"], dtype="fp32")
+    _check_softcap_output(ex, out)
+
+
 def test_huge_cap_is_no_cap():
     w = wl.custom(dtype="bf16", prefix_lens=[9, 30], extend_lens=[4, 11], hq=4, hkv=2, lq=64, lv=64)
     base = oracle.extend_attention_workload(w)
