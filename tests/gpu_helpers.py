@@ -41,15 +41,3 @@ def check(got, want, dtype, what=""):
     say(f"  {what}: max-abs {mx:.3g} mean-abs {mean:.3g}")
     assert mx <= bar_max and mean <= bar_mean, f"{what}: max-abs {mx:.3g}, mean-abs {mean:.3g}"
 
-
-def sample_rows(w, n_random=48, seed=0):
-    """First and last new token of every sequence plus random rows."""
-    rng = np.random.default_rng(seed)
-    rows = set()
-    for b in range(w.bs):
-        lo, hi = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
-        if hi > lo:
-            rows.update({lo, hi - 1})
-    if w.total_q:
-        rows.update(rng.integers(0, w.total_q, size=n_random).tolist())
-    return np.array(sorted(rows), np.int64)
