@@ -335,6 +335,34 @@ int decode_attention_fwd(const void* q, void* o, const void* k_pool, const void*
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * extend_attention_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation, kernels and
+ * arguments as extend_attention_fwd, with the plan, the work list and the
+ * split chunks' partial states kept in a scratch array of the library's own,
+ * extend_attention_noalloc_scratch_bytes() = 32 MiB per device, which each
+ * device the library runs on holds until the process ends.  The call itself
+ * allocates nothing and calls no allocating routine.  Partial states get at
+ * most 24 MiB of it (long key ranges are then split less finely than with a
+ * full workspace: the result is the same up to rounding).
+ *
+ * Every call on one device shares that device's array: calls whose work
+ * overlaps on one device (several streams, several host threads) race and
+ * give undefined results; calls ordered on one stream are safe.  Nothing in
+ * the array needs clearing between calls (each call writes what it reads).
+ *
+ * Returns as extend_attention_fwd, plus PKV_ERR_UNSUPPORTED when the batch's
+ * planning state would not fit the array (at 32 query heads over 8 KV heads
+ * and head dim 128: more than about 877 000 new tokens) or for a device
+ * index >= 64.
+ */
+int extend_attention_fwd_noalloc(const void* q_extend, const void* k_extend, const void* v_extend, void* o,
+                                 const void* k_pool, const void* v_pool, const int32_t* qo_indptr,
+                                 const int32_t* kv_indptr, const int64_t* kv_indices, float sm_scale,
+                                 float logit_cap, const pkv_attn_desc_t* desc, void* stream);
+size_t extend_attention_noalloc_scratch_bytes(void);
+
+/*
  * Process-wide kernel preference for later extend_attention_fwd calls, for
  * tests and benchmarks: "auto" (the default: the fastest measured kernel that
  * serves the shape), "r64" (64 query rows per wave; bf16, lq == lv == 128), "dl"

@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_fwd_unified",
-           "extend_attention_workspace_size", "decode_attention_fwd", "decode_attention_workspace_size", "store_kv_cache", "gather_kv_indices",
+           "extend_attention_workspace_size", "extend_attention_fwd_noalloc", "decode_attention_fwd", "decode_attention_workspace_size", "store_kv_cache", "gather_kv_indices",
            "extend_attention_kernel_name", "extend_attention_prefer_kernel", "extend_attention_set_split",
            "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "LIB_PATH", "PkvError"]
 
@@ -66,6 +66,10 @@ def library() -> ctypes.CDLL:
     lib.extend_attention_fwd_unified.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
                                                  ctypes.POINTER(AttnDesc), P, ctypes.c_size_t, P]
     lib.extend_attention_fwd_unified.restype = ctypes.c_int
+    lib.extend_attention_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
+                                                 ctypes.POINTER(AttnDesc), P]
+    lib.extend_attention_fwd_noalloc.restype = ctypes.c_int
+    lib.extend_attention_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.decode_attention_workspace_size.argtypes = [ctypes.POINTER(AttnDesc)]
     lib.decode_attention_workspace_size.restype = ctypes.c_size_t
     lib.decode_attention_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
@@ -291,6 +295,26 @@ def extend_attention_fwd(q_extend: torch.Tensor, k_extend: torch.Tensor, v_exten
         _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
         float(sm_scale or 0.0), float(logit_cap), ctypes.byref(desc),
         _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    _check(rc)
+    return o
+
+
+def extend_attention_fwd_noalloc(q_extend: torch.Tensor, k_extend: torch.Tensor, v_extend: torch.Tensor,
+                                 o: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                 qo_indptr: torch.Tensor, kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
+                                 sm_scale: Optional[float] = None, logit_cap: float = 0.0) -> torch.Tensor:
+    """extend_attention_fwd without a workspace: the library keeps the plan and the
+    partial states in a scratch array of its own per device (no allocation in the
+    call; calls that overlap on one device race).  See include/pkv.h."""
+    _want(qo_indptr, "qo_indptr", torch.int32)
+    _want(kv_indptr, "kv_indptr", torch.int32)
+    _want(kv_indices, "kv_indices", torch.int64)
+    bs = qo_indptr.numel() - 1
+    desc = make_desc(q_extend, k_extend, v_extend, o, k_pool, v_pool, bs, kv_indices.numel())
+    rc = library().extend_attention_fwd_noalloc(
+        _ptr(q_extend), _ptr(k_extend), _ptr(v_extend), _ptr(o), _ptr(k_pool), _ptr(v_pool),
+        _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices), float(sm_scale or 0.0), float(logit_cap),
+        ctypes.byref(desc), _stream(q_extend.device))
     _check(rc)
     return o
 

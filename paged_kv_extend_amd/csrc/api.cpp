@@ -169,12 +169,12 @@ int check_desc(const pkv_attn_desc_t* d, pkv::Tiling* t) {
   return PKV_OK;
 }
 
-pkv::PlanBounds plan_bounds(const pkv_attn_desc_t* d, const pkv::Tiling& t) {
+pkv::PlanBounds plan_bounds(const pkv_attn_desc_t* d, const pkv::Tiling& t, size_t partial_bytes = kPartialBytes) {
   pkv::PlanBounds pb;
   const int64_t group = d->num_q_heads / d->num_kv_heads;
   // sum_b ceil(E_b G / BM) <= T G / BM + bs
   pb.max_items = (int64_t)d->num_kv_heads * (d->total_q_tokens * group / t.bm + d->bs + 1);
-  int64_t budget = (int64_t)(kPartialBytes / ((size_t)t.bm * (d->lv + 2) * sizeof(float)));
+  int64_t budget = (int64_t)(partial_bytes / ((size_t)t.bm * (d->lv + 2) * sizeof(float)));
   if (budget > 4096) budget = 4096;
   if (budget < 16) budget = 16;
   pb.part_budget = budget;
@@ -413,12 +413,48 @@ size_t extend_attention_workspace_size(const pkv_attn_desc_t* desc) {
 
 namespace {
 
+// The workspace of extend_attention_fwd_noalloc: one array per device, held
+// until the process ends.  Its name is a host-side stand-in; the device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = 32u << 20;
+constexpr size_t kNoAllocPartialBytes = 24u << 20;  // of it, for split chunks' partial states
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array into *out; returns
+// PKV_OK or an error code (message set).
+int device_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "device %d beyond the %d the no-allocation entry point serves", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress of the scratch array: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 // Both entry points: two-part when prefix_lens is NULL (new tokens' K/V from
 // k_extend / v_extend), unified otherwise (every key through kv_indices).
+// partial_bytes bounds the split chunks' partial states; noalloc: the
+// workspace is the current device's scratch array, of workspace_bytes
+// (no profiling events).
 int attention_call(const void* q_extend, const void* k_extend, const void* v_extend, void* o, const void* k_pool,
                    const void* v_pool, const int32_t* qo_indptr, const int32_t* kv_indptr,
                    const int64_t* kv_indices, const int32_t* prefix_lens, float sm_scale, float logit_cap,
-                   const pkv_attn_desc_t* desc, void* workspace, size_t workspace_bytes, void* stream) {
+                   const pkv_attn_desc_t* desc, void* workspace, size_t workspace_bytes, void* stream,
+                   size_t partial_bytes = kPartialBytes, bool noalloc = false) {
   pkv::Tiling t;
   int rc = check_desc(desc, &t);
   if (rc != PKV_OK) return rc;
@@ -440,8 +476,17 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
 
   const bool vk = v_inside_k(d, k_extend, v_extend, k_pool, v_pool);
   if (vk) tiling_for(d, true, &t);  // the tiling of the kernel that serves this call
-  const pkv::PlanBounds pb = plan_bounds(&d, t);
+  const pkv::PlanBounds pb = plan_bounds(&d, t, partial_bytes);
   const pkv::WsLayout wl = ws_layout(&d, t, pb);
+  if (noalloc) {
+    if (wl.total > workspace_bytes)
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "batch too large for the no-allocation entry point: %zu bytes of planning and partial state "
+                  "needed, its scratch array holds %zu",
+                  wl.total, workspace_bytes);
+    rc = device_scratch(&workspace);
+    if (rc != PKV_OK) return rc;
+  }
   if (!workspace || workspace_bytes < wl.total)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
                 wl.total);
@@ -522,7 +567,7 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   a.merge = pa.merge;
   a.part_acc = reinterpret_cast<float*>(ws + wl.part_acc);
   a.part_ml = reinterpret_cast<float*>(ws + wl.part_ml);
-  const auto ev = profile_slot();
+  const auto ev = noalloc ? std::pair<hipEvent_t, hipEvent_t>{nullptr, nullptr} : profile_slot();
   if (ev.first) (void)hipEventRecord(ev.first, s);
   pkv::Tiling td;
   switch (pick_kernel(d.dtype, d.lq, d.lv, vk, &td, has_options(d))) {
@@ -562,6 +607,25 @@ int extend_attention_fwd_unified(const void* q_extend, void* o, const void* k_po
   return attention_call(q_extend, nullptr, nullptr, o, k_pool, v_pool, qo_indptr, unified_kv_indptr,
                         unified_kv_indices, prefix_lens ? prefix_lens : &kNoPrefix, sm_scale, logit_cap, desc,
                         workspace, workspace_bytes, stream);
+}
+
+size_t extend_attention_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int extend_attention_fwd_noalloc(const void* q_extend, const void* k_extend, const void* v_extend, void* o,
+                                 const void* k_pool, const void* v_pool, const int32_t* qo_indptr,
+                                 const int32_t* kv_indptr, const int64_t* kv_indices, float sm_scale,
+                                 float logit_cap, const pkv_attn_desc_t* desc, void* stream) {
+  pkv::Tiling t;
+  int rc = check_desc(desc, &t);
+  if (rc != PKV_OK) return rc;
+  if (desc->bs == 0 || desc->total_q_tokens == 0) return ok();  // no query rows: nothing to write
+  // the scratch array is taken inside, once the sizes are known to fit; nothing
+  // in it needs to start at zero: the planner writes the plan header, the
+  // zero row and every work item, and each partial state is written before
+  // the merge reads it
+  return attention_call(q_extend, k_extend, v_extend, o, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices,
+                        nullptr, sm_scale, logit_cap, desc, nullptr, kNoAllocScratchBytes, stream,
+                        kNoAllocPartialBytes, true);
 }
 
 }  // extern "C"

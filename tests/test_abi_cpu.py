@@ -133,6 +133,21 @@ def call_fwd(d, ws_bytes=1 << 30, ptr=4096, ws=4096):
                                     ctypes.byref(d) if d is not None else None, ws, ws_bytes, None)
 
 
+def test_noalloc_rejects_batches_beyond_its_scratch_without_device():
+    lib = pkv.library()
+    assert lib.extend_attention_noalloc_scratch_bytes() == 32 << 20
+    p = 4096
+
+    def call(d):
+        return lib.extend_attention_fwd_noalloc(p, p, p, p, p, p, p, p, p, 0.0, 0.0, ctypes.byref(d), None)
+
+    assert call(desc(total_q_tokens=3_000_000, bs=64)) == -2
+    assert "no-allocation" in pkv.last_error() and "scratch" in pkv.last_error()
+    assert call(desc(lq=72, lv=72)) == -2
+    assert call(desc(num_kv_heads=7)) == -1
+    assert call(desc(bs=0)) == 0
+
+
 def test_fwd_argument_errors_without_device():
     assert call_fwd(None) == pkv.PkvError(-1, "").code == -1
     assert call_fwd(desc(lq=72, lv=72)) == -2
