@@ -11,8 +11,12 @@ Prints ONE JSON line:
             pairs x Hq x 2 (Lq + Lv), divided by the mean step time)
   roofline  the attention kernel alone: its TFLOP/s from HIP events recorded
             on its own stream around every launch in the timed region,
-            against the MI355X dense bf16 MFMA peak
+            against the MI355X dense bf16 MFMA peak (or its algorithmic
+            bytes against the HBM peak for batches under the ridge)
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  workloads the same figures (step and kernel times, bound, fraction of the
+            binding roofline, oracle sample) for every other workload, when
+            no --workload is named
 """
 
 from __future__ import annotations
@@ -38,11 +42,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None,
+                    help="one workload only (default: the llama8b headline plus every other workload)")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = enough to exceed 512 MiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--other-cpu-seconds", type=float, default=4.0,
+                    help="target CPU time of each other workload's oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel", default="auto", help="attention kernel preference: auto, r64, dl, attn")
+    ap.add_argument("--kernel", default="auto", help="attention kernel preference: auto, dl, attn")
     ap.add_argument("--op", default="attention", choices=["attention", "store", "gather", "decode"],
                     help="attention: the hot path; store / gather: the KV-cache store of the new tokens or the "
                          "request-to-token index gather of the same batch, reported in GB/s against HBM; "
@@ -118,9 +125,43 @@ def main():
     dev = torch.device("cuda", 0)
     if args.op == "decode":
         return bench_decode(args, dev, torch, pkv)
-    w = wl.get(args.workload)
+    name = args.workload or DEFAULT_WORKLOAD
     if args.op != "attention":
-        return bench_copy_op(args, w, dev, torch, pkv)
+        return bench_copy_op(args, wl.get(name), dev, torch, pkv)
+    line = bench_attention(args, name, dev, args.cpu_seconds)
+    if args.workload is None:
+        # every other workload, one after another, in the same run
+        line["workloads"] = {}
+        for other in wl.CONFIG_ORDER + wl.AUX_CONFIGS:
+            if other != name:
+                torch.cuda.empty_cache()
+                line["workloads"][other] = brief(bench_attention(args, other, dev, args.other_cpu_seconds))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def brief(line):
+    """The per-workload figures of a bench line."""
+    r = line["roofline"]
+    out = {"description": line["config"]["description"], "dtype": line["dtype"],
+           "ms_per_step": line["ms_per_step"], "ms_per_launch": r["ms_per_launch"],
+           "step_tflops": line["value"], "kernel": r["kernel"], "bound": r["bound"], "achieved": r["achieved"],
+           "peak": r["peak"], "unit": r["unit"], "frac": r["frac"], "traffic": r["traffic"],
+           "causal_gflop": line["config"]["causal_gflop"], "algorithmic_mb": line["config"]["algorithmic_mb"]}
+    if "tflops" in r:
+        out["kernel_tflops"] = r["tflops"]
+    if "cpu_baseline" in line:
+        out["cpu_baseline"] = line["cpu_baseline"]
+    return out
+
+
+def bench_attention(args, name, dev, cpu_seconds):
+    """The whole path on one workload: index build + extend attention per step."""
+    import torch
+    import paged_kv_extend_amd as pkv
+    import workloads as wl
+
+    w = wl.get(name)
     flops = w.causal_flops()
     algo_bytes = w.algorithmic_bytes()
     copies = args.copies or max(1, min(16, int(np.ceil(512e6 / algo_bytes))))
@@ -166,18 +207,19 @@ def main():
     ms_per_step = start.elapsed_time(stop) / args.steps
     ms_attn = attn_ms_total / max(calls, 1)
 
+    del sets
     peak = PEAK[w.cfg.dtype]
     # the kernel's bound: products above the ridge (peak flop/s over HBM
     # bytes/s), HBM below it (short extends over long prefixes)
     hbm_bound = flops / algo_bytes < peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     achieved = flops / (ms_attn * 1e-3) / 1e12
     traffic = None
-    if os.path.exists(args.traffic_json):
+    if os.path.exists(args.traffic_json) and args.path == "two-part":
         with open(args.traffic_json) as f:
             tj = json.load(f)
-        if (tj.get("workload") == args.workload and tj.get("kernel_source_sha") == kernel_source_sha()
-                and args.path == "two-part"):
-            traffic = tj.get("bytes_per_launch")
+        rec = tj.get("records", {}).get(name)
+        if rec and tj.get("kernel_source_sha") == kernel_source_sha():
+            traffic = rec.get("bytes_per_launch")
     line = {
         "metric": "extend-attention TFLOP/s (causal-adjusted) + % of bf16 MFMA peak, 1 GPU",
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
@@ -208,9 +250,8 @@ def main():
                       "tflops": round(achieved, 2)}),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
-    return 0
+        line["cpu_baseline"] = cpu_baseline(w, cpu_seconds)
+    return line
 
 
 def bench_copy_op(args, w, dev, torch, pkv):
@@ -365,8 +406,7 @@ def bench_decode(args, dev, torch, pkv):
     return 0
 
 
-ATTENTION_SOURCES = ("device_common.h", "pkv_internal.h", "attention.hip", "attention_dl.hip", "attention_r64.hip",
-                     "plan.hip")
+ATTENTION_SOURCES = ("device_common.h", "pkv_internal.h", "attention.hip", "attention_dl.hip", "plan.hip")
 DECODE_SOURCES = ("device_common.h", "pkv_internal.h", "decode.hip")
 
 

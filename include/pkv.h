@@ -365,9 +365,9 @@ size_t extend_attention_noalloc_scratch_bytes(void);
 /*
  * Process-wide kernel preference for later extend_attention_fwd calls, for
  * tests and benchmarks: "auto" (the default: the fastest measured kernel that
- * serves the shape), "r64" (64 query rows per wave; bf16, lq == lv == 128), "dl"
- * (direct global-to-LDS loads; bf16, head dims 64, 128, 256, and 576/512
- * with V inside K), "attn" (register-staged; every supported shape).  A
+ * serves the shape), "dl" (direct global-to-LDS loads; bf16, plain head dims
+ * 64 to 256 and 576/512 with V inside K), "attn" (register-staged; fp32 64
+ * and 128, bf16 64, 128, 256, 192/128, 288/256 and 576/512).  A
  * preferred kernel that does not serve a call's shape is passed over for the
  * automatic choice.  Results of every kernel meet the same accuracy bounds;
  * workspaces sized by extend_attention_workspace_size fit any choice.
@@ -394,7 +394,7 @@ int extend_attention_set_split(int rounds, int min_chunk_tiles);
 
 /*
  * Name of the attention kernel symbol that serves a call with `desc` and these
- * K/V base pointers ("attn_r64_kernel", "attn_dl_kernel" or "attn_kernel", as
+ * K/V base pointers ("attn_dl_kernel" or "attn_kernel", as
  * profilers list it; pass NULL new-token pointers for a unified call),
  * or NULL when desc is invalid.  The pointers are only compared (V inside K
  * selects a variant), never dereferenced.  For matching profiler output;

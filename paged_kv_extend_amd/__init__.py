@@ -241,7 +241,7 @@ def extend_attention_kernel_name(desc: AttnDesc, k_extend=None, v_extend=None, k
 
 
 def extend_attention_prefer_kernel(name: str) -> None:
-    """Process-wide kernel preference: "auto", "r64", "dl" or "attn" (tests, benchmarks)."""
+    """Process-wide kernel preference: "auto", "dl" or "attn" (tests, benchmarks)."""
     _check(library().extend_attention_prefer_kernel(name.encode()))
 
 

@@ -11,14 +11,13 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = ["api.cpp", "index_build.hip", "kv_cache.hip", "plan.hip", "attention.hip", "attention_dl.hip",
-           "attention_r64.hip", "decode.hip"]
+           "decode.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          # no packed fp32 instructions from the compiler
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# per-source additions: the 64-row kernel keeps its S tiles in ordinary vector
-# registers for the softmax, so its MFMA results are taken in VGPR form
-SOURCE_FLAGS = {"attention_r64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source additions to FLAGS (none at present)
+SOURCE_FLAGS = {}
 
 
 def _compile(src: str, verbose: bool) -> str:

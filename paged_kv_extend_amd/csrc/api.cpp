@@ -59,9 +59,8 @@ bool v_inside_k(const pkv_attn_desc_t& d, const void* k_extend, const void* v_ex
 }
 
 // The attention kernel that serves (dtype, lq, lv), with V inside K or not,
-// and its row / key tiling.  Automatic order: direct loads, 64 rows per wave,
-// register-staged.
-enum class Kernel { kNone, kR64, kDl, kAttn };
+// and its row / key tiling.  Automatic order: direct loads, register-staged.
+enum class Kernel { kNone, kDl, kAttn };
 
 std::atomic<int> g_prefer{0};  // Kernel preferred by extend_attention_prefer_kernel, 0 = automatic
 // Split granularity set by extend_attention_set_split (0: the defaults above)
@@ -71,32 +70,23 @@ std::atomic<int> g_min_chunk{0};
 // Tiling of kernel k for the shape, or false when k does not serve it.
 bool kernel_tiling(Kernel k, int dtype, int lq, int lv, bool v_in_k, pkv::Tiling* t) {
   switch (k) {
-    case Kernel::kR64: return pkv::r64_tiling(dtype, lq, lv, t);
     case Kernel::kDl: return pkv::dl_tiling(dtype, lq, lv, v_in_k, t);
     case Kernel::kAttn: return pkv::attn_tiling(dtype, lq, lv, t);
     default: return false;
   }
 }
 
-// (options: a sliding window or sinks, which the 64-row kernel does not serve)
-Kernel pick_kernel(int dtype, int lq, int lv, bool v_in_k, pkv::Tiling* t, bool options = false) {
+Kernel pick_kernel(int dtype, int lq, int lv, bool v_in_k, pkv::Tiling* t) {
   const Kernel pref = static_cast<Kernel>(g_prefer.load(std::memory_order_relaxed));
-  const auto serves = [&](Kernel k) {
-    return !(options && k == Kernel::kR64) && kernel_tiling(k, dtype, lq, lv, v_in_k, t);
-  };
+  const auto serves = [&](Kernel k) { return kernel_tiling(k, dtype, lq, lv, v_in_k, t); };
   if (pref != Kernel::kNone && serves(pref)) return pref;
-  for (Kernel k : {Kernel::kDl, Kernel::kR64, Kernel::kAttn})
+  for (Kernel k : {Kernel::kDl, Kernel::kAttn})
     if (serves(k)) return k;
   return Kernel::kNone;
 }
 
-bool has_options(const pkv_attn_desc_t& d) {
-  return d.sliding_window > 0 || d.sinks != nullptr || d.custom_mask != nullptr;
-}
-
 const char* kernel_symbol(Kernel k) {
   switch (k) {
-    case Kernel::kR64: return "attn_r64_kernel";
     case Kernel::kDl: return "attn_dl_kernel";
     case Kernel::kAttn: return "attn_kernel";
     default: return nullptr;
@@ -104,13 +94,13 @@ const char* kernel_symbol(Kernel k) {
 }
 
 // Resident attention workgroups on the current device, cached per (device, variant).
-int resident_slots(int dtype, int lq, int lv, bool v_in_k, bool options) {
+int resident_slots(int dtype, int lq, int lv, bool v_in_k) {
   static std::mutex mu;
   static std::unordered_map<long long, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   pkv::Tiling t;
-  const Kernel k = pick_kernel(dtype, lq, lv, v_in_k, &t, options);
+  const Kernel k = pick_kernel(dtype, lq, lv, v_in_k, &t);
   const long long key = ((long long)dev << 36) | ((long long)k << 33) | ((long long)v_in_k << 32) |
                         ((long long)dtype << 24) | ((long long)lq << 12) | lv;
   std::lock_guard<std::mutex> lk(mu);
@@ -121,7 +111,6 @@ int resident_slots(int dtype, int lq, int lv, bool v_in_k, bool options) {
     cus = 256;
   int per_cu = 1;
   switch (k) {
-    case Kernel::kR64: per_cu = pkv::r64_blocks_per_cu(lq); break;
     case Kernel::kDl: per_cu = pkv::dl_blocks_per_cu(lq, lv, v_in_k); break;
     default: per_cu = pkv::attention_blocks_per_cu(dtype, lq, lv); break;
   }
@@ -132,7 +121,7 @@ int resident_slots(int dtype, int lq, int lv, bool v_in_k, bool options) {
 
 // Row and key tiling of the kernel serving (dtype, lq, lv) with or without V inside K.
 bool tiling_for(const pkv_attn_desc_t& d, bool v_in_k, pkv::Tiling* t) {
-  return pick_kernel(d.dtype, d.lq, d.lv, v_in_k, t, has_options(d)) != Kernel::kNone;
+  return pick_kernel(d.dtype, d.lq, d.lv, v_in_k, t) != Kernel::kNone;
 }
 
 // Sizes derived from the descriptor; returns 0 and sets the error when invalid.
@@ -275,7 +264,7 @@ const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc, const void
   pkv::Tiling t;
   if (check_desc(desc, &t) != PKV_OK) return nullptr;
   const bool vk = v_inside_k(*desc, k_extend, v_extend, k_pool, v_pool);
-  return kernel_symbol(pick_kernel(desc->dtype, desc->lq, desc->lv, vk, &t, has_options(*desc)));
+  return kernel_symbol(pick_kernel(desc->dtype, desc->lq, desc->lv, vk, &t));
 }
 
 int build_unified_kv_indices(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
@@ -374,13 +363,13 @@ int extend_attention_prefer_kernel(const char* name) {
   static const struct {
     const char* name;
     Kernel k;
-  } names[] = {{"auto", Kernel::kNone}, {"r64", Kernel::kR64}, {"dl", Kernel::kDl}, {"attn", Kernel::kAttn}};
+  } names[] = {{"auto", Kernel::kNone}, {"dl", Kernel::kDl}, {"attn", Kernel::kAttn}};
   for (const auto& n : names)
     if (strcmp(name, n.name) == 0) {
       g_prefer.store(static_cast<int>(n.k), std::memory_order_relaxed);
       return ok();
     }
-  return fail(PKV_ERR_INVALID, "unknown kernel \"%s\" (auto, r64, dl, attn)", name);
+  return fail(PKV_ERR_INVALID, "unknown kernel \"%s\" (auto, dl, attn)", name);
 }
 
 int extend_attention_set_split(int rounds, int min_chunk_tiles) {
@@ -400,7 +389,7 @@ size_t extend_attention_workspace_size(const pkv_attn_desc_t* desc) {
   // K (which only the call shows) and on the kernel preference: size for
   // every kernel that could serve the shape
   size_t total = 0;
-  for (Kernel k : {Kernel::kR64, Kernel::kDl, Kernel::kAttn})
+  for (Kernel k : {Kernel::kDl, Kernel::kAttn})
     for (bool vk : {false, true}) {
       pkv::Tiling tk;
       if (kernel_tiling(k, desc->dtype, desc->lq, desc->lv, vk, &tk))
@@ -508,7 +497,7 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   pa.group = group;
   pa.bm = t.bm;
   pa.bn = t.bn;
-  pa.slots = resident_slots(d.dtype, d.lq, d.lv, vk, has_options(d));
+  pa.slots = resident_slots(d.dtype, d.lq, d.lv, vk);
   const int forced_rounds = g_split_rounds.load(std::memory_order_relaxed);
   const int forced_min = g_min_chunk.load(std::memory_order_relaxed);
   pa.min_chunk = forced_min > 0 ? forced_min : kMinChunkTiles;
@@ -570,8 +559,7 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   const auto ev = noalloc ? std::pair<hipEvent_t, hipEvent_t>{nullptr, nullptr} : profile_slot();
   if (ev.first) (void)hipEventRecord(ev.first, s);
   pkv::Tiling td;
-  switch (pick_kernel(d.dtype, d.lq, d.lv, vk, &td, has_options(d))) {
-    case Kernel::kR64: e = pkv::launch_r64(d.lq, a, pb.max_work, s); break;
+  switch (pick_kernel(d.dtype, d.lq, d.lv, vk, &td)) {
     case Kernel::kDl: e = pkv::launch_dl(d.lq, d.lv, vk, a, pb.max_work, s); break;
     default: e = pkv::launch_attention(d.dtype, d.lq, d.lv, a, pb.max_work, s); break;
   }

@@ -234,9 +234,5 @@ int attention_blocks_per_cu(int dtype, int lq, int lv);
 bool dl_tiling(int dtype, int lq, int lv, bool v_in_k, Tiling* t);
 hipError_t launch_dl(int lq, int lv, bool v_in_k, const AttnArgs& a, int64_t grid, hipStream_t s);
 int dl_blocks_per_cu(int lq, int lv, bool v_in_k);
-// The 64-rows-per-wave kernel (bf16, lq == lv == 128).
-bool r64_tiling(int dtype, int lq, int lv, Tiling* t);
-hipError_t launch_r64(int lq, const AttnArgs& a, int64_t grid, hipStream_t s);
-int r64_blocks_per_cu(int lq);
 
 }  // namespace pkv

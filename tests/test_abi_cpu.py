@@ -55,15 +55,15 @@ def test_kernel_name_per_variant():
 
 def test_kernel_preference():
     try:
-        pkv.extend_attention_prefer_kernel("r64")
-        assert kernel_name(desc()) == "attn_r64_kernel"
         pkv.extend_attention_prefer_kernel("attn")
         assert kernel_name(desc()) == "attn_kernel"
         # a preferred kernel that does not serve the shape is passed over
-        pkv.extend_attention_prefer_kernel("r64")
-        assert kernel_name(desc(lq=64, lv=64)) == "attn_dl_kernel"
-        with pytest.raises(pkv.PkvError):
-            pkv.extend_attention_prefer_kernel("fastest")
+        assert kernel_name(desc(lq=96, lv=96)) == "attn_dl_kernel"
+        pkv.extend_attention_prefer_kernel("dl")
+        assert kernel_name(desc(dtype=1, lq=64, lv=64)) == "attn_kernel"
+        for gone in ("fastest", "r64"):
+            with pytest.raises(pkv.PkvError):
+                pkv.extend_attention_prefer_kernel(gone)
     finally:
         pkv.extend_attention_prefer_kernel("auto")
     assert kernel_name(desc()) == "attn_dl_kernel"
@@ -82,7 +82,7 @@ def test_workspace_covers_every_kernel():
     d = desc()
     sizes = []
     try:
-        for k in ("auto", "r64", "dl", "attn"):
+        for k in ("auto", "dl", "attn"):
             pkv.extend_attention_prefer_kernel(k)
             sizes.append(lib.extend_attention_workspace_size(ctypes.byref(d)))
     finally:

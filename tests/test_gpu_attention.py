@@ -57,7 +57,7 @@ EDGE = [
     dict(name="group7", dtype="bf16", prefix_lens=[200, 17], extend_lens=[37, 100], hq=28, hkv=4, lq=128, lv=128),
     dict(name="fp32-128", dtype="fp32", prefix_lens=[40, 0, 100], extend_lens=[9, 50, 1], hq=4, hkv=2, lq=128, lv=128, sm_scale=0.05),
     dict(name="neg-scale", dtype="bf16", prefix_lens=[20], extend_lens=[20], hq=2, hkv=1, lq=64, lv=64, sm_scale=-0.1),
-    # head dim 128 (64 rows per wave): soft-cap and a negative scale, ragged groups
+    # head dim 128: soft-cap and a negative scale, ragged groups
     dict(name="cap-d128", dtype="bf16", prefix_lens=[90, 0, 300], extend_lens=[70, 130, 1], hq=12, hkv=4, lq=128,
          lv=128, logit_cap=20.0),
     dict(name="neg-d128", dtype="bf16", prefix_lens=[37, 64], extend_lens=[100, 3], hq=6, hkv=2, lq=128, lv=128,
@@ -146,7 +146,7 @@ def test_empty_batch_is_noop():
     assert dev["o"].numel() == 0
 
 
-@pytest.mark.parametrize("kernel", ["r64", "dl", "attn"])
+@pytest.mark.parametrize("kernel", ["dl", "attn"])
 def test_every_kernel_on_one_batch(kernel):
     # each kernel that serves bf16 head dim 128, on the same ragged batch with split key ranges
     w = wl.build(wl.CONFIGS["llama8b"], prefix_lens=np.array([0, 300, 77, 9000, 5]),
@@ -157,7 +157,7 @@ def test_every_kernel_on_one_batch(kernel):
     try:
         pkv.extend_attention_prefer_kernel(kernel)
         name = pkv.extend_attention_kernel_name(desc, dev["k_ext"], dev["v_ext"], dev["k_pool"], dev["v_pool"])
-        assert name == {"r64": "attn_r64_kernel", "dl": "attn_dl_kernel", "attn": "attn_kernel"}[kernel]
+        assert name == {"dl": "attn_dl_kernel", "attn": "attn_kernel"}[kernel]
         parity_full(w, f"llama8b-shape-{kernel}")
     finally:
         pkv.extend_attention_prefer_kernel("auto")

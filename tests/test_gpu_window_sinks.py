@@ -71,20 +71,3 @@ def test_unified_window_sinks():
     want = oracle.extend_attention_unified(w.q, w.k_pool, w.v_pool, w.qo_indptr, indptr, indices, plens,
                                            w.sm_scale, 0.0, "bf16", window=100, sinks=sinks)
     check(out_f64(dev), want, "bf16", "unified-w100-sinks")
-
-
-def test_options_pass_over_the_64_row_kernel():
-    w = wl.build(wl.CONFIGS["llama8b"], prefix_lens=np.array([100, 7]), extend_lens=np.array([90, 40]))
-    dev = wl.to_torch(w)
-    desc = pkv.make_desc(dev["q"], dev["k_ext"], dev["v_ext"], dev["o"], dev["k_pool"], dev["v_pool"], w.bs,
-                         w.num_prefix)
-    try:
-        pkv.extend_attention_prefer_kernel("r64")
-        assert pkv.extend_attention_kernel_name(desc, dev["k_ext"], dev["v_ext"], dev["k_pool"],
-                                                dev["v_pool"]) == "attn_r64_kernel"
-        desc.sliding_window = 16
-        assert pkv.extend_attention_kernel_name(desc, dev["k_ext"], dev["v_ext"], dev["k_pool"],
-                                                dev["v_pool"]) == "attn_dl_kernel"
-        run(w, 16, None, "r64-preferred-w16")
-    finally:
-        pkv.extend_attention_prefer_kernel("auto")
