@@ -40,6 +40,7 @@ extern "C" {
 #define PKV_ERR_WORKSPACE (-3)   /* workspace missing or smaller than the size query */
 #define PKV_ERR_CAPACITY (-4)    /* output index buffer too small */
 #define PKV_ERR_HIP (-5)         /* a HIP runtime call or kernel launch failed */
+#define PKV_ERR_RANGE (-6)       /* index or indptr out of range: debug build (libpkv_debug.so) only */
 
 /* Element types of q / k / v / o and the pools. */
 #define PKV_BF16 0

@@ -19,9 +19,12 @@ import torch
 __all__ = ["build_unified_kv_indices", "extend_attention_fwd", "extend_attention_fwd_unified",
            "extend_attention_workspace_size", "extend_attention_fwd_noalloc", "decode_attention_fwd", "decode_attention_workspace_size", "store_kv_cache", "gather_kv_indices",
            "extend_attention_kernel_name", "extend_attention_prefer_kernel", "extend_attention_set_split",
-           "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "LIB_PATH", "PkvError"]
+           "make_desc", "profile_enable", "profile_read", "last_error", "version", "library", "debug_library",
+           "LIB_PATH", "LIB_DEBUG_PATH", "PkvError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+# the same kernels with every index array checked on the device first (PKV_ERR_RANGE); one host sync per call
+LIB_DEBUG_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv_debug.so")
 
 PKV_BF16 = 0
 PKV_FP32 = 1
@@ -45,16 +48,30 @@ class AttnDesc(ctypes.Structure):
 
 
 _lib = None
+_lib_debug = None
 
 
 def library() -> ctypes.CDLL:
     """Load libpkv.so (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_extend_amd._build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def debug_library() -> ctypes.CDLL:
+    """Load libpkv_debug.so: the same C ABI, which also checks every index array against
+    the sizes passed (returning PKV_ERR_RANGE, -6) before any kernel reads it."""
+    global _lib_debug
+    if _lib_debug is None:
+        _lib_debug = _load(LIB_DEBUG_PATH)
+    return _lib_debug
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_kv_extend_amd._build`")
+    lib = ctypes.CDLL(path)
     P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.build_unified_kv_indices.argtypes = [P, P, P, P, P, i32, i64, i64, P, P, i64, P, P]
     lib.build_unified_kv_indices.restype = ctypes.c_int
@@ -91,7 +108,6 @@ def library() -> ctypes.CDLL:
     lib.extend_attention_set_split.restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

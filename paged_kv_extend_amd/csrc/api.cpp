@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <stddef.h>
+
 #include <algorithm>
 #include <atomic>
 #include <mutex>
@@ -195,6 +197,39 @@ pkv::WsLayout ws_layout(const pkv_attn_desc_t* d, const pkv::Tiling& t, const pk
   return l;
 }
 
+#ifdef PKV_DEBUG
+// Debug build: validate the index arrays on the device before anything reads
+// them, then wait for the verdict (the one host sync of the library, in this
+// build only).  flag: a device word of the workspace the launch sequence
+// does not use yet.
+int debug_check(int32_t* flag, const int32_t* qo_indptr, const int32_t* kv_indptr, const int64_t* kv_indices,
+                const int32_t* prefix_lens, int32_t bs, int64_t total_q_tokens, int64_t num_indices,
+                int64_t pool_slots, hipStream_t s) {
+  if (bs <= 0) return PKV_OK;
+  pkv::CheckArgs c;
+  c.qo_indptr = qo_indptr;
+  c.kv_indptr = kv_indptr;
+  c.kv_indices = kv_indices;
+  c.prefix_lens = prefix_lens;
+  c.bs = bs;
+  c.total_q_tokens = total_q_tokens;
+  c.num_indices = num_indices;
+  c.pool_slots = pool_slots;
+  c.flag = flag;
+  hipError_t e = hipMemsetAsync(flag, 0, sizeof(int32_t), s);
+  if (e == hipSuccess) e = pkv::launch_check_indices(c, s);
+  int32_t bad = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&bad, flag, sizeof bad, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "debug index check: %s", hipGetErrorString(e));
+  if (bad)
+    return fail(PKV_ERR_RANGE, "debug index check failed:%s%s%s%s", (bad & 1) ? " qo_indptr" : "",
+                (bad & 2) ? " kv_indptr" : "", (bad & 4) ? " a slot outside [0, pool_slots)" : "",
+                (bad & 8) ? " a negative prefix_lens" : "");
+  return PKV_OK;
+}
+#endif
+
 // Event pairs around attention launches while profiling is enabled.
 struct Profile {
   std::mutex mu;
@@ -257,7 +292,11 @@ int pkv_profile_read(double* total_ms, int64_t* calls) {
 
 const char* pkv_last_error(void) { return g_err; }
 
-const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+#ifdef PKV_DEBUG
+const char* pkv_version(void) { return "pkv 0.2.0 (gfx950, debug: index checks)"; }
+#else
+const char* pkv_version(void) { return "pkv 0.2.0 (gfx950)"; }
+#endif
 
 const char* extend_attention_kernel_name(const pkv_attn_desc_t* desc, const void* k_extend, const void* v_extend,
                                          const void* k_pool, const void* v_pool) {
@@ -485,6 +524,11 @@ int attention_call(const void* q_extend, const void* k_extend, const void* v_ext
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int group = d.num_q_heads / d.num_kv_heads;
+#ifdef PKV_DEBUG
+  rc = debug_check(reinterpret_cast<int32_t*>(ws + wl.header + offsetof(pkv::PlanHeader, pad)), qo_indptr,
+                   kv_indptr, kv_indices, prefix_lens, d.bs, d.total_q_tokens, d.num_prefix_indices, d.pool_slots, s);
+  if (rc != PKV_OK) return rc;
+#endif
 
   pkv::PlanArgs pa;
   pa.qo_indptr = qo_indptr;
@@ -783,6 +827,11 @@ int decode_attention_fwd(const void* q, void* o, const void* k_pool, const void*
     return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   char* ws = static_cast<char*>(workspace);
+#ifdef PKV_DEBUG
+  rc = debug_check(reinterpret_cast<int32_t*>(ws + z.part_ml), nullptr, kv_indptr, kv_indices, nullptr, d.bs, d.bs,
+                   d.num_prefix_indices, d.pool_slots, reinterpret_cast<hipStream_t>(stream));
+  if (rc != PKV_OK) return rc;
+#endif
   const double scale = sm_scale != 0.0f ? (double)sm_scale : 1.0 / sqrt((double)d.lq);
   const double log2e = 1.4426950408889634;
   pkv::DecodeArgs a;

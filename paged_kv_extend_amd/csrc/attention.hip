@@ -443,6 +443,8 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
     }
   } else {
     // unnormalised partial state of this chunk, one slot row per packed row
+    // (the merge reads only rows of the item's tokens: padding rows write nothing)
+    if (!valid) return;
     const int64_t prow = (int64_t)it.part * BM + wv * 32 + qi;
     float* pa = a.part_acc + prow * LV;
 #pragma unroll

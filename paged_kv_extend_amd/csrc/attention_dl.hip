@@ -652,6 +652,8 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
       }
     }
   } else {
+    // the merge reads only rows of the item's tokens: padding rows write nothing
+    if (!valid) return;
     const int64_t prow = (int64_t)it.part * BM + rg * 32 + qi;
     float* pa = a.part_acc + prow * C::LVR;  // rows of the real width
 #pragma unroll

@@ -186,6 +186,22 @@ struct GatherArgs {
 };
 hipError_t launch_gather_indices(const GatherArgs& a, hipStream_t s);
 
+// Index validation (launched by the debug build only).  The kv_indices read
+// are [kv_indptr[0], kv_indptr[bs]); flag gets bits set for each kind of
+// violation (qo_indptr 1, kv_indptr 2, slot 4, prefix_lens 8).
+struct CheckArgs {
+  const int32_t* qo_indptr;    // [bs + 1] or NULL (decode)
+  const int32_t* kv_indptr;    // [bs + 1]
+  const int64_t* kv_indices;
+  const int32_t* prefix_lens;  // [bs] or NULL
+  int32_t bs;
+  int64_t total_q_tokens;      // bound of qo_indptr[bs]
+  int64_t num_indices;         // bound of kv_indptr[bs] - kv_indptr[0]
+  int64_t pool_slots;
+  int32_t* flag;               // device word, zero before the launch
+};
+hipError_t launch_check_indices(const CheckArgs& a, hipStream_t s);
+
 hipError_t launch_index_build(const int32_t* prefix_kv_indptr, const int64_t* prefix_kv_indices,
                               const int32_t* extend_start_loc, const int32_t* extend_seq_lens,
                               const int64_t* extend_kv_indices, int32_t bs,

@@ -29,6 +29,18 @@ def test_exports_every_declared_function():
     assert "gfx950" in pkv.version()
 
 
+def test_debug_library_exports_the_same_functions():
+    names = header_functions()
+    lib = pkv.debug_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "debug" in lib.pkv_version().decode() and "debug" not in pkv.version()
+    # host-side checks are the same: a bad descriptor fails before any device work
+    d = desc(num_kv_heads=7)
+    assert lib.extend_attention_fwd(4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 0.0, 0.0,
+                                    ctypes.byref(d), 4096, 1 << 30, None) == -1
+
+
 def kernel_name(d, k_ext=4096, v_ext=8192, k_pool=12288, v_pool=16384):
     lib = pkv.library()
     n = lib.extend_attention_kernel_name(ctypes.byref(d), k_ext, v_ext, k_pool, v_pool)
