@@ -1,5 +1,5 @@
 // Merge of the chunks of split items, a launch of its own after the attention
-// launch.  In chunk order (deterministic):
+// launch.  In chunk order (deterministic), batch by batch:
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s acc_s 2^(m_s - M) / L
 // the log-sum-exp state merge (page "flashinfer_backend.py", forward_extend:
 // merge_state of the ragged and paged partial outputs), plus the sink term.
@@ -16,6 +16,8 @@
 #include "pkv_internal.h"
 
 namespace pkv {
+
+constexpr int kMergeBatch = 16;  // partial states loaded together per thread
 
 // Work of the merge launch: (merge record, block of rows) tasks, strided over
 // the grid; thread = (row of the block, 4 columns).  Rows hold lv columns
@@ -36,22 +38,44 @@ __global__ __launch_bounds__(256) void split_merge_kernel(AttnArgs a, int bm, in
     const int q0 = a.qo_indptr[mi.b], E = a.qo_indptr[mi.b + 1] - q0;
     const int r = mi.t * bm + row;
     if (row >= bm || r >= E * G || d >= lv) continue;
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int s = 0; s < mi.n; ++s) M = fmaxf(M, a.part_ml[((int64_t)(mi.part_base + s) * bm + row) * 2]);
-    float L = 0.0f;
+    // pieces in batches of kMergeBatch, every load of a batch in flight at
+    // once; the running state is rescaled when a batch raises the maximum
+    float M = -INFINITY, L = 0.0f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-    for (int s = 0; s < mi.n; ++s) {
-      const int64_t prow = (int64_t)(mi.part_base + s) * bm + row;
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
-      const float w = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
-      L += ml.y * w;
-      const float4 v = *reinterpret_cast<const float4*>(a.part_acc + prow * lv + d);
-      o.x += v.x * w;
-      o.y += v.y * w;
-      o.z += v.z * w;
-      o.w += v.w * w;
+    for (int s0 = 0; s0 < mi.n; s0 += kMergeBatch) {
+      float2 ml[kMergeBatch];
+      float4 v[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        ml[i] = make_float2(-INFINITY, 0.0f);
+        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (s0 + i < mi.n) {
+          const int64_t prow = (int64_t)(mi.part_base + s0 + i) * bm + row;
+          ml[i] = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
+          v[i] = *reinterpret_cast<const float4*>(a.part_acc + prow * lv + d);
+        }
+      }
+      float Mb = M;
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, ml[i].x);
+      if (Mb > M) {
+        const float sc = M == -INFINITY ? 0.0f : fast_exp2(M - Mb);
+        L *= sc;
+        o.x *= sc;
+        o.y *= sc;
+        o.z *= sc;
+        o.w *= sc;
+        M = Mb;
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const float w = ml[i].x == -INFINITY ? 0.0f : fast_exp2(ml[i].x - M);
+        L += ml[i].y * w;
+        o.x += v[i].x * w;
+        o.y += v[i].y * w;
+        o.z += v[i].z * w;
+        o.w += v[i].w * w;
+      }
     }
     const int tok = r / G, head = mi.g * G + r % G;
     if (a.sinks) L += fast_exp2(a.sinks[head] * kLog2e - M);

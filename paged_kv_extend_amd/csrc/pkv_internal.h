@@ -112,7 +112,7 @@ struct PlanArgs {
   void* zero_row;    // zeroed by the planner: kZeroRowBytes bytes
   WorkItem* work;    // [max_work]
   MergeItem* merge;  // [max_merge]
-  int32_t* scratch;  // [3 * bs + 1 + 3 * max_items], used when the batch exceeds the LDS arrays
+  int32_t* scratch;  // [3 * bs + 3 + 3 * max_items], used when the batch exceeds the LDS arrays
 };
 
 // Keys of sequence b as the attention kernels see them.

@@ -41,9 +41,9 @@ struct Shared {
   int32_t seq_base[kSeqLds + 1];  // first item of sequence b
   int32_t seq_e[kSeqLds];         // new tokens E_b
   int32_t seq_p[kSeqLds];         // prefix tokens P_b
-  int32_t cost[kItemLds];         // KV tiles of item n
-  int32_t cum[kItemLds];          // exclusive running sum of costs
+  int32_t cum[kItemLds + 1];      // exclusive running sum of the items' KV tiles
   int32_t pm[kItemLds];           // partial base << 16 | merge index (split items)
+  int32_t cb[kItemLds + 1];       // first chunk of item n (the item's cost until chunks are cut)
 };
 
 // Inclusive scan over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8
@@ -86,34 +86,24 @@ __device__ void block_excl_scan(const int (&v)[N], int (&ex)[N], int64_t (&total
   __syncthreads();
 }
 
-__device__ int64_t block_sum(int64_t v, Shared& sh) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  if ((threadIdx.x & 63) == 0) sh.wave_tot[threadIdx.x >> 6][0] = v;
-  __syncthreads();
-  int64_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += sh.wave_tot[w][0];
-  __syncthreads();
-  return t;
-}
-
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Per-item arrays in LDS when the batch fits (the only global reads are the
-// indptrs), else in the global scratch.  Items and sequences are handed out
-// in contiguous runs per thread, so each scan is a local pass, one block
-// scan and a second local pass, whatever the batch size.
+// indptrs), else in the global scratch.  Sequences, items and chunks are
+// handed out in contiguous runs per thread, so each pass is a local walk,
+// one block scan and a second local walk, whatever the batch size; the walks
+// over chunks spread an item cut into many chunks over many threads.
 template <bool LDS_ARRAYS>
 __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   const int tid = threadIdx.x;
   const int G = a.group, BM = a.bm, BN = a.bn, H = a.num_kv_heads;
-  // global scratch: seq_base[bs+1] | E[bs] | P[bs] | cost | cum | pm  (per item)
+  // global scratch: seq_base[bs+1] | E[bs] | P[bs] | cum[items+1] | pm[items] | cb[items+1]
   int32_t* seq_base = LDS_ARRAYS ? sh.seq_base : a.scratch;
   int32_t* seq_e = LDS_ARRAYS ? sh.seq_e : a.scratch + a.bs + 1;
   int32_t* seq_p = LDS_ARRAYS ? sh.seq_p : a.scratch + 2 * a.bs + 1;
-  int32_t* cost_of = LDS_ARRAYS ? sh.cost : a.scratch + 3 * a.bs + 1;
-  int32_t* cum_cost = LDS_ARRAYS ? sh.cum : cost_of + a.max_items;
-  int32_t* pm = LDS_ARRAYS ? sh.pm : cum_cost + a.max_items;
+  int32_t* cum = LDS_ARRAYS ? sh.cum : a.scratch + 3 * a.bs + 1;
+  int32_t* pm = LDS_ARRAYS ? sh.pm : cum + a.max_items + 1;
+  int32_t* cb = LDS_ARRAYS ? sh.cb : pm + a.max_items;
 
   // 1. per sequence: E, P and items H * ceil(E G / BM), exclusive scan
   const int spt = ceil_div(a.bs, kThreads);  // sequences per thread
@@ -166,43 +156,60 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     g = loc / T;
     t = loc % T;
   };
+  // the item after (b, g, t): next tile, next head, or next sequence with rows
+  auto next_item = [&](int& b, int& g, int& t) {
+    if (++t == ceil_div(seq_e[b] * G, BM)) {
+      t = 0;
+      if (++g == H) {
+        g = 0;
+        do ++b; while (b < a.bs && seq_e[b] == 0);
+      }
+    }
+  };
+  // tile of the first key any row of tile t of sequence b sees (sliding window)
+  auto first_tile = [&](int b, int t) {
+    return a.window > 0 ? max(0, seq_p[b] + (t * BM) / G - a.window) / BN : 0;
+  };
   const int ipt = ceil_div(n_items, kThreads);  // items per thread, contiguous
   const int n0 = min(n_items, tid * ipt), n1 = min(n_items, n0 + ipt);
 
   // 2. cost of every item in KV tiles (keys up to the last token of its rows)
-  int64_t my_total = 0;
+  //    and its running sum; cb holds the costs until the chunks are cut
+  int my_total = 0;
   if (n0 < n1) {
     int b, g, t;
     decode(n0, b, g, t);
     for (int n = n0; n < n1; ++n) {
       const int row_hi = min((t + 1) * BM, seq_e[b] * G) - 1;
-      // tiles from the first key any row of the item sees (sliding window) to its last
-      const int first = a.window > 0 ? max(0, seq_p[b] + (t * BM) / G - a.window) / BN : 0;
       // with a custom mask every key of the sequence may be seen
       const int keys = !a.masked ? seq_p[b] + row_hi / G + 1
                                  : (a.prefix_lens ? a.kv_indptr[b + 1] - a.kv_indptr[b] : seq_p[b] + seq_e[b]);
       // (at least one tile: size classes and chunk ranges assume it)
-      const int cost = max(1, ceil_div(keys, BN) - first);
-      cost_of[n] = cost;
+      const int cost = max(1, ceil_div(keys, BN) - first_tile(b, t));
+      cb[n] = cost;
       my_total += cost;
-      // next item: next tile, next head, or next sequence
-      const int T = ceil_div(seq_e[b] * G, BM);
-      if (++t == T) {
-        t = 0;
-        if (++g == H) {
-          g = 0;
-          do ++b; while (b < a.bs && seq_e[b] == 0);
-        }
-      }
+      next_item(b, g, t);
     }
   }
-  const int64_t total = block_sum(my_total, sh);
+  int64_t total;
+  {
+    int v[1] = {my_total}, ex[1];
+    int64_t tot[1];
+    block_excl_scan<1>(v, ex, tot, sh);
+    int run = ex[0];
+    for (int n = n0; n < n1; ++n) {
+      cum[n] = run;
+      run += cb[n];
+    }
+    if (tid == 0) cum[n_items] = (int)tot[0];
+    total = tot[0];
+  }
 
   // 3. chunk limit: a 1/rounds share of the average work per resident
   //    workgroup (so that heaviest-first placement can even out the CUs),
   //    grown until the split chunks fit the partial-state budget; and
   // 4. with the limit that fits, in the same block scan: partial-slot and
-  //    merge-record offsets of split items, running cost, number of chunks
+  //    merge-record offsets of split items and the first chunk of every item
   const int64_t shares = (int64_t)a.slots * (a.rounds > 0 ? a.rounds : 1);
   int64_t chunk = (total + shares - 1) / shares;
   if (chunk < a.min_chunk) chunk = a.min_chunk;
@@ -210,33 +217,34 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   auto pieces = [&](int c) { return c > chunk ? (int)((uint32_t)(c - 1) / (uint32_t)chunk) + 1 : 1; };
   int mcarry, n_chunks;
   for (;;) {
-    int v[4] = {0, 0, 0, 0}, ex[4];
-    int64_t tot[4];
+    int v[3] = {0, 0, 0}, ex[3];
+    int64_t tot[3];
     for (int n = n0; n < n1; ++n) {
-      const int c = cost_of[n], k = pieces(c);
+      const int k = pieces(cb[n]);
       v[0] += k > 1 ? k : 0;
       v[1] += k > 1 ? 1 : 0;
-      v[2] += c;
-      v[3] += k;
+      v[2] += k;
     }
-    block_excl_scan<4>(v, ex, tot, sh);
+    block_excl_scan<3>(v, ex, tot, sh);
     if (tot[0] > a.part_budget) {
       chunk *= 2;
       continue;
     }
     for (int n = n0; n < n1; ++n) {
-      const int c = cost_of[n], k = pieces(c);
+      const int k = pieces(cb[n]);
       // partial bases < part_budget <= 4096 and merge indices < part_budget fit 16 bits each
       pm[n] = (ex[0] << 16) | ex[1];
-      cum_cost[n] = ex[2];
+      cb[n] = ex[2];  // from here on the item's cost is cum[n + 1] - cum[n]
       ex[0] += k > 1 ? k : 0;
       ex[1] += k > 1 ? 1 : 0;
-      ex[2] += c;
+      ex[2] += k;
     }
+    if (tid == 0) cb[n_items] = (int)tot[2];
     mcarry = (int)tot[1];
-    n_chunks = (int)tot[3];
+    n_chunks = (int)tot[2];
     break;
   }
+  __syncthreads();  // cum, pm and cb complete before the walks over chunks
 
   // 5. XCD bin of every chunk (midpoint rule), then heaviest first inside a bin
   // size class of a chunk of sz tiles (sizes are <= chunk); only orders
@@ -255,22 +263,41 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     for (int x = 0; x < kMaxXcd; ++x) bnd2[x] = 2 * ((x + 1) * q + ((x + 1) * rem) / X);
   }
   auto bin_of = [&](int n, int k0, int k1) {
-    const int64_t mid2 = 2 * (int64_t)cum_cost[n] + k0 + k1;
+    const int64_t mid2 = 2 * (int64_t)cum[n] + k0 + k1;
     int x = 0;
 #pragma unroll
     for (int i = 0; i < kMaxXcd - 1; ++i) x += (i < X - 1 && mid2 >= bnd2[i]) ? 1 : 0;
     return x;
   };
-  // tile range of chunk s of k over c tiles: full chunks of `chunk` tiles and
-  // the remainder last (chunks of mixed sizes let the heaviest-first
-  // placement fill the last round, where equal pieces would quantise it)
-  auto chunk_range = [&](int c, int s, int k, int& k0, int& k1) {
-    if (k == 1) {
-      k0 = 0;
-      k1 = c;
-    } else {
-      k0 = (int)(s * chunk);
-      k1 = min(c, (int)((s + 1) * chunk));
+  // chunks in contiguous runs per thread; the item of the run's first chunk
+  // is the last n with cb[n] <= j0 (every item has at least one chunk)
+  const int cpt = ceil_div(n_chunks, kThreads);
+  const int j0 = min(n_chunks, tid * cpt), j1 = min(n_chunks, j0 + cpt);
+  int n_first = 0;
+  if (j0 < j1) {
+    int lo = 0, hi = n_items - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cb[mid] <= j0) lo = mid; else hi = mid - 1;
+    }
+    n_first = lo;
+  }
+  // visit(n, b, g, t, s, k, k0, k1) for the thread's chunks in order: piece s
+  // of the k of item n = (b, g, t), KV tiles k0 .. k1 - 1 of the item's range;
+  // full chunks of `chunk` tiles and the remainder last (chunks of mixed sizes
+  // let the heaviest-first placement fill the last round, where equal pieces
+  // would quantise it)
+  auto walk = [&](auto&& visit) {
+    if (j0 >= j1) return;
+    int n = n_first, b, g, t;
+    decode(n, b, g, t);
+    for (int j = j0; j < j1; ++j) {
+      const int base = cb[n], k = cb[n + 1] - base, s = j - base;
+      const int c = cum[n + 1] - cum[n];
+      const int k0 = k == 1 ? 0 : (int)(s * chunk);
+      const int k1 = k == 1 ? c : min(c, (int)((s + 1) * chunk));
+      visit(n, b, g, t, s, k, k0, k1);
+      if (s + 1 == k && ++n < n_items) next_item(b, g, t);
     }
   };
   constexpr int kPer = kMaxXcd * kBuckets / kThreads;  // counters per thread in the scan
@@ -278,14 +305,9 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   for (int attempt = 0; attempt < 2; ++attempt) {
     for (int i = tid; i < kMaxXcd * kBuckets; i += kThreads) sh.bucket[i] = 0;
     __syncthreads();
-    for (int n = n0; n < n1; ++n) {
-      const int c = cost_of[n], k = pieces(c);
-      for (int s = 0; s < k; ++s) {
-        int k0, k1;
-        chunk_range(c, s, k, k0, k1);
-        atomicAdd(&sh.bucket[bin_of(n, k0, k1) * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1);
-      }
-    }
+    walk([&](int n, int, int, int, int, int, int k0, int k1) {
+      atomicAdd(&sh.bucket[bin_of(n, k0, k1) * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1);
+    });
     __syncthreads();
     // one exclusive scan over all (bin, class) counters, kPer per thread; a
     // bin's ranks are offsets from its first counter's scan value
@@ -330,62 +352,44 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     a.hdr->total_tiles = (int32_t)total;
     a.hdr->num_items = n_items;
   }
-  if (n0 < n1) {
-    int b, ig, itt;
-    decode(n0, b, ig, itt);
-    for (int n = n0; n < n1; ++n) {
-      const int c = cost_of[n], k = pieces(c);
-      const int pbase = (int)((uint32_t)pm[n] >> 16), midx = pm[n] & 0xFFFF;
-      const int first = a.window > 0 ? max(0, seq_p[b] + (itt * BM) / G - a.window) / BN : 0;
-      for (int s = 0; s < k; ++s) {
-        int k0, k1;
-        chunk_range(c, s, k, k0, k1);
-        const int x = bin_of(n, k0, k1);
-        const int rank = atomicAdd(&sh.bucket[x * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1) -
-                         sh.bin_start[x];
-        WorkItem w;
-        w.b = b;
-        w.g = ig;
-        w.t = itt;
-        w.kt_begin = first + k0;
-        w.kt_end = first + k1;
-        w.part = k > 1 ? pbase + s : -1;
-        w.merge = k > 1 ? midx : -1;
-        w.pad0 = 0;
-        a.work[rank * X + x] = w;
-      }
-      if (k > 1) {
-        MergeItem m;
-        m.b = b;
-        m.g = ig;
-        m.t = itt;
-        m.part_base = pbase;
-        m.n = k;
-        m.pad2 = 0;
-        m.pad0 = m.pad1 = 0;
-        a.merge[midx] = m;
-      }
-      const int T = ceil_div(seq_e[b] * G, BM);
-      if (++itt == T) {
-        itt = 0;
-        if (++ig == H) {
-          ig = 0;
-          do ++b; while (b < a.bs && seq_e[b] == 0);
-        }
-      }
+  walk([&](int n, int b, int g, int t, int s, int k, int k0, int k1) {
+    const int x = bin_of(n, k0, k1);
+    const int rank =
+        atomicAdd(&sh.bucket[x * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1) - sh.bin_start[x];
+    const int pbase = (int)((uint32_t)pm[n] >> 16), midx = pm[n] & 0xFFFF;
+    const int first = first_tile(b, t);
+    WorkItem w;
+    w.b = b;
+    w.g = g;
+    w.t = t;
+    w.kt_begin = first + k0;
+    w.kt_end = first + k1;
+    w.part = k > 1 ? pbase + s : -1;
+    w.merge = k > 1 ? midx : -1;
+    w.pad0 = 0;
+    a.work[rank * X + x] = w;
+    if (k > 1 && s == 0) {
+      MergeItem m;
+      m.b = b;
+      m.g = g;
+      m.t = t;
+      m.part_base = pbase;
+      m.n = k;
+      m.pad2 = 0;
+      m.pad0 = m.pad1 = 0;
+      a.merge[midx] = m;
     }
-  }
-  // unused slots of shorter bins hold empty items
-  for (int x = 0; x < X; ++x) {
-    for (int rank = sh.bin_count[x] + tid; rank < max_count; rank += kThreads) {
-      WorkItem w;
-      w.b = -1;
-      w.g = w.t = w.kt_begin = w.kt_end = 0;
-      w.part = -1;
-      w.merge = -1;
-      w.pad0 = 0;
-      a.work[rank * X + x] = w;
-    }
+  });
+  // unused slots of shorter bins hold empty items (slot i = rank X + x)
+  for (int i = tid; i < max_count * X; i += kThreads) {
+    if (i / X < sh.bin_count[i % X]) continue;
+    WorkItem w;
+    w.b = -1;
+    w.g = w.t = w.kt_begin = w.kt_end = 0;
+    w.part = -1;
+    w.merge = -1;
+    w.pad0 = 0;
+    a.work[i] = w;
   }
 }
 
