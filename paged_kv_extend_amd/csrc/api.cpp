@@ -188,7 +188,7 @@ pkv::WsLayout ws_layout(const pkv_attn_desc_t* d, const pkv::Tiling& t, const pk
   l.merge = off;
   off = align_up(off + sizeof(pkv::MergeItem) * (size_t)(pb.max_merge > 0 ? pb.max_merge : 1), 256);
   l.scratch = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)(3 * d->bs + 3 + 3 * pb.max_items), 256);
+  off = align_up(off + sizeof(int32_t) * (size_t)(6 * d->bs + 3 + 3 * pb.max_items), 256);
   l.part_ml = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)pb.part_budget * t.bm, 256);
   l.part_acc = off;

@@ -122,15 +122,21 @@ __global__ __launch_bounds__(256, MINB) void attn_kernel(AttnArgs a) {
   T* __restrict__ Ks = lds;
   T* __restrict__ Vs = lds + C::K_ELEMS;
 
-  if ((int)blockIdx.x >= a.hdr->num_work) return;
+  // the work record and the plan header in one round trip: the grid is the
+  // workspace's capacity of records, so every block index names a record.
+  // (Left alone, the compiler loads each piece right before its first use,
+  // one round trip after another; the empty asm takes a field of every 16
+  // bytes and the header before the branch.)
   const WorkItem it = a.work[blockIdx.x];
-  if (it.b < 0) return;  // empty placement slot
+  const int num_work = a.hdr->num_work;
+  asm volatile("" ::"s"(it.b), "s"(it.kt_end), "s"(it.q0), "s"(it.n_idx), "s"(num_work));
+  if (it.b < 0 || (int)blockIdx.x >= num_work) return;  // empty or unused placement slot
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qi = lane & 31, hi = lane >> 5;
   const int G = a.group;
   const int b = it.b, g = it.g;
   const bool causal = !OPT || a.custom_mask == nullptr;
-  const SeqKeys sk = seq_keys(a.qo_indptr, a.kv_indptr, a.prefix_lens, b, causal);
+  const SeqKeys sk = item_keys(it);
   // last visible key of a row of token i: the diagonal, or every key with a custom mask
   auto last_key = [&](int i) __attribute__((always_inline)) {
     return causal ? min(sk.P + i, sk.n_keys - 1) : sk.n_keys - 1;

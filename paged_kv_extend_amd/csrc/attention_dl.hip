@@ -98,20 +98,22 @@ struct DlCfg {
   // of the next tile right after each barrier and waves 4..7 its V rows after
   // their S = K Q^T products, so while one wave of a SIMD waits for the
   // memory pipeline to take its loads, the other has products to run.
-  static constexpr bool OFFLOAD = SPLIT == 1 && NW == 8;
+  static constexpr bool OFFLOAD = SPLIT == 1 && NW == 8 && NS == 2;
   static constexpr int LOADERS = OFFLOAD ? NW / 2 : NW;   // waves per load group
   static constexpr int TW = OFFLOAD ? NW / 2 : 0;         // the wave that builds tables
   static constexpr int L = OFFLOAD ? 2 * V_LOADS : K_LOADS + V_LOADS;  // tile loads per wave per tile
   static constexpr int I = BN * 8 / 256;  // row-slot loads (64 lanes x 4 bytes) per tile, table wave
   // waits at the top of an iteration (see the loop): outstanding loads allowed
   static constexpr int W_OTHER = (NS - 2) * L;
-  static constexpr int W_TABLE = (NS - 2) * (I + L) < 2 * L + I ? (NS - 2) * (I + L) : 2 * L + I;
+  // (the row slots of a tile are requested in the same group as the tile
+  // NS-1 groups before it, so the tile's wait is the binding one)
+  static constexpr int W_TABLE = (NS - 2) * (I + L);
   static constexpr int XCH_BYTES = SPLIT > 1 ? NW * BN * 32 * 4 : 0;  // S^T halves exchanged
   static_assert(CK == 8 || CK == 16 || CK == 32 || CK == 72, "lq");
   static_assert(VK ? LV <= LQ : (CV == 8 || CV == 16 || CV == 32), "lv");
   static_assert(!WIDE || VK, "576-wide rows only with V inside K");
   static_assert(K_CHUNKS >= NW && (V_CHUNKS == 0 || V_CHUNKS >= NW), "every wave has a chunk to repeat");
-  static_assert(NS >= 2 && W_TABLE < 64 && W_OTHER < 64, "pipeline depth");
+  static_assert(NS >= 2 && NS <= 5 && W_TABLE < 64 && W_OTHER < 64, "pipeline depth (slot ring of 4)");
   static_assert(!OFFLOAD || (NS == 2 && K_LOADS == V_LOADS), "staggered loads: every wait is vmcnt(0)");
   static_assert(RG >= 2 || SPLIT == 1, "split variant: at least two row groups");
   static_assert(QD % 16 == 0 && VD % 32 == 0, "split");
@@ -167,10 +169,22 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   __shared__ gptr<T> vptr[NS][BN];
   __shared__ __attribute__((aligned(16))) int64_t slots[4][BN];  // row slots of later tiles, slot kt & 3
 
-  if ((int)blockIdx.x >= a.hdr->num_work) return;
+  // the work record and the plan header in one round trip: the grid is the
+  // workspace's capacity of records, so every block index names a record.
+  // (Left alone, the compiler loads each piece right before its first use,
+  // one round trip after another; the empty asm takes a field of every 16
+  // bytes and the header before the branch.)
   const WorkItem it = a.work[blockIdx.x];
-  if (it.b < 0) return;  // empty placement slot
+  const int num_work = a.hdr->num_work;
+  asm volatile("" ::"s"(it.b), "s"(it.kt_end), "s"(it.q0), "s"(it.n_idx), "s"(num_work));
+  if (it.b < 0 || (int)blockIdx.x >= num_work) return;  // empty or unused placement slot
   const int tid = threadIdx.x, lane = tid & 63;
+  // the lane index the loop's table and load addressing starts from: the
+  // 576-wide variant, at its register limit, re-derives those per-lane
+  // addresses on every trip from this copy (see the loop) -- a few VALU
+  // operations -- where the compiler would otherwise keep them across the
+  // loop and spill them
+  int ln = lane;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
   const int rg = wv % C::RG, half = wv / C::RG;  // row group; which half of Q dims / O columns
   const int qi = lane & 31, hi = lane >> 5;
@@ -183,7 +197,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   const int G = a.group;
   const int b = it.b, g = it.g;
   const bool causal = !OPT || a.custom_mask == nullptr;
-  const SeqKeys sk = seq_keys(a.qo_indptr, a.kv_indptr, a.prefix_lens, b, causal);
+  const SeqKeys sk = item_keys(it);
   const int q0 = sk.q0, E = sk.E, kvs = sk.kvs, P = sk.P;
   const int R = E * G;
   // last visible key of a row of token i: the diagonal, or every key with a custom mask
@@ -210,6 +224,10 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   const gptr<T> vext = (gptr<T>)a.v_ext;
   const gptr<T> zrow = (gptr<T>)a.zero_row;
   const int kt0 = it.kt_begin, kt1 = it.kt_end;
+  // last key whose K/V rows are loaded: the tiles the pipeline requests past
+  // the chunk's range (so that every trip has the same loads in flight) read
+  // the zero row, not the next chunk's keys
+  const int key_load_last = min(key_last, kt1 * BN - 1);
 
   // ---- Q^T operand (B) in registers, negated when the scale is negative
   bf16x8 qr[NQ];
@@ -237,7 +255,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   auto key_ptrs = [&](int j, int64_t slot, gptr<T>& kp, gptr<T>& vp) __attribute__((always_inline)) {
     kp = zrow;
     vp = zrow;
-    if (j <= key_last) {
+    if (j <= key_load_last) {
       if (j < sk.n_idx) {
         kp = kpool_g + slot * kp_ss;
         vp = vpool_g + slot * vp_ss;
@@ -251,7 +269,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   // table of tile kt from the row slots already in LDS (table wave)
   auto write_table = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = lane; e < (BN > 64 ? BN : 64); e += 64) {
+    for (int e = ln; e < (BN > 64 ? BN : 64); e += 64) {
       if (e < BN) {
         gptr<T> kp, vp;
         key_ptrs(kt * BN + e, slots[kt & 3][e], kp, vp);
@@ -265,10 +283,10 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   auto issue_slots = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::I; ++i) {
-      const int o = i * 256 + lane * 4;  // byte offset in the tile's slot block
+      const int o = i * 256 + ln * 4;  // byte offset in the tile's slot block
       const int j = kt * BN + o / 8;
       gptr<char> src = (gptr<char>)zrow;
-      if (j < sk.n_idx && j <= key_last) src = (gptr<char>)a.kv_indices + (int64_t)(kvs + j) * 8 + (o & 4);
+      if (j < sk.n_idx && j <= key_load_last) src = (gptr<char>)a.kv_indices + (int64_t)(kvs + j) * 8 + (o & 4);
       load_lds_4((gptr<void>)src, lds_addr(&slots[kt & 3][0]) + i * 256);
     }
   };
@@ -297,7 +315,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
       if (do_k) {
 #pragma unroll
         for (int i = 0; i < C::K_LOADS; ++i) {
-          const unsigned off = (unsigned)kchunk(i, vw) * 1024u + (unsigned)lane * 16u;
+          const unsigned off = (unsigned)kchunk(i, vw) * 1024u + (unsigned)ln * 16u;
           const unsigned row = off / (LQ * 2), p = (off % (LQ * 2)) / 16;
           const unsigned c = (unsigned)swz_k<C>(row, p);
           ksrc[q][i] = C::CKR < C::CK && c >= (unsigned)C::CKR ? zrow : kptr[kt % NS][row] + c * 8u;
@@ -306,7 +324,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
       if (do_v) {
 #pragma unroll
         for (int i = 0; i < C::V_LOADS; ++i) {
-          const unsigned off = (unsigned)vchunk(i, vw) * 1024u + (unsigned)lane * 16u;
+          const unsigned off = (unsigned)vchunk(i, vw) * 1024u + (unsigned)ln * 16u;
           const unsigned row = off / (LV * 2), p = (off % (LV * 2)) / 16;
           const unsigned c = (unsigned)swz_v<C>(row, p);
           vsrc[q][i] = C::CVR < C::CV && c >= (unsigned)C::CVR ? zrow : vptr[kt % NS][row] + c * 8u;
@@ -360,35 +378,40 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   float l_run = 0.0f;       // this lane's share of the running sum
 
   // Pipeline.  Iteration kt computes tile kt while tiles kt+1 .. kt+NS-2 are
-  // in flight; after its barrier it requests the row slots of tile kt+NS+1
-  // (table wave) and then tile kt+NS-1.  Tiles and slots past the end of the
+  // in flight; after its barrier it requests the row slots of tile kt+2NS-2
+  // (table wave) and then tile kt+NS-1: a tile's slots get as many groups of
+  // lead as its rows (NS-1), so deeper stages deepen both.  Tiles and slots past the end of the
   // range are requested too (zero rows, unused), so every wave has the same
   // number of loads in flight on every trip and the waits are fixed counts.
   if (kt0 < kt1) {
-    // tables of the first NS-1 tiles straight from global memory
+    // tables of the first NS-1 tiles straight from global memory: every
+    // lane's slots first (from the index array, or the zero row's 8 zero
+    // bytes), so that they come back in one round trip
+    constexpr int EPL = (BN + 63) / 64;  // keys per lane
     for (int v = wv; v < NS - 1; v += C::NW) {
+      int64_t sl[EPL];
 #pragma unroll
-      for (int e = lane; e < (BN > 64 ? BN : 64); e += 64) {
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i, j = (kt0 + v) * BN + e;
+        const bool real = e < BN && j < sk.n_idx && j <= key_load_last;
+        sl[i] = *(real ? (gptr<int64_t>)a.kv_indices + ((int64_t)kvs + j) : (gptr<int64_t>)zrow);
+      }
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
         if (e < BN) {
-          const int j = (kt0 + v) * BN + e;
-          const int64_t slot = (j < sk.n_idx && j <= key_last) ? ((gptr<int64_t>)a.kv_indices)[kvs + j] : 0;
           gptr<T> kp, vp;
-          key_ptrs(j, slot, kp, vp);
+          key_ptrs((kt0 + v) * BN + e, sl[i], kp, vp);
           kptr[(kt0 + v) % NS][e] = kp;
           vptr[(kt0 + v) % NS][e] = vp;
         }
       }
     }
     __syncthreads();
-    // with two stages, the first trip's table comes from slots no earlier
-    // group carries
-    if constexpr (NS == 2) {
-      if (wv == C::TW) issue_slots(kt0 + 1);
-    }
     // the groups that iterations kt0-NS+1 .. kt0-1 would have issued
 #pragma unroll
     for (int v = 0; v < NS - 1; ++v) {
-      if (wv == C::TW) issue_slots(kt0 + v + 2);
+      if (wv == C::TW) issue_slots(kt0 + NS - 1 + v);
       issue_tile(kt0 + v);
     }
   }
@@ -450,7 +473,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          xw[(kb * 4 + q4) * 64 + lane] = f32x4{s[kb][4 * q4], s[kb][4 * q4 + 1], s[kb][4 * q4 + 2], s[kb][4 * q4 + 3]};
+          xw[(kb * 4 + q4) * 64 + ln] = f32x4{s[kb][4 * q4], s[kb][4 * q4 + 1], s[kb][4 * q4 + 2], s[kb][4 * q4 + 3]};
     }
     wait_lds();
     barrier_fence();
@@ -460,7 +483,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
         f32x16 o;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 v = xr[(kb * 4 + q4) * 64 + lane];
+          const f32x4 v = xr[(kb * 4 + q4) * 64 + ln];
           o[4 * q4] = v[0];
           o[4 * q4 + 1] = v[1];
           o[4 * q4 + 2] = v[2];
@@ -581,9 +604,9 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
     }
   };
 
-  // Top of iteration kt.  Tile kt was requested NS-1 groups ago and the row
-  // slots of tile kt+NS-1 two groups ago (first in that group): wait until at
-  // most the later loads are outstanding.  The table wave then writes table kt+NS-1
+  // Top of iteration kt.  Tile kt and the row slots of tile kt+NS-1 were
+  // requested NS-1 groups ago (the slots first): wait until at most the later
+  // loads are outstanding.  The table wave then writes table kt+NS-1
   // (its slot held table kt-1, issued long ago) before the barrier that
   // publishes it and tile kt.
   auto tile_top = [&](int kt) __attribute__((always_inline)) {
@@ -596,10 +619,11 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
     }
     barrier_fence();
   };
-  // the group of iteration kt: row slots of tile kt+NS+1 (table wave) and tile
-  // kt+NS-1 into stage (kt-1) % NS, which tile kt-1 no longer needs
+  // the group of iteration kt: row slots of tile kt+2NS-2 (table wave; ring
+  // entry of tile kt+NS-1, whose table was written before the barrier) and
+  // tile kt+NS-1 into stage (kt-1) % NS, which tile kt-1 no longer needs
   auto issue_group = [&](int kt) __attribute__((always_inline)) {
-    if (wv == C::TW) issue_slots(kt + NS + 1);
+    if (wv == C::TW) issue_slots(kt + 2 * NS - 2);
     if constexpr (C::OFFLOAD) {
       if (wv < C::LOADERS) issue_loads(kt + NS - 1, true, false);
     } else {
@@ -608,6 +632,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   };
 
   for (int kt = kt0; kt < kt1; ++kt) {
+    if constexpr (C::WIDE || OPT) asm volatile("" : "+v"(ln));  // (ln is lane; the compiler no longer knows it)
     tile_top(kt);
     issue_group(kt);
     const bool act = active(kt);
@@ -701,6 +726,8 @@ int dl_occupancy_t() {
 // bf16 variants served here: (lq, lv, key tile, V inside K, 32-row groups,
 // waves per row group, LDS stages, real plain head dim in a wider tile or 0,
 // workgroups per CU)
+// (lq, lv, keys per tile, V inside K, row groups, waves per row group,
+//  stages, real plain head dim, min blocks per CU)
 #define PKV_DL_VARIANTS(X)                   \
   X(64, 64, 64, false, 4, 1, 4, 0, 2)        \
   X(128, 128, 128, false, 8, 1, 2, 0, 1)     \

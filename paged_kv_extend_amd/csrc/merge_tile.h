@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(AttnArgs a, int bm, in
   for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
     const MergeItem mi = a.merge[task / blocks];
     const int row = (task % blocks) * RPB + row_in;
-    const int q0 = a.qo_indptr[mi.b], E = a.qo_indptr[mi.b + 1] - q0;
+    const int q0 = mi.q0, E = mi.E;
     const int r = mi.t * bm + row;
     if (row >= bm || r >= E * G || d >= lv) continue;
     // pieces in batches of kMergeBatch, every load of a batch in flight at

@@ -19,13 +19,20 @@ struct WorkItem {
   int32_t b, g, t, kt_begin, kt_end, part;
   int32_t merge;  // merge record of a split item's chunk, else -1
   int32_t pad0;
+  // sequence b's keys as the planner read them from the index pointers, so
+  // that a workgroup's first loads depend on this record alone
+  int32_t q0, E;      // first new-token row, new tokens
+  int32_t kvs, P;     // first index of the sequence, prefix keys
+  int32_t n_idx;      // keys read through kv_indices: j < n_idx
+  int32_t n_keys;     // keys that exist: j < n_keys
+  int32_t pad1, pad2;
 };
 
 // A split item whose chunks occupy partial slots [part_base, part_base + n).
 struct MergeItem {
   int32_t b, g, t, part_base, n;
-  int32_t pad2;
-  int32_t pad0, pad1;
+  int32_t q0, E;  // sequence b's first new-token row and new tokens
+  int32_t pad0;
 };
 
 // Planner output header at the start of the workspace.
@@ -112,7 +119,7 @@ struct PlanArgs {
   void* zero_row;    // zeroed by the planner: kZeroRowBytes bytes
   WorkItem* work;    // [max_work]
   MergeItem* merge;  // [max_merge]
-  int32_t* scratch;  // [3 * bs + 3 + 3 * max_items], used when the batch exceeds the LDS arrays
+  int32_t* scratch;  // [6 * bs + 3 + 3 * max_items], used when the batch exceeds the LDS arrays
 };
 
 // Keys of sequence b as the attention kernels see them.
@@ -134,21 +141,14 @@ struct SeqKeys {
   int n_idx;   // keys read through kv_indices: j < n_idx
   int n_keys;  // keys that exist: j < n_keys
 };
-__device__ __forceinline__ SeqKeys seq_keys(const int32_t* qo_indptr, const int32_t* kv_indptr,
-                                            const int32_t* prefix_lens, int b, bool causal = true) {
+__device__ __forceinline__ SeqKeys item_keys(const WorkItem& it) {
   SeqKeys k;
-  k.q0 = qo_indptr[b];
-  k.E = qo_indptr[b + 1] - k.q0;
-  k.kvs = kv_indptr[b];
-  const int span = kv_indptr[b + 1] - k.kvs;
-  if (prefix_lens) {
-    k.P = prefix_lens[b];
-    k.n_idx = k.n_keys = causal ? min(span, k.P + k.E) : span;
-  } else {
-    k.P = span;
-    k.n_idx = span;
-    k.n_keys = span + k.E;
-  }
+  k.q0 = it.q0;
+  k.E = it.E;
+  k.kvs = it.kvs;
+  k.P = it.P;
+  k.n_idx = it.n_idx;
+  k.n_keys = it.n_keys;
   return k;
 }
 

@@ -30,7 +30,7 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBuckets = 256;
 constexpr int kMaxXcd = 8;
-constexpr int kSeqLds = 4096;   // per-sequence arrays kept in LDS up to this batch size
+constexpr int kSeqLds = 2048;   // per-sequence arrays kept in LDS up to this batch size
 constexpr int kItemLds = 8192;  // per-item arrays kept in LDS up to this many items
 
 struct Shared {
@@ -41,6 +41,9 @@ struct Shared {
   int32_t seq_base[kSeqLds + 1];  // first item of sequence b
   int32_t seq_e[kSeqLds];         // new tokens E_b
   int32_t seq_p[kSeqLds];         // prefix tokens P_b
+  int32_t seq_q0[kSeqLds];        // first new-token row qo_indptr[b]
+  int32_t seq_kvs[kSeqLds];       // first index kv_indptr[b]
+  int32_t seq_span[kSeqLds];      // indices kv_indptr[b + 1] - kv_indptr[b]
   int32_t cum[kItemLds + 1];      // exclusive running sum of the items' KV tiles
   int32_t pm[kItemLds];           // partial base << 16 | merge index (split items)
   int32_t cb[kItemLds + 1];       // first chunk of item n (the item's cost until chunks are cut)
@@ -97,11 +100,14 @@ template <bool LDS_ARRAYS>
 __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   const int tid = threadIdx.x;
   const int G = a.group, BM = a.bm, BN = a.bn, H = a.num_kv_heads;
-  // global scratch: seq_base[bs+1] | E[bs] | P[bs] | cum[items+1] | pm[items] | cb[items+1]
+  // global scratch: seq_base[bs+1] | E | P | q0 | kvs | span (bs each) | cum[items+1] | pm[items] | cb[items+1]
   int32_t* seq_base = LDS_ARRAYS ? sh.seq_base : a.scratch;
   int32_t* seq_e = LDS_ARRAYS ? sh.seq_e : a.scratch + a.bs + 1;
   int32_t* seq_p = LDS_ARRAYS ? sh.seq_p : a.scratch + 2 * a.bs + 1;
-  int32_t* cum = LDS_ARRAYS ? sh.cum : a.scratch + 3 * a.bs + 1;
+  int32_t* seq_q0 = LDS_ARRAYS ? sh.seq_q0 : a.scratch + 3 * a.bs + 1;
+  int32_t* seq_kvs = LDS_ARRAYS ? sh.seq_kvs : a.scratch + 4 * a.bs + 1;
+  int32_t* seq_span = LDS_ARRAYS ? sh.seq_span : a.scratch + 5 * a.bs + 1;
+  int32_t* cum = LDS_ARRAYS ? sh.cum : a.scratch + 6 * a.bs + 1;
   int32_t* pm = LDS_ARRAYS ? sh.pm : cum + a.max_items + 1;
   int32_t* cb = LDS_ARRAYS ? sh.cb : pm + a.max_items;
 
@@ -110,11 +116,15 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   const int s0 = min(a.bs, tid * spt), s1 = min(a.bs, s0 + spt);
   int local = 0;
   for (int b = s0; b < s1; ++b) {
-    const int E = a.qo_indptr[b + 1] - a.qo_indptr[b];
+    const int q0 = a.qo_indptr[b], E = a.qo_indptr[b + 1] - q0;
+    const int kvs = a.kv_indptr[b], span = a.kv_indptr[b + 1] - kvs;
     // prefix keys: the sequence's index span, or prefix_lens[b] for a unified call
-    const int P = a.prefix_lens ? a.prefix_lens[b] : a.kv_indptr[b + 1] - a.kv_indptr[b];
+    const int P = a.prefix_lens ? a.prefix_lens[b] : span;
     seq_e[b] = E;
     seq_p[b] = P;
+    seq_q0[b] = q0;
+    seq_kvs[b] = kvs;
+    seq_span[b] = span;
     local += H * ceil_div(E * G, BM);
   }
   {
@@ -182,8 +192,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     for (int n = n0; n < n1; ++n) {
       const int row_hi = min((t + 1) * BM, seq_e[b] * G) - 1;
       // with a custom mask every key of the sequence may be seen
-      const int keys = !a.masked ? seq_p[b] + row_hi / G + 1
-                                 : (a.prefix_lens ? a.kv_indptr[b + 1] - a.kv_indptr[b] : seq_p[b] + seq_e[b]);
+      const int keys = !a.masked ? seq_p[b] + row_hi / G + 1 : (a.prefix_lens ? seq_span[b] : seq_p[b] + seq_e[b]);
       // (at least one tile: size classes and chunk ranges assume it)
       const int cost = max(1, ceil_div(keys, BN) - first_tile(b, t));
       cb[n] = cost;
@@ -367,6 +376,17 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     w.part = k > 1 ? pbase + s : -1;
     w.merge = k > 1 ? midx : -1;
     w.pad0 = 0;
+    // the sequence's keys: kv_indices serves j < n_idx; in a two-part call
+    // the new tokens' rows follow (n_keys = P + E); in a unified call the
+    // index span holds every key, of which a causal row sees at most P + E
+    const int E = seq_e[b], P = seq_p[b], span = seq_span[b];
+    w.q0 = seq_q0[b];
+    w.E = E;
+    w.kvs = seq_kvs[b];
+    w.P = P;
+    w.n_idx = a.prefix_lens ? (!a.masked ? min(span, P + E) : span) : span;
+    w.n_keys = a.prefix_lens ? w.n_idx : span + E;
+    w.pad1 = w.pad2 = 0;
     a.work[rank * X + x] = w;
     if (k > 1 && s == 0) {
       MergeItem m;
@@ -375,8 +395,9 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       m.t = t;
       m.part_base = pbase;
       m.n = k;
-      m.pad2 = 0;
-      m.pad0 = m.pad1 = 0;
+      m.q0 = w.q0;
+      m.E = E;
+      m.pad0 = 0;
       a.merge[midx] = m;
     }
   });
@@ -389,6 +410,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     w.part = -1;
     w.merge = -1;
     w.pad0 = 0;
+    w.q0 = w.E = w.kvs = w.P = w.n_idx = w.n_keys = w.pad1 = w.pad2 = 0;
     a.work[i] = w;
   }
 }

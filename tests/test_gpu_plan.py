@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 
 HEADER_BYTES = 256       # the plan header: 64 int32
 WORK_OFFSET = 256 + 4096  # after the header and the zero row
-WORK_INTS = 8            # b, g, t, kt_begin, kt_end, part, merge, pad
+WORK_INTS = 16           # b, g, t, kt_begin, kt_end, part, merge, pad, q0, E, kvs, P, n_idx, n_keys, pad, pad
 
 
 def _plan(w, dev, window=0, split=None):
@@ -72,6 +72,12 @@ def _check_plan(w, hdr, work, window=0):
     empty = work[work[:, 0] < 0]
     assert len(live) == hdr["chunks"], (len(live), hdr)
     assert (empty[:, 1:7] == np.array([0, 0, 0, 0, -1, -1])).all()
+    # each record carries its sequence's keys as the index pointers give them (two-part call)
+    b = live[:, 0]
+    assert (live[:, 8] == w.qo_indptr[b]).all() and (live[:, 9] == w.extend_lens[b]).all()
+    assert (live[:, 10] == w.kv_indptr[b]).all() and (live[:, 11] == w.prefix_lens[b]).all()
+    assert (live[:, 12] == w.prefix_lens[b]).all()
+    assert (live[:, 13] == w.prefix_lens[b] + w.extend_lens[b]).all()
     assert (live[:, 4] > live[:, 3]).all(), "empty chunk"
     groups = {}
     for row in live:
