@@ -354,7 +354,7 @@ int decode_attention_fwd(const void* q, void* o, const void* k_pool, const void*
  *
  * Returns as extend_attention_fwd, plus PKV_ERR_UNSUPPORTED when the batch's
  * planning state would not fit the array (at 32 query heads over 8 KV heads
- * and head dim 128: more than about 877 000 new tokens) or for a device
+ * and head dim 128, 16 sequences: more than about 470 000 new tokens) or for a device
  * index >= 64.
  */
 int extend_attention_fwd_noalloc(const void* q_extend, const void* k_extend, const void* v_extend, void* o,
