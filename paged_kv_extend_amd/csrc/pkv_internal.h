@@ -15,6 +15,7 @@ namespace pkv {
 // part < 0: the item covers all KV tiles and writes o directly; otherwise it is
 // one chunk of a split item and writes unnormalised partial state into
 // partial slot `part`.  b < 0 marks an empty slot.
+// (an empty placement slot has b = -1 and nothing else written)
 struct WorkItem {
   int32_t b, g, t, kt_begin, kt_end, part;
   int32_t merge;  // merge record of a split item's chunk, else -1

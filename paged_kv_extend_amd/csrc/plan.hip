@@ -279,12 +279,14 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     return x;
   };
   // chunks in contiguous runs per thread; the item of the run's first chunk
-  // is the last n with cb[n] <= j0 (every item has at least one chunk)
+  // is the last n with cb[n] <= j0.  Every item has at least one chunk, so
+  // n <= cb[n] <= n + (n_chunks - n_items): that item lies in
+  // [j0 - (n_chunks - n_items), j0] (one step when nothing is split)
   const int cpt = ceil_div(n_chunks, kThreads);
   const int j0 = min(n_chunks, tid * cpt), j1 = min(n_chunks, j0 + cpt);
   int n_first = 0;
   if (j0 < j1) {
-    int lo = 0, hi = n_items - 1;
+    int lo = max(0, j0 - (n_chunks - n_items)), hi = min(n_items - 1, j0);
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (cb[mid] <= j0) lo = mid; else hi = mid - 1;
@@ -401,17 +403,11 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       a.merge[midx] = m;
     }
   });
-  // unused slots of shorter bins hold empty items (slot i = rank X + x)
+  // unused slots of shorter bins hold empty items (slot i = rank X + x):
+  // b = -1 is all a workgroup reads of one before it returns
   for (int i = tid; i < max_count * X; i += kThreads) {
     if (i / X < sh.bin_count[i % X]) continue;
-    WorkItem w;
-    w.b = -1;
-    w.g = w.t = w.kt_begin = w.kt_end = 0;
-    w.part = -1;
-    w.merge = -1;
-    w.pad0 = 0;
-    w.q0 = w.E = w.kvs = w.P = w.n_idx = w.n_keys = w.pad1 = w.pad2 = 0;
-    a.work[i] = w;
+    a.work[i].b = -1;
   }
 }
 

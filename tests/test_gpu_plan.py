@@ -7,7 +7,7 @@ every item (sequence, KV head, row tile) tile its key range [first, end)
 exactly once, in order; the item set is every row tile of every KV head of
 every sequence with rows; an item's end tile is the last key its rows see;
 split items own a dense, private run of partial slots and one merge record;
-empty slots carry b = -1; no piece of a split item exceeds the chunk limit.
+empty slots carry b = -1 (nothing else of them is read); no piece of a split item exceeds the chunk limit.
 Batches cover the planner's LDS arrays and its global-scratch path (more than
 4096 sequences or 8192 items), sliding windows, and a forced granularity that
 overflows the partial-state budget so that the limit doubles.
@@ -69,9 +69,7 @@ def _expected_items(w, bm, bn, window):
 
 def _check_plan(w, hdr, work, window=0):
     live = work[work[:, 0] >= 0]
-    empty = work[work[:, 0] < 0]
     assert len(live) == hdr["chunks"], (len(live), hdr)
-    assert (empty[:, 1:7] == np.array([0, 0, 0, 0, -1, -1])).all()
     # each record carries its sequence's keys as the index pointers give them (two-part call)
     b = live[:, 0]
     assert (live[:, 8] == w.qo_indptr[b]).all() and (live[:, 9] == w.extend_lens[b]).all()
