@@ -23,10 +23,12 @@
 //    when choosing each lane's global address, undone on reads): the
 //    MFMA operand reads of K and the transposing reads of V stay free of bank
 //    conflicts.
-//  * Head dim 128 runs 256 rows (8 waves, two per SIMD) per workgroup, so one
-//    K/V tile in LDS serves twice the rows of a 128-row workgroup; waves 0-3
-//    request the next tile's K rows after each barrier and waves 4-7 its V
-//    rows after their QK products (waves w and w+4 share a SIMD).
+//  * Head dims 128 and 256 run 256 rows (8 waves, two per SIMD) per
+//    workgroup, so one K/V tile in LDS serves twice the rows of a 128-row
+//    workgroup.  At 128, waves 0-3 request the next tile's K rows after each
+//    barrier and waves 4-7 its V rows after their QK products (waves w and
+//    w+4 share a SIMD).  At 256 a wave holds all of its 32 rows' Q^T (64
+//    registers) and O^T (128) and takes 32-key tiles in three stages.
 //  * When V is the first Lv columns of K (the MLA layout on page
 //    "cpu_graph_runner.py", qkv_proj_with_rope: v = k.narrow(-1, 0, lv)), only
 //    the K tile is loaded and the V^T operand is read from it.
@@ -59,9 +61,9 @@ struct DlCfg {
   // 32-column output blocks 2m + h, so that inside a swizzle group its
   // operand addresses differ from one per-lane base by constants only.
   static constexpr int SPLIT = SPLIT_;
-  // 32-row groups per workgroup.  The split variants use 4 (8 waves, two
-  // per SIMD): a wave's Q^T and O^T halves take ~200 registers at 576/512
-  // and ~100 at 256/256, so two waves fit one SIMD's register file.
+  // 32-row groups per workgroup.  The split variant (576/512) uses 4 (8
+  // waves, two per SIMD): a wave's Q^T and O^T halves take ~200 registers,
+  // so two waves fit one SIMD's register file.
   static constexpr int RG = RG_;
   // LDS stages: tile kt+NS-1 is requested while tile kt is computed
   static constexpr int NS = NS_;
@@ -78,6 +80,9 @@ struct DlCfg {
   static constexpr int NQ = SPLIT == 1 ? (CKR + 1) / 2 : QD / 16;
   static constexpr int NDB = SPLIT == 1 ? (LVR + 31) / 32 : VD / 32;
   static constexpr bool WIDE = CK == 72;  // 576-element rows: swizzle inside 8-chunk groups
+  // at the register limit (two waves per SIMD, 256 registers each): re-derive
+  // the per-lane table and load addresses every trip rather than keep them
+  static constexpr bool REMAT = WIDE || LQ >= 256;
   // rows sharing one 256-byte window of the 64 LDS banks
   static constexpr int RPK = CK >= 16 ? 1 : 16 / CK;
   static constexpr int RPV = CV >= 16 ? 1 : 16 / CV;
@@ -180,10 +185,10 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   if (it.b < 0 || (int)blockIdx.x >= num_work) return;  // empty or unused placement slot
   const int tid = threadIdx.x, lane = tid & 63;
   // the lane index the loop's table and load addressing starts from: the
-  // 576-wide variant, at its register limit, re-derives those per-lane
-  // addresses on every trip from this copy (see the loop) -- a few VALU
-  // operations -- where the compiler would otherwise keep them across the
-  // loop and spill them
+  // variants at their register limit (REMAT, and those with options)
+  // re-derive those per-lane addresses on every trip from this copy (see the
+  // loop) -- a few VALU operations -- where the compiler would otherwise keep
+  // them across the loop and spill them
   int ln = lane;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
   const int rg = wv % C::RG, half = wv / C::RG;  // row group; which half of Q dims / O columns
@@ -632,7 +637,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   };
 
   for (int kt = kt0; kt < kt1; ++kt) {
-    if constexpr (C::WIDE || OPT) asm volatile("" : "+v"(ln));  // (ln is lane; the compiler no longer knows it)
+    if constexpr (C::REMAT || OPT) asm volatile("" : "+v"(ln));  // (ln is lane; the compiler no longer knows it)
     tile_top(kt);
     issue_group(kt);
     const bool act = active(kt);
@@ -731,13 +736,13 @@ int dl_occupancy_t() {
 #define PKV_DL_VARIANTS(X)                   \
   X(64, 64, 64, false, 4, 1, 4, 0, 2)        \
   X(128, 128, 128, false, 8, 1, 2, 0, 1)     \
-  X(256, 256, 32, false, 4, 2, 3, 0, 1)      \
+  X(256, 256, 32, false, 8, 1, 3, 0, 1)      \
   X(576, 512, 32, true, 4, 2, 3, 0, 1)       \
   X(128, 128, 128, false, 8, 1, 2, 80, 1)    \
   X(128, 128, 128, false, 8, 1, 2, 96, 1)    \
   X(128, 128, 128, false, 8, 1, 2, 112, 1)   \
-  X(256, 256, 32, false, 4, 2, 3, 160, 1)    \
-  X(256, 256, 32, false, 4, 2, 3, 192, 1)
+  X(256, 256, 32, false, 8, 1, 3, 160, 1)    \
+  X(256, 256, 32, false, 8, 1, 3, 192, 1)
 
 // head dims a variant serves: its tile's, or the real plain dim it pads
 #define PKV_DL_MATCH(Q, V, VK, DR) \
