@@ -19,9 +19,10 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_extend_amd as pkv
 import workloads as wl
-from gpu_helpers import say
+from gpu_helpers import check, out_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -132,16 +133,21 @@ def test_plan_tiles_every_item(case):
     _check_plan(w, hdr, work)
 
 
-def test_plan_global_scratch_path():
-    # 5000 sequences: more than the planner keeps in LDS
+@pytest.mark.parametrize("n,hq,hkv", [(5000, 4, 2), (1500, 8, 8)], ids=["seqs-past-lds", "items-past-lds"])
+def test_plan_global_scratch_path(n, hq, hkv):
+    # more sequences (5000 > 2048) or more items (12 000 > 8192) than the
+    # planner keeps in LDS: the same code on global arrays; the plan and the
+    # attention output both checked
     rng = np.random.default_rng(3)
-    n = 5000
-    w = wl.custom(dtype="bf16", prefix_lens=rng.integers(0, 50, n).tolist(), extend_lens=rng.integers(0, 4, n).tolist(),
-                  hq=4, hkv=2, lq=64, lv=64, seed=29)
-    hdr, work = _plan(w, wl.to_torch(w))
-    say(f"plan bs=5000: {hdr}")
-    assert hdr["items"] > 0
+    lo = 0 if n == 5000 else 1
+    w = wl.custom(dtype="bf16", prefix_lens=rng.integers(0, 50, n).tolist(),
+                  extend_lens=rng.integers(lo, 4, n).tolist(), hq=hq, hkv=hkv, lq=64, lv=64, seed=29)
+    dev = wl.to_torch(w)
+    hdr, work = _plan(w, dev)
+    say(f"plan bs={n}: {hdr}")
+    assert hdr["items"] > (0 if n == 5000 else 8192)
     _check_plan(w, hdr, work)
+    check(out_f64(dev), oracle.extend_attention_workload(w), "bf16", f"plan-global-{n}")
 
 
 def test_plan_window():
