@@ -50,8 +50,9 @@ def parse():
                     help="target CPU time of each other workload's oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel", default="auto", help="attention kernel preference: auto, dl, attn")
-    ap.add_argument("--op", default="attention", choices=["attention", "store", "gather", "decode"],
-                    help="attention: the hot path; store / gather: the KV-cache store of the new tokens or the "
+    ap.add_argument("--op", default="attention", choices=["attention", "index", "store", "gather", "decode"],
+                    help="attention: the hot path; index: the unified index build alone (indptr scan and index "
+                         "copy); store / gather: the KV-cache store of the new tokens or the "
                          "request-to-token index gather of the same batch, reported in GB/s against HBM; "
                          "decode: decode attention on a decode batch (--workload decode_llama8b, decode_long, "
                          "decode_mla), GB/s against HBM")
@@ -255,11 +256,33 @@ def bench_attention(args, name, dev, cpu_seconds):
 
 
 def bench_copy_op(args, w, dev, torch, pkv):
-    """KV-cache store or request-to-token gather of the workload's batch, timed over rotated input copies."""
+    """Unified index build, KV-cache store or request-to-token gather of the workload's batch, timed over
+    rotated input copies."""
     c = w.cfg
     esz = 2 if c.dtype == "bf16" else 4
     sets = []
-    if args.op == "store":
+    if args.op == "index":
+        # every prefix and new-token index read once and written once, the
+        # indptr read and the unified indptr written, three length arrays
+        n_p, n_e = w.num_prefix, w.total_q
+        nbytes = 16 * (n_p + n_e) + 8 * (w.bs + 1) + 12 * w.bs
+        copies = args.copies or max(1, min(16, int(np.ceil(64e6 / max(nbytes, 1)))))
+
+        def t(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a).astype(dt)).to(dev)
+        for _ in range(copies):
+            sets.append(dict(kvp=t(w.kv_indptr, np.int32), kvi=t(w.kv_indices, np.int64),
+                             esl=t(w.extend_start_loc, np.int32), elen=t(w.extend_lens, np.int32),
+                             eki=t(w.extend_kv_indices, np.int64),
+                             out=(torch.empty(w.bs + 1, dtype=torch.int32, device=dev),
+                                  torch.empty(max(n_p + n_e, 1), dtype=torch.int64, device=dev),
+                                  torch.empty(w.bs, dtype=torch.int32, device=dev))))
+
+        def step(i):
+            d = sets[i % copies]
+            pkv.build_unified_kv_indices(d["kvp"], d["kvi"], d["esl"], d["elen"], d["eki"], w.bs, out=d["out"])
+        metric, what = "unified KV index build GB/s (indptr scan and index copy), 1 GPU", "index_build_kernel"
+    elif args.op == "store":
         import workloads as wl
         row_bytes = c.lq * esz + (0 if c.v_aliases_k else c.lv * esz)
         nbytes = 2 * w.total_q * c.hkv * row_bytes  # each new row read once and written once
