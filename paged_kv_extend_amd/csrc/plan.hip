@@ -4,9 +4,11 @@
 // number of KV tiles it must visit: the prefix plus the new tokens up to the
 // last token in its rows (keys past the causal diagonal are never visited).
 // An item costing more than one resident workgroup's average share (total
-// cost / resident workgroups) is split into near-equal KV ranges whose
-// partial softmax states are merged afterwards; the limit grows when the
-// partial-state budget would overflow.
+// cost / resident workgroups) is split into KV ranges of that many tiles (the
+// remainder last) whose partial softmax states are merged afterwards; the
+// limit grows when the partial-state budget would overflow.  Every work
+// record also carries its sequence's key bounds, so that a workgroup's first
+// loads depend on the record alone.
 //
 // Placement: workgroup i of a launch runs on XCD i mod 8, and each XCD has
 // its own L2.  The (b, g, t, chunk)-ordered cost sequence is cut into one

@@ -9,7 +9,7 @@ every sequence with rows; an item's end tile is the last key its rows see;
 split items own a dense, private run of partial slots and one merge record;
 empty slots carry b = -1 (nothing else of them is read); no piece of a split item exceeds the chunk limit.
 Batches cover the planner's LDS arrays and its global-scratch path (more than
-4096 sequences or 8192 items), sliding windows, and a forced granularity that
+2048 sequences or 8192 items), sliding windows, and a forced granularity that
 overflows the partial-state budget so that the limit doubles.
 """
 
