@@ -1,7 +1,9 @@
 // C ABI of libpkv.so: host-side argument checks, workspace sizing and the
 // stream-ordered launch sequence of an extend call (plan, attention, then a
 // merge launch that combines the chunks of split items).  Checks use only
-// host-visible sizes, so no call reads device memory or waits for the device.
+// host-visible sizes, so no call reads device memory or waits for the device
+// -- except in the debug build (PKV_DEBUG), which first checks the index
+// arrays on the device and waits for the verdict.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
