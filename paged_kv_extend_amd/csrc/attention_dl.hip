@@ -99,13 +99,15 @@ struct DlCfg {
   // every wave issues the same number of loads
   static constexpr int K_LOADS = (K_CHUNKS + NW - 1) / NW;
   static constexpr int V_LOADS = (V_CHUNKS + NW - 1) / NW;
-  // Eight waves (two per SIMD), staggered loads: waves 0..3 issue the K rows
-  // of the next tile right after each barrier and waves 4..7 its V rows after
-  // their S = K Q^T products, so while one wave of a SIMD waits for the
-  // memory pipeline to take its loads, the other has products to run.
+  // Eight waves (two per SIMD: waves w and w + 4 share one), staggered
+  // loads: waves 0..3 issue the K rows of the next tile right after each
+  // barrier and waves 4..7 its V rows after their S = K Q^T products, so
+  // while one wave of a SIMD waits for the memory pipeline to take its loads,
+  // the other has products to run.  Which wave builds the tables is decided
+  // per work item (see the kernel).
   static constexpr bool OFFLOAD = SPLIT == 1 && NW == 8 && NS == 2;
   static constexpr int LOADERS = OFFLOAD ? NW / 2 : NW;   // waves per load group
-  static constexpr int TW = OFFLOAD ? NW / 2 : 0;         // the wave that builds tables
+  static constexpr int TW = 0;                            // the wave that builds tables (not staggered)
   static constexpr int L = OFFLOAD ? 2 * V_LOADS : K_LOADS + V_LOADS;  // tile loads per wave per tile
   static constexpr int I = BN * 8 / 256;  // row-slot loads (64 lanes x 4 bytes) per tile, table wave
   // waits at the top of an iteration (see the loop): outstanding loads allowed
@@ -222,6 +224,12 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   const int lo_lo_w = W > 0 ? P + tok_lo_w - W : kNoLowerKey;
   const int lo_hi_w = W > 0 ? P + tok_hi_w - W : kNoLowerKey;
   const int key_last = last_key(min(R - 1, it.t * BM + BM - 1) / G);
+  // The table wave with staggered loads: a wave without rows when the item
+  // leaves the last one empty, else wave 3 -- the waves of the K group
+  // finish their tile first and wait at the barrier the longest, while
+  // table work on a wave of the V group delays the whole tile.
+  const int n_live = min(C::NW, (R - it.t * BM + 31) / 32);  // waves with rows (one row group each when staggered)
+  const int tw = !C::OFFLOAD ? C::TW : n_live < C::NW ? C::NW - 1 : C::LOADERS - 1;
 
   const gptr<T> kpool = (gptr<T>)a.k_pool;
   const gptr<T> vpool = (gptr<T>)a.v_pool;
@@ -248,7 +256,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
     }
   }
 
-  // ---- row pointer tables (NS slots), built by the table wave C::TW; lane e owns key kt*BN + e.
+  // ---- row pointer tables (NS slots), built by the table wave tw; lane e owns key kt*BN + e.
   //      Strides and per-head bases are read once into scalar registers.
   const int64_t kp_ss = uniform64(a.kp_ss), vp_ss = uniform64(a.vp_ss);
   const int64_t ke_st = uniform64(a.ke_st), ve_st = uniform64(a.ve_st);
@@ -416,7 +424,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
     // the groups that iterations kt0-NS+1 .. kt0-1 would have issued
 #pragma unroll
     for (int v = 0; v < NS - 1; ++v) {
-      if (wv == C::TW) issue_slots(kt0 + NS - 1 + v);
+      if (wv == tw) issue_slots(kt0 + NS - 1 + v);
       issue_tile(kt0 + v);
     }
   }
@@ -615,7 +623,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   // (its slot held table kt-1, issued long ago) before the barrier that
   // publishes it and tile kt.
   auto tile_top = [&](int kt) __attribute__((always_inline)) {
-    if (wv == C::TW) {
+    if (wv == tw) {
       wait_vm<C::W_TABLE>();
       write_table(kt + NS - 1);
       wait_lds();
@@ -628,7 +636,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   // entry of tile kt+NS-1, whose table was written before the barrier) and
   // tile kt+NS-1 into stage (kt-1) % NS, which tile kt-1 no longer needs
   auto issue_group = [&](int kt) __attribute__((always_inline)) {
-    if (wv == C::TW) issue_slots(kt + 2 * NS - 2);
+    if (wv == tw) issue_slots(kt + 2 * NS - 2);
     if constexpr (C::OFFLOAD) {
       if (wv < C::LOADERS) issue_loads(kt + NS - 1, true, false);
     } else {
