@@ -93,6 +93,18 @@ __device__ void block_excl_scan(const int (&v)[N], int (&ex)[N], int64_t (&total
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// n / d for 0 <= n < 2^31 and 0 < d < 2^31, given inv = 1.0 / d: the double
+// product lies within 2^-21 of n / d, so its truncation is the quotient or
+// one less, and the remainder settles which (a few instructions instead of
+// the ~40 of a 32-bit integer divide)
+__device__ __forceinline__ int div_by(int n, int d, double inv) {
+  int q = (int)((double)n * inv);
+  const int r = n - q * d;
+  q += r >= d ? 1 : 0;
+  q -= r < 0 ? 1 : 0;
+  return q;
+}
+
 // Per-item arrays in LDS when the batch fits (the only global reads are the
 // indptrs), else in the global scratch.  Sequences, items and chunks are
 // handed out in contiguous runs per thread, so each pass is a local walk,
@@ -102,6 +114,10 @@ template <bool LDS_ARRAYS>
 __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   const int tid = threadIdx.x;
   const int G = a.group, BM = a.bm, BN = a.bn, H = a.num_kv_heads;
+  const int lbm = __builtin_ctz(BM), lbn = __builtin_ctz(BN);  // powers of two (launch_plan checks)
+  const double inv_g = 1.0 / G;
+  // row tiles of a sequence with E new tokens (E G < 2^31: the host checks)
+  auto row_tiles = [&](int E) { return (int)(((uint32_t)(E * G) + (uint32_t)(BM - 1)) >> lbm); };
   // global scratch: seq_base[bs+1] | E | P | q0 | kvs | span (bs each) | cum[items+1] | pm[items] | cb[items+1]
   int32_t* seq_base = LDS_ARRAYS ? sh.seq_base : a.scratch;
   int32_t* seq_e = LDS_ARRAYS ? sh.seq_e : a.scratch + a.bs + 1;
@@ -127,7 +143,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     seq_q0[b] = q0;
     seq_kvs[b] = kvs;
     seq_span[b] = span;
-    local += H * ceil_div(E * G, BM);
+    local += H * row_tiles(E);
   }
   {
     int v[1] = {local}, ex[1];
@@ -136,7 +152,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     int run = ex[0];
     for (int b = s0; b < s1; ++b) {
       seq_base[b] = run;
-      run += H * ceil_div(seq_e[b] * G, BM);
+      run += H * row_tiles(seq_e[b]);
     }
     if (tid == 0) seq_base[a.bs] = (int)tot[0];
     local = (int)tot[0];
@@ -163,14 +179,14 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       if (seq_base[mid] <= n) lo = mid; else hi = mid - 1;
     }
     b = lo;
-    const int T = ceil_div(seq_e[b] * G, BM);
+    const int T = row_tiles(seq_e[b]);
     const int loc = n - seq_base[b];
-    g = loc / T;
-    t = loc % T;
+    g = div_by(loc, T, 1.0 / T);
+    t = loc - g * T;
   };
   // the item after (b, g, t): next tile, next head, or next sequence with rows
   auto next_item = [&](int& b, int& g, int& t) {
-    if (++t == ceil_div(seq_e[b] * G, BM)) {
+    if (++t == row_tiles(seq_e[b])) {
       t = 0;
       if (++g == H) {
         g = 0;
@@ -180,7 +196,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   };
   // tile of the first key any row of tile t of sequence b sees (sliding window)
   auto first_tile = [&](int b, int t) {
-    return a.window > 0 ? max(0, seq_p[b] + (t * BM) / G - a.window) / BN : 0;
+    return a.window > 0 ? max(0, seq_p[b] + div_by(t * BM, G, inv_g) - a.window) >> lbn : 0;
   };
   const int ipt = ceil_div(n_items, kThreads);  // items per thread, contiguous
   const int n0 = min(n_items, tid * ipt), n1 = min(n_items, n0 + ipt);
@@ -194,9 +210,10 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     for (int n = n0; n < n1; ++n) {
       const int row_hi = min((t + 1) * BM, seq_e[b] * G) - 1;
       // with a custom mask every key of the sequence may be seen
-      const int keys = !a.masked ? seq_p[b] + row_hi / G + 1 : (a.prefix_lens ? seq_span[b] : seq_p[b] + seq_e[b]);
+      const int keys =
+          !a.masked ? seq_p[b] + div_by(row_hi, G, inv_g) + 1 : (a.prefix_lens ? seq_span[b] : seq_p[b] + seq_e[b]);
       // (at least one tile: size classes and chunk ranges assume it)
-      const int cost = max(1, ceil_div(keys, BN) - first_tile(b, t));
+      const int cost = max(1, ((keys + BN - 1) >> lbn) - first_tile(b, t));
       cb[n] = cost;
       my_total += cost;
       next_item(b, g, t);
@@ -221,11 +238,12 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   //    grown until the split chunks fit the partial-state budget; and
   // 4. with the limit that fits, in the same block scan: partial-slot and
   //    merge-record offsets of split items and the first chunk of every item
+  // (the total fits 31 bits: cum holds its running sums)
   const int64_t shares = (int64_t)a.slots * (a.rounds > 0 ? a.rounds : 1);
-  int64_t chunk = (total + shares - 1) / shares;
+  int chunk = (int)((total + shares - 1) / shares);
   if (chunk < a.min_chunk) chunk = a.min_chunk;
-  // (c > chunk: both fit 32 bits, and a 32-bit divide is much shorter than a 64-bit one)
-  auto pieces = [&](int c) { return c > chunk ? (int)((uint32_t)(c - 1) / (uint32_t)chunk) + 1 : 1; };
+  double inv_chunk = 1.0 / chunk;
+  auto pieces = [&](int c) { return c > chunk ? div_by(c - 1, chunk, inv_chunk) + 1 : 1; };
   int mcarry, n_chunks;
   for (;;) {
     int v[3] = {0, 0, 0}, ex[3];
@@ -239,6 +257,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     block_excl_scan<3>(v, ex, tot, sh);
     if (tot[0] > a.part_budget) {
       chunk *= 2;
+      inv_chunk = 1.0 / chunk;
       continue;
     }
     for (int n = n0; n < n1; ++n) {
@@ -265,16 +284,18 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   int X = a.xcds < 1 ? 1 : (a.xcds > kMaxXcd ? kMaxXcd : a.xcds);
   // XCD of a chunk: which of X equal-cost ranges holds its midpoint (twice the
   // midpoint against twice the range ends; integer compares only)
-  int64_t bnd2[kMaxXcd];
+  // (twice the total fits 32 bits unsigned)
+  uint32_t bnd2[kMaxXcd];
   {
-    // (x+1) total / X with one 64-bit divide: (x+1)(q X + r) / X = (x+1) q + (x+1) r / X
-    const int64_t q = total / X;
-    const int rem = (int)(total - q * X);
+    // (x+1) total / X as (x+1)(q X + r) / X = (x+1) q + (x+1) r / X
+    const double inv_x = 1.0 / X;
+    const int q = div_by((int)total, X, inv_x);
+    const int rem = (int)total - q * X;
 #pragma unroll
-    for (int x = 0; x < kMaxXcd; ++x) bnd2[x] = 2 * ((x + 1) * q + ((x + 1) * rem) / X);
+    for (int x = 0; x < kMaxXcd; ++x) bnd2[x] = 2u * (uint32_t)((x + 1) * q + div_by((x + 1) * rem, X, inv_x));
   }
   auto bin_of = [&](int n, int k0, int k1) {
-    const int64_t mid2 = 2 * (int64_t)cum[n] + k0 + k1;
+    const uint32_t mid2 = 2u * (uint32_t)cum[n] + (uint32_t)(k0 + k1);
     int x = 0;
 #pragma unroll
     for (int i = 0; i < kMaxXcd - 1; ++i) x += (i < X - 1 && mid2 >= bnd2[i]) ? 1 : 0;
@@ -307,8 +328,8 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     for (int j = j0; j < j1; ++j) {
       const int base = cb[n], k = cb[n + 1] - base, s = j - base;
       const int c = cum[n + 1] - cum[n];
-      const int k0 = k == 1 ? 0 : (int)(s * chunk);
-      const int k1 = k == 1 ? c : min(c, (int)((s + 1) * chunk));
+      const int k0 = s * chunk;  // (0 when the item is whole)
+      const int k1 = s + 1 == k ? c : (s + 1) * chunk;
       visit(n, b, g, t, s, k, k0, k1);
       if (s + 1 == k && ++n < n_items) next_item(b, g, t);
     }
@@ -361,7 +382,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     a.hdr->num_chunks = n_chunks;
     a.hdr->xcds = X;
     a.hdr->num_merge = mcarry;
-    a.hdr->chunk_tiles = (int32_t)chunk;
+    a.hdr->chunk_tiles = chunk;
     a.hdr->total_tiles = (int32_t)total;
     a.hdr->num_items = n_items;
   }
@@ -427,6 +448,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+  // the planner divides by the tile sizes with shifts
+  if (a.bm <= 0 || a.bn <= 0 || (a.bm & (a.bm - 1)) != 0 || (a.bn & (a.bn - 1)) != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
