@@ -36,9 +36,8 @@ constexpr int kSeqLds = 2048;   // per-sequence arrays kept in LDS up to this ba
 constexpr int kItemLds = 8192;  // per-item arrays kept in LDS up to this many items
 
 struct Shared {
-  int64_t wave_tot[kWaves][4];
+  int32_t wave_tot[2][3][kWaves];  // two buffers, used by alternate scans
   int32_t bucket[kMaxXcd * kBuckets];
-  int32_t bin_count[kMaxXcd];
   int32_t bin_start[kMaxXcd];
   int32_t seq_base[kSeqLds + 1];  // first item of sequence b
   int32_t seq_e[kSeqLds];         // new tokens E_b
@@ -63,32 +62,36 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive block-wide scans of up to three 64-bit-summed ints per thread
-// (each value and each total must fit 31 bits); returns the scans, sets the totals.
+// Exclusive block-wide scans of up to three ints per thread (each value and
+// each total must fit 31 bits); returns the scans, sets the totals.  Buffer
+// `buf` of the wave totals must alternate between consecutive calls: the
+// barrier inside the next call is what orders the reads of this one before
+// the writes of the call after it, so no barrier closes a scan.
 template <int N>
-__device__ void block_excl_scan(const int (&v)[N], int (&ex)[N], int64_t (&total)[N], Shared& sh) {
+__device__ void block_excl_scan(const int (&v)[N], int (&ex)[N], int64_t (&total)[N], Shared& sh, int buf) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int inc[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) inc[i] = wave_incl_scan(v[i]);
   if (lane == 63) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) sh.wave_tot[w][i] = inc[i];
+    for (int i = 0; i < N; ++i) sh.wave_tot[buf][i][w] = inc[i];
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    int64_t before = 0, all = 0;
+    const int4 t0 = *reinterpret_cast<const int4*>(&sh.wave_tot[buf][i][0]);
+    const int4 t1 = *reinterpret_cast<const int4*>(&sh.wave_tot[buf][i][4]);
+    const int t[kWaves] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    int before = 0, all = 0;
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) {
-      const int64_t t = sh.wave_tot[k][i];
-      before += k < w ? t : 0;
-      all += t;
+      before += k < w ? t[k] : 0;
+      all += t[k];
     }
-    ex[i] = (int)before + inc[i] - v[i];
+    ex[i] = before + inc[i] - v[i];
     total[i] = all;
   }
-  __syncthreads();
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -116,6 +119,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   const int G = a.group, BM = a.bm, BN = a.bn, H = a.num_kv_heads;
   const int lbm = __builtin_ctz(BM), lbn = __builtin_ctz(BN);  // powers of two (launch_plan checks)
   const double inv_g = 1.0 / G;
+  int scan_no = 0;  // alternates the scans' buffers (the same sequence of scans on every thread)
   // row tiles of a sequence with E new tokens (E G < 2^31: the host checks)
   auto row_tiles = [&](int E) { return (int)(((uint32_t)(E * G) + (uint32_t)(BM - 1)) >> lbm); };
   // global scratch: seq_base[bs+1] | E | P | q0 | kvs | span (bs each) | cum[items+1] | pm[items] | cb[items+1]
@@ -128,6 +132,8 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   int32_t* cum = LDS_ARRAYS ? sh.cum : a.scratch + 6 * a.bs + 1;
   int32_t* pm = LDS_ARRAYS ? sh.pm : cum + a.max_items + 1;
   int32_t* cb = LDS_ARRAYS ? sh.cb : pm + a.max_items;
+  // the placement's counters, zeroed here (the barriers of the first scans order it)
+  for (int i = tid; i < kMaxXcd * kBuckets; i += kThreads) sh.bucket[i] = 0;
 
   // 1. per sequence: E, P and items H * ceil(E G / BM), exclusive scan
   const int spt = ceil_div(a.bs, kThreads);  // sequences per thread
@@ -148,7 +154,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   {
     int v[1] = {local}, ex[1];
     int64_t tot[1];
-    block_excl_scan<1>(v, ex, tot, sh);
+    block_excl_scan<1>(v, ex, tot, sh, scan_no++ & 1);
     int run = ex[0];
     for (int b = s0; b < s1; ++b) {
       seq_base[b] = run;
@@ -223,7 +229,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   {
     int v[1] = {my_total}, ex[1];
     int64_t tot[1];
-    block_excl_scan<1>(v, ex, tot, sh);
+    block_excl_scan<1>(v, ex, tot, sh, scan_no++ & 1);
     int run = ex[0];
     for (int n = n0; n < n1; ++n) {
       cum[n] = run;
@@ -254,7 +260,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       v[1] += k > 1 ? 1 : 0;
       v[2] += k;
     }
-    block_excl_scan<3>(v, ex, tot, sh);
+    block_excl_scan<3>(v, ex, tot, sh, scan_no++ & 1);
     if (tot[0] > a.part_budget) {
       chunk *= 2;
       inv_chunk = 1.0 / chunk;
@@ -335,10 +341,11 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
     }
   };
   constexpr int kPer = kMaxXcd * kBuckets / kThreads;  // counters per thread in the scan
-  int max_count = 0;
+  int max_count = 0, n_placed = 0;
+  // chunks of bin x (bin_start as set by the last scan)
+  auto bin_count = [&](int x) { return (x + 1 < X ? sh.bin_start[x + 1] : n_placed) - sh.bin_start[x]; };
   for (int attempt = 0; attempt < 2; ++attempt) {
-    for (int i = tid; i < kMaxXcd * kBuckets; i += kThreads) sh.bucket[i] = 0;
-    __syncthreads();
+    // (the first attempt's counters were zeroed at the start)
     walk([&](int n, int, int, int, int, int, int k0, int k1) {
       atomicAdd(&sh.bucket[bin_of(n, k0, k1) * kBuckets + (kBuckets - 1 - size_class(k1 - k0))], 1);
     });
@@ -355,26 +362,25 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
       }
       int v[1] = {sum}, ex[1];
       int64_t tot[1];
-      block_excl_scan<1>(v, ex, tot, sh);
+      block_excl_scan<1>(v, ex, tot, sh, scan_no++ & 1);
       int run = ex[0];
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int idx = tid * kPer + i;
-        if (idx < X * kBuckets) sh.bucket[idx] = run;
+        if (idx < X * kBuckets) {
+          sh.bucket[idx] = run;
+          if (idx % kBuckets == 0) sh.bin_start[idx / kBuckets] = run;
+        }
         run += cnt[i];
       }
-      __syncthreads();
-      if (tid < X) {
-        sh.bin_start[tid] = sh.bucket[tid * kBuckets];
-        sh.bin_count[tid] =
-            (tid + 1 < X ? sh.bucket[(tid + 1) * kBuckets] : (int)tot[0]) - sh.bucket[tid * kBuckets];
-      }
+      n_placed = (int)tot[0];
       __syncthreads();
     }
     max_count = 0;
-    for (int x = 0; x < X; ++x) max_count = max(max_count, sh.bin_count[x]);
+    for (int x = 0; x < X; ++x) max_count = max(max_count, bin_count(x));
     if ((int64_t)max_count * X <= a.max_work || X == 1) break;
     X = 1;  // bins too uneven for the grid: plain heaviest-first order
+    for (int i = tid; i < kMaxXcd * kBuckets; i += kThreads) sh.bucket[i] = 0;
     __syncthreads();
   }
   if (tid == 0) {
@@ -429,7 +435,7 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   // unused slots of shorter bins hold empty items (slot i = rank X + x):
   // b = -1 is all a workgroup reads of one before it returns
   for (int i = tid; i < max_count * X; i += kThreads) {
-    if (i / X < sh.bin_count[i % X]) continue;
+    if (i / X < bin_count(i % X)) continue;
     a.work[i].b = -1;
   }
 }
