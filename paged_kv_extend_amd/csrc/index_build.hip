@@ -64,8 +64,10 @@ hipError_t launch_index_build(const int32_t* prefix_kv_indptr, const int64_t* pr
                               const int64_t* extend_kv_indices, int32_t bs,
                               int32_t* unified_kv_indptr, int64_t* unified_kv_indices,
                               int32_t* prefix_lens, hipStream_t s) {
-  // spread small batches over more workgroups so long segments copy in parallel
-  const int ways = bs >= 256 ? 1 : (bs >= 32 ? 4 : 16);
+  // spread small batches over more workgroups so long segments copy in
+  // parallel (a wave's runs are serial round trips: with four sequences of
+  // 16 K indices each, 64 ways leave about one run per wave)
+  const int ways = bs >= 256 ? 1 : bs >= 32 ? 4 : bs >= 8 ? 16 : 64;
   dim3 grid(bs > 0 ? bs : 1, bs > 0 ? ways : 1);
   hipLaunchKernelGGL(index_build_kernel, grid, dim3(kThreads), 0, s, prefix_kv_indptr,
                      prefix_kv_indices, extend_start_loc, extend_seq_lens, extend_kv_indices, bs,
