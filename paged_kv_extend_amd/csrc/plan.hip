@@ -11,13 +11,16 @@
 // loads depend on the record alone.
 //
 // Placement: workgroup i of a launch runs on XCD i mod 8, and each XCD has
-// its own L2.  The (b, g, t, chunk)-ordered cost sequence is cut into one
-// contiguous, equal-cost range per XCD (a chunk goes to the range holding its
-// midpoint), so the q-tiles of one (sequence, KV head) -- which read the same
-// prefix K/V -- share an L2 while every XCD gets the same work.  Within an
-// XCD chunks run heaviest first (counting sort over 256 size classes), which
+// its own L2.  With fewer than three chunks per resident workgroup, the
+// (b, g, t, chunk)-ordered cost sequence is cut into one contiguous,
+// equal-cost range per XCD (a chunk goes to the range holding its midpoint),
+// so the q-tiles of one (sequence, KV head) -- which read the same prefix
+// K/V -- share an L2 while every XCD gets the same work.  Within an XCD
+// chunks run heaviest first (counting sort over 256 size classes), which
 // with in-order dispatch approximates longest-processing-time-first; slot
-// rank*8 + xcd holds the XCD's rank-th chunk and unused slots hold empty items.
+// rank*8 + xcd holds the XCD's rank-th chunk and unused slots hold empty
+// items.  With more chunks per workgroup, one heaviest-first list over all
+// slots balances the CUs better than the ranges keep L2 sharing.
 //
 // The pages' own grids launch one program per (sequence, head, query block)
 // with every program visiting all keys (page "extend_attention.py",
@@ -288,6 +291,11 @@ __device__ void plan_body(const PlanArgs& a, Shared& sh) {
   const float cls_scale = (float)kBuckets / (float)chunk;
   auto size_class = [&](int sz) { return min(kBuckets - 1, (int)((float)(sz - 1) * cls_scale)); };
   int X = a.xcds < 1 ? 1 : (a.xcds > kMaxXcd ? kMaxXcd : a.xcds);
+  // With three or more chunks per resident workgroup, one heaviest-first
+  // list dealt round-robin over the XCDs evens out the CUs better than
+  // per-XCD ranges, and that outweighs the L2 sharing the ranges buy; with
+  // fewer, the ranges' sharing of a sequence's K/V rows in one L2 wins.
+  if ((int64_t)n_chunks >= 3 * (int64_t)a.slots) X = 1;
   // XCD of a chunk: which of X equal-cost ranges holds its midpoint (twice the
   // midpoint against twice the range ends; integer compares only)
   // (twice the total fits 32 bits unsigned)
