@@ -7,10 +7,12 @@ every item (sequence, KV head, row tile) tile its key range [first, end)
 exactly once, in order; the item set is every row tile of every KV head of
 every sequence with rows; an item's end tile is the last key its rows see;
 split items own a dense, private run of partial slots and one merge record;
-empty slots carry b = -1 (nothing else of them is read); no piece of a split item exceeds the chunk limit.
+empty slots carry b = -1 (nothing else of them is read); no piece of a split item exceeds the chunk limit
+or is empty.
 Batches cover the planner's LDS arrays and its global-scratch path (more than
 2048 sequences or 8192 items), sliding windows, and a forced granularity that
-overflows the partial-state budget so that the limit doubles.
+overflows the partial-state budget so that the limit doubles, and forced
+one-tile granularity on a batch with fewer tiles than slots.
 """
 
 import math
@@ -166,3 +168,19 @@ def test_plan_partial_budget_doubles_the_limit():
     say(f"plan forced fine split: {hdr}")
     assert hdr["chunk"] > 1 and hdr["num_merge"] == 16
     _check_plan(w, hdr, work)
+
+
+@pytest.mark.parametrize("split", [(1, 1), (2, 1), (16, 1)], ids=["r1", "r2", "r16"])
+def test_plan_forced_split_of_a_small_batch(split):
+    # fewer KV tiles in all than resident workgroups, with a forced minimum
+    # chunk of one tile: items cut into one-tile pieces, none empty (an empty
+    # piece has no size class and would corrupt the placement), and the
+    # attention output still meets the oracle
+    w = wl.custom(dtype="bf16", prefix_lens=[0, 300, 77, 1000, 5], extend_lens=[200, 1, 64, 33, 129], hq=32, hkv=8,
+                  lq=128, lv=128)
+    dev = wl.to_torch(w)
+    hdr, work = _plan(w, dev, split=split)
+    say(f"plan small forced {split}: {hdr}")
+    assert hdr["total"] < torch.cuda.get_device_properties(0).multi_processor_count * split[0]
+    _check_plan(w, hdr, work)
+    check(out_f64(dev), oracle.extend_attention_workload(w), "bf16", f"plan-small-{split[0]}")
