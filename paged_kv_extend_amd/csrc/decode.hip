@@ -20,9 +20,11 @@
 //  * Inside a workgroup each of the (usually four) waves streams its own contiguous
 //    share of the chunk's keys, 16 keys per tile, through a ring of LDS stages
 //    filled by global-to-LDS loads (16 bytes per lane, whole rows per group of
-//    lanes).  The slots of later tiles come into LDS the same way, far enough
-//    ahead that every wait in the loop is a fixed vmcnt, and no wave waits
-//    for another until the chunk is done.
+//    lanes).  A stage is refilled as soon as the wave is done with it,
+//    before the wave waits for its next tile, so that every stage is in
+//    flight during that wait.  The slots of later tiles come into LDS the
+//    same way, far enough ahead that every wait in the loop is a fixed vmcnt,
+//    and no wave waits for another until the chunk is done.
 //  * The G query heads of a KV head (padded to 16) form the N side of 16x16
 //    MFMAs: S^T = K Q^T on 16x16x32 bf16 with K read from LDS, O^T = V^T P^T
 //    on 16x16x16 bf16 with V^T read by the transposing LDS read; the
@@ -59,12 +61,15 @@ struct DecCfg {
   static constexpr int MERGE_BYTES = NW * 16 * (LV + 2) * 4;
   static constexpr int LDS = NW * WAVE_BYTES > MERGE_BYTES ? NW * WAVE_BYTES : MERGE_BYTES;
   static constexpr int NT = NW * 64;
-  // loads that may stay in flight at the top of trip t once tile t has landed:
-  // the slot table requested right after it and NS - 2 whole later trips
-  static constexpr int WAIT = 1 + (NS - 2) * L;
+  // loads that may stay in flight in trip t (which issues tile t + NS - 1
+  // before it waits for tile t): once the slot table of tile t + NS - 1 has
+  // landed, the NS - 1 trips issued after it; once tile t has landed, the
+  // slot table requested right after it and NS - 1 whole trips
+  static constexpr int W_SLOTS = (NS - 1) * L;
+  static constexpr int W_TILE = 1 + (NS - 1) * L;
   static_assert(LQ % 32 == 0 && LV % 16 == 0, "head dims");
   static_assert(VK ? LV <= LQ : CV % 4 == 0, "lv");
-  static_assert(NS >= 2 && WAIT < 64, "pipeline depth");
+  static_assert(NS >= 2 && W_TILE < 64, "pipeline depth");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -253,11 +258,18 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
       }
 
       for (int t = 0; t < nt; ++t) {
-        // tile t has landed; so has the slot table of tile t + NS - 1, which
-        // was requested before it
-        if (t + NS - 2 < nt) wait_vm<C::WAIT>(); else wait_all_mem();
-        if (t + NS - 1 < nt) issue_tile(t + NS - 1);
+        // Trip t first refills the stage trip t - 1 has finished with (the
+        // wait is also the compiler fence that keeps that trip's operand
+        // reads ahead of the refill): tile t + NS - 1, whose slot table has
+        // landed once at most the NS - 1 trips issued after it are in flight,
+        // then the slot table NS tiles later.  Only then does it wait for
+        // tile t, so that while it waits all NS stages are in flight.
+        if (t + NS - 1 < nt) {
+          wait_vm<C::W_SLOTS>();
+          issue_tile(t + NS - 1);
+        }
         issue_slots(t + 2 * NS - 1);
+        if (t + NS - 1 < nt) wait_vm<C::W_TILE>(); else wait_all_mem();
 
         const char* st = wbase + (t % NS) * C::STAGE;
         // S^T = K Q^T: lane holds keys 4 j4 .. 4 j4 + 3 of head row r16
@@ -267,6 +279,22 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
           const unsigned cc = 4u * kk + j4;
           const bf16x8 kv = *(lptr<bf16x8>)(st + r16 * (C::CK * 16) + (cc ^ swz_k<C::CK>(r16)) * 16u);
           s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[kk], s, 0, 0, 0);
+        }
+        // Schedule: the first PRE operand reads, then one product per further
+        // read, so that reads stay in flight ahead of the products (left to
+        // itself the compiler reused one register and waited for each read
+        // before its product: 18 LDS round trips per tile on 576-wide rows).
+        // The barrier keeps the softmax and the V^T reads out of these groups.
+        {
+          constexpr int PRE = NKK < 6 ? NKK : 6;
+          __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);  // DS reads
+#pragma unroll
+          for (int i = 0; i < NKK - PRE; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         float x[4];
         float mx = -INFINITY;
@@ -385,12 +413,15 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
 
 // Requests whose keys span several chunks: one workgroup per (head block,
 // 64-column slice, request) combines the chunks' states in chunk order
-// (deterministic):
+// (deterministic), batch by batch:
 //   M = max_c m_c,  L = sum_c l_c 2^(m_c - M),  o = sum_c acc_c 2^(m_c - M) / L
-// plus the sink term.  Thread = (head row, 4 columns); the chunk loops are
-// unrolled so that several partial rows are in flight per thread.  A request
-// with no visible key gets a zero output here (there is nothing to average).
+// plus the sink term.  Thread = (head row, 4 columns), the partial rows of
+// kMergeBatch chunks in flight per thread at once (one pass: a maximum
+// taken first over every chunk would cost a dependent round trip).  A
+// request with no visible key gets a zero output here (there is nothing to
+// average).
 constexpr int kMergeCols = 64;
+constexpr int kMergeBatch = 16;
 
 template <int LV>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
@@ -408,25 +439,44 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
   const int c0 = v0 / a.chunk, c1 = (v1 - 1) / a.chunk;
   if (c0 == c1) return;  // written by its only chunk
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int cc = c0; cc <= c1; ++cc) {
-    const int64_t prow = (piece_slot(cc, v0, a.chunk) * a.gh_count + gh) * 16 + row;
-    M = fmaxf(M, a.part_ml[prow * 2]);
-  }
-  float L = 0.0f;
+  // the chunks in batches, every load of a batch in flight at once; the
+  // running state is rescaled when a batch raises the maximum
+  float M = -INFINITY, L = 0.0f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int cc = c0; cc <= c1; ++cc) {
-    const int64_t prow = (piece_slot(cc, v0, a.chunk) * a.gh_count + gh) * 16 + row;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
-    const float wt = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - M);
-    L += ml.y * wt;
-    const float4 v = *reinterpret_cast<const float4*>(a.part_acc + prow * LV + d);
-    o.x += v.x * wt;
-    o.y += v.y * wt;
-    o.z += v.z * wt;
-    o.w += v.w * wt;
+  for (int cb = c0; cb <= c1; cb += kMergeBatch) {
+    float2 ml[kMergeBatch];
+    float4 v[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      ml[i] = make_float2(-INFINITY, 0.0f);
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (cb + i <= c1) {
+        const int64_t prow = (piece_slot(cb + i, v0, a.chunk) * a.gh_count + gh) * 16 + row;
+        ml[i] = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
+        v[i] = *reinterpret_cast<const float4*>(a.part_acc + prow * LV + d);
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, ml[i].x);
+    if (Mb > M) {
+      const float sc = M == -INFINITY ? 0.0f : fast_exp2(M - Mb);
+      L *= sc;
+      o.x *= sc;
+      o.y *= sc;
+      o.z *= sc;
+      o.w *= sc;
+      M = Mb;
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const float wt = ml[i].x == -INFINITY ? 0.0f : fast_exp2(ml[i].x - M);
+      L += ml[i].y * wt;
+      o.x += v[i].x * wt;
+      o.y += v[i].y * wt;
+      o.z += v[i].z * wt;
+      o.w += v[i].w * wt;
+    }
   }
   if (a.sinks) L += fast_exp2(a.sinks[h] * kLog2e - M);
   const float inv = 1.0f / L;
