@@ -156,11 +156,19 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
   if (cs >= total) return;
   const int ce = min(cs + a.chunk, total);
 
-  // the last request whose visible keys start at or before the chunk start
+  // the last request whose visible keys start at or before the chunk start,
+  // by a 64-way search: vis[lo] <= cs always holds (vis[0] = 0); each round
+  // the lanes probe 64 evenly spaced requests of (lo, hi] at once and the
+  // interval shrinks to one step (one memory round trip for up to 65
+  // requests, where halving took one per halving)
   int lo = 0, hi = a.bs - 1;
   while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.vis[mid] <= cs) lo = mid; else hi = mid - 1;
+    const int step = (hi - lo + 63) >> 6;
+    const int p = lo + (lane + 1) * step;
+    const bool le = p <= hi && a.vis[p] <= cs;  // true on a prefix of the lanes
+    const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
+    hi = min(hi, lo + (k + 1) * step - 1);
+    lo += k * step;
   }
 
   char* wbase = lds + w * C::WAVE_BYTES;
