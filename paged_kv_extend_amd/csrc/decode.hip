@@ -58,7 +58,11 @@ struct DecCfg {
   static constexpr int NSI = 2 * NS;  // slot tables in the ring
   static constexpr int SLOT_BYTES = 256;  // one table: 16 int64 slots, written twice (all 64 lanes load)
   static constexpr int WAVE_BYTES = NS * STAGE + NSI * SLOT_BYTES;
-  static constexpr int MERGE_BYTES = NW * 16 * (LV + 2) * 4;
+  // the waves' states for their merge: (m, l) of 16 rows, then the 16 rows'
+  // accumulators at a pitch of LV + 4 floats (16 bytes of padding put the 16
+  // rows one 16-byte write touches on distinct LDS banks)
+  static constexpr int MP = LV + 4;
+  static constexpr int MERGE_BYTES = NW * 16 * (2 + MP) * 4;
   static constexpr int LDS = NW * WAVE_BYTES > MERGE_BYTES ? NW * WAVE_BYTES : MERGE_BYTES;
   static constexpr int NT = NW * 64;
   // loads that may stay in flight in trip t (which issues tile t + NS - 1
@@ -364,14 +368,14 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
     // ---- merge the waves' states through LDS (the stages are free now)
     barrier_fence();
     float* mml = reinterpret_cast<float*>(lds);              // [NW][16][2]
-    float* macc = reinterpret_cast<float*>(lds) + NW * 32;   // [NW][16][LV]
+    float* macc = reinterpret_cast<float*>(lds) + NW * 32;   // [NW][16][MP]
     if (lane < 16) {
       mml[(w * 16 + lane) * 2] = m;
       mml[(w * 16 + lane) * 2 + 1] = lsum;
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<float4*>(macc + (w * 16 + r16) * LV + 16 * db + 4 * j4) =
+      *reinterpret_cast<float4*>(macc + (w * 16 + r16) * C::MP + 16 * db + 4 * j4) =
           make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
     barrier_fence();
 
@@ -379,7 +383,12 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
     const bool single = c0 == c1;
     const int64_t slot = piece_slot(c, v0, a.chunk);
     constexpr int V4 = LV / 4;
-    for (int idx = tid; idx < 16 * V4; idx += C::NT) {
+    static_assert(16 * V4 % C::NT == 0, "merge items per thread");
+    // unrolled by two, so that the LDS reads of two items are issued
+    // together (more would spill the 576-wide rows' registers)
+#pragma unroll 2
+    for (int it = 0; it < 16 * V4 / C::NT; ++it) {
+      const int idx = tid + it * C::NT;
       const int row = idx / V4, d = 4 * (idx % V4);
       if (hb * 16 + row >= G) continue;
       float M = -INFINITY;
@@ -392,7 +401,7 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
         const float mu = mml[(u * 16 + row) * 2];
         const float wt = mu == -INFINITY ? 0.0f : fast_exp2(mu - M);
         L += mml[(u * 16 + row) * 2 + 1] * wt;
-        const float4 v = *reinterpret_cast<const float4*>(macc + (u * 16 + row) * LV + d);
+        const float4 v = *reinterpret_cast<const float4*>(macc + (u * 16 + row) * C::MP + d);
         o.x += v.x * wt;
         o.y += v.y * wt;
         o.z += v.z * wt;
