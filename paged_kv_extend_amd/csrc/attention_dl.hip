@@ -675,18 +675,26 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
     // a sink joins the denominator once, here or in the merge of split chunks
     const float inv = 1.0f / (a.sinks ? l_tot + fast_exp2(a.sinks[g * G + r % G] * kLog2e - m_ref) : l_tot);
     T* orow = reinterpret_cast<T*>(a.o) + (int64_t)(q0 + r / G) * a.o_st + (int64_t)(g * G + r % G) * a.o_sh;
+    // Lanes hi = 0 and 1 of a row hold dims 8 g4 + 4 hi + (0..3) of each
+    // 32-column block; one exchange between them gives each lane 8
+    // consecutive dims, 16 h2 + 8 hi + (0..7), written with one 16-byte
+    // store (half the store instructions of 8-byte writes, and half the
+    // partial cache lines each touches)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = o_block(db) * 32 + 8 * g4 + 4 * hi;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int d = o_block(db) * 32 + 16 * h2 + 8 * hi;
+        bf16x8 ov;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = acc[db][8 * h2 + j], up = acc[db][8 * h2 + 4 + j];  // dims 16 h2 + 4 hi + j, + 8
+          const float got = __shfl_xor(hi ? lo : up, 32);                        // the partner's value this lane needs
+          ov[j] = (__bf16)((hi ? got : lo) * inv);
+          ov[4 + j] = (__bf16)((hi ? up : got) * inv);
+        }
         if (C::LVR < LV && d >= C::LVR) continue;  // padded columns
-        bf16x4 ov;
-        ov[0] = (__bf16)(acc[db][4 * g4] * inv);
-        ov[1] = (__bf16)(acc[db][4 * g4 + 1] * inv);
-        ov[2] = (__bf16)(acc[db][4 * g4 + 2] * inv);
-        ov[3] = (__bf16)(acc[db][4 * g4 + 3] * inv);
-        *reinterpret_cast<bf16x4*>(orow + d) = ov;
+        *reinterpret_cast<bf16x8*>(orow + d) = ov;
       }
     }
   } else {
