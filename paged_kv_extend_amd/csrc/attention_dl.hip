@@ -242,17 +242,18 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   // the zero row, not the next chunk's keys
   const int key_load_last = min(key_last, kt1 * BN - 1);
 
-  // ---- Q^T operand (B) in registers, negated when the scale is negative
-  bf16x8 qr[NQ];
-  {
-    const uint32_t flip = a.neg_q ? 0x80008000u : 0u;
-    gptr<T> qrow = (gptr<T>)a.q + (int64_t)(q0 + (valid ? r / G : 0)) * a.q_st +
-                   (int64_t)(g * G + (valid ? r % G : 0)) * a.q_sh;
+  // ---- slots of the first NS - 1 tables (waves 0 .. NS - 2 build one each):
+  //      from the index array, or the zero row's 8 zero bytes
+  constexpr int EPL = (BN + 63) / 64;  // keys per lane
+  static_assert(NS - 1 <= C::NW, "one first table per wave at most");
+  const bool builds_first = kt0 < kt1 && wv < NS - 1;
+  int64_t sl0[EPL];
+  if (builds_first) {
 #pragma unroll
-    for (int ks = 0; ks < NQ; ++ks) {
-      const int ch = qk_chunk(ks) + hi;
-      const u32x4 v = valid && ch < C::CKR ? *(gptr<u32x4>)(qrow + ch * 8) : u32x4{0u, 0u, 0u, 0u};
-      qr[ks] = __builtin_bit_cast(bf16x8, v ^ flip);
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i, j = (kt0 + wv) * BN + e;
+      const bool real = e < BN && j < sk.n_idx && j <= key_load_last;
+      sl0[i] = *(real ? (gptr<int64_t>)a.kv_indices + ((int64_t)kvs + j) : (gptr<int64_t>)zrow);
     }
   }
 
@@ -396,34 +397,50 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   // lead as its rows (NS-1), so deeper stages deepen both.  Tiles and slots past the end of the
   // range are requested too (zero rows, unused), so every wave has the same
   // number of loads in flight on every trip and the waits are fixed counts.
-  if (kt0 < kt1) {
-    // tables of the first NS-1 tiles straight from global memory: every
-    // lane's slots first (from the index array, or the zero row's 8 zero
-    // bytes), so that they come back in one round trip
-    constexpr int EPL = (BN + 63) / 64;  // keys per lane
-    for (int v = wv; v < NS - 1; v += C::NW) {
-      int64_t sl[EPL];
+
+  // the first NS - 1 tables from their slots (the only loads in flight yet)
+  if (builds_first) {
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i, j = (kt0 + v) * BN + e;
-        const bool real = e < BN && j < sk.n_idx && j <= key_load_last;
-        sl[i] = *(real ? (gptr<int64_t>)a.kv_indices + ((int64_t)kvs + j) : (gptr<int64_t>)zrow);
-      }
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        if (e < BN) {
-          gptr<T> kp, vp;
-          key_ptrs((kt0 + v) * BN + e, sl[i], kp, vp);
-          kptr[(kt0 + v) % NS][e] = kp;
-          vptr[(kt0 + v) % NS][e] = vp;
-        }
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < BN) {
+        gptr<T> kp, vp;
+        key_ptrs((kt0 + wv) * BN + e, sl0[i], kp, vp);
+        kptr[(kt0 + wv) % NS][e] = kp;
+        vptr[(kt0 + wv) % NS][e] = vp;
       }
     }
-    __syncthreads();
-    // the groups that iterations kt0-NS+1 .. kt0-1 would have issued
+  }
+
+  // ---- Q^T operand (B) in registers, negated when the scale is negative
+  //      (requested after the first tables, so that those wait only for
+  //      their slots and the Q rows arrive while tile kt0 is in flight)
+  bf16x8 qr[NQ];
+  {
+    const uint32_t flip = a.neg_q ? 0x80008000u : 0u;
+    gptr<T> qrow = (gptr<T>)a.q + (int64_t)(q0 + (valid ? r / G : 0)) * a.q_st +
+                   (int64_t)(g * G + (valid ? r % G : 0)) * a.q_sh;
 #pragma unroll
-    for (int v = 0; v < NS - 1; ++v) {
+    for (int ks = 0; ks < NQ; ++ks) {
+      const int ch = qk_chunk(ks) + hi;
+      const u32x4 v = valid && ch < C::CKR ? *(gptr<u32x4>)(qrow + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+      qr[ks] = __builtin_bit_cast(bf16x8, v ^ flip);
+    }
+  }
+
+  if (kt0 < kt1) {
+    // the tables published by a barrier that does not wait for the Q rows
+    wait_lds();
+    barrier_fence();
+    // the groups that iterations kt0-NS+1 .. kt0-1 would have issued; tile
+    // kt0 goes out while the Q rows are still arriving, and the full wait
+    // after it (Q rows, slots, tile kt0) leaves no load the compiler tracks
+    // outstanding in the loop
+    if (wv == tw) issue_slots(kt0 + NS - 1);
+    issue_tile(kt0);
+    wait_all_mem();
+#pragma unroll
+    for (int v = 1; v < NS - 1; ++v) {
       if (wv == tw) issue_slots(kt0 + NS - 1 + v);
       issue_tile(kt0 + v);
     }
