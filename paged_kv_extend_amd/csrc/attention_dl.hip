@@ -106,7 +106,13 @@ struct DlCfg {
   // the other has products to run.  Which wave builds the tables is decided
   // per work item (see the kernel).
   static constexpr bool OFFLOAD = SPLIT == 1 && NW == 8 && NS == 2;
-  static constexpr int LOADERS = OFFLOAD ? NW / 2 : NW;   // waves per load group
+  // Eight waves, three stages (head dim 256): one half of the waves issues
+  // every load of a tile (each wave its own chunks and those of the wave 4
+  // apart) -- waves 0..3 when the item has rows for all eight (the other
+  // half of each SIMD then goes straight to its products), waves 4..7 when
+  // it leaves them without rows.
+  static constexpr bool GROUPED = SPLIT == 1 && NW == 8 && NS == 3;
+  static constexpr int LOADERS = OFFLOAD || GROUPED ? NW / 2 : NW;  // waves per load group
   static constexpr int TW = 0;                            // the wave that builds tables (not staggered)
   static constexpr int L = OFFLOAD ? 2 * V_LOADS : K_LOADS + V_LOADS;  // tile loads per wave per tile
   static constexpr int I = BN * 8 / 256;  // row-slot loads (64 lanes x 4 bytes) per tile, table wave
@@ -115,12 +121,16 @@ struct DlCfg {
   // (the row slots of a tile are requested in the same group as the tile
   // NS-1 groups before it, so the tile's wait is the binding one)
   static constexpr int W_TABLE = (NS - 2) * (I + L);
+  // grouped loads: a loading wave issues twice the chunks, the others none
+  static constexpr int L_G = 2 * (K_LOADS + V_LOADS);
+  static constexpr int W_LOADER_G = (NS - 2) * L_G;
+  static constexpr int W_TABLE_G = (NS - 2) * (I + L_G);
   static constexpr int XCH_BYTES = SPLIT > 1 ? NW * BN * 32 * 4 : 0;  // S^T halves exchanged
   static_assert(CK == 8 || CK == 16 || CK == 32 || CK == 72, "lq");
   static_assert(VK ? LV <= LQ : (CV == 8 || CV == 16 || CV == 32), "lv");
   static_assert(!WIDE || VK, "576-wide rows only with V inside K");
   static_assert(K_CHUNKS >= NW && (V_CHUNKS == 0 || V_CHUNKS >= NW), "every wave has a chunk to repeat");
-  static_assert(NS >= 2 && NS <= 5 && W_TABLE < 64 && W_OTHER < 64, "pipeline depth (slot ring of 4)");
+  static_assert(NS >= 2 && NS <= 5 && W_TABLE < 64 && W_OTHER < 64 && W_TABLE_G < 64, "pipeline depth (slot ring of 4)");
   static_assert(!OFFLOAD || (NS == 2 && K_LOADS == V_LOADS), "staggered loads: every wait is vmcnt(0)");
   static_assert(RG >= 2 || SPLIT == 1, "split variant: at least two row groups");
   static_assert(QD % 16 == 0 && VD % 32 == 0, "split");
@@ -229,7 +239,11 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   // finish their tile first and wait at the barrier the longest, while
   // table work on a wave of the V group delays the whole tile.
   const int n_live = min(C::NW, (R - it.t * BM + 31) / 32);  // waves with rows (one row group each when staggered)
-  const int tw = !C::OFFLOAD ? C::TW : n_live < C::NW ? C::NW - 1 : C::LOADERS - 1;
+  // grouped loads: the loading half of the waves, and its table wave
+  const bool upper_loads = C::GROUPED && R - it.t * BM <= (C::RG / 2) * 32;
+  const bool loader = !C::GROUPED || (upper_loads ? wv >= C::LOADERS : wv < C::LOADERS);
+  const int tw = C::GROUPED ? (upper_loads ? C::NW - 1 : C::TW)
+                            : !C::OFFLOAD ? C::TW : n_live < C::NW ? C::NW - 1 : C::LOADERS - 1;
 
   const gptr<T> kpool = (gptr<T>)a.k_pool;
   const gptr<T> vpool = (gptr<T>)a.v_pool;
@@ -325,7 +339,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
     gptr<T> vsrc[PER][C::V_LOADS > 0 ? C::V_LOADS : 1];
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-      const int vw = C::OFFLOAD ? wv % C::LOADERS + q * C::LOADERS : wv;  // wave whose chunks these are
+      const int vw = C::OFFLOAD || C::GROUPED ? wv % C::LOADERS + q * C::LOADERS : wv;  // wave whose chunks these are
       if (do_k) {
 #pragma unroll
         for (int i = 0; i < C::K_LOADS; ++i) {
@@ -347,7 +361,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
     }
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-      const int vw = C::OFFLOAD ? wv % C::LOADERS + q * C::LOADERS : wv;
+      const int vw = C::OFFLOAD || C::GROUPED ? wv % C::LOADERS + q * C::LOADERS : wv;
       if (do_k) {
 #pragma unroll
         for (int i = 0; i < C::K_LOADS; ++i) load_lds_16((gptr<void>)ksrc[q][i], stage + kchunk(i, vw) * 1024);
@@ -363,6 +377,8 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   auto issue_tile = [&](int kt) __attribute__((always_inline)) {
     if constexpr (C::OFFLOAD) {
       issue_loads(kt, wv < C::LOADERS, wv >= C::LOADERS);
+    } else if constexpr (C::GROUPED) {
+      if (loader) issue_loads(kt, true, true);
     } else {
       issue_loads(kt, true, true);
     }
@@ -641,9 +657,11 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   // publishes it and tile kt.
   auto tile_top = [&](int kt) __attribute__((always_inline)) {
     if (wv == tw) {
-      wait_vm<C::W_TABLE>();
+      if constexpr (C::GROUPED) wait_vm<C::W_TABLE_G>(); else wait_vm<C::W_TABLE>();
       write_table(kt + NS - 1);
       wait_lds();
+    } else if constexpr (C::GROUPED) {
+      if (loader) wait_vm<C::W_LOADER_G>(); else wait_vm<0>();
     } else {
       wait_vm<C::W_OTHER>();
     }
