@@ -126,6 +126,11 @@ struct DlCfg {
   static constexpr int W_LOADER_G = (NS - 2) * L_G;
   static constexpr int W_TABLE_G = (NS - 2) * (I + L_G);
   static constexpr int XCH_BYTES = SPLIT > 1 ? NW * BN * 32 * 4 : 0;  // S^T halves exchanged
+  // 576-wide rows: the workgroup's Q rows staged through LDS at the start
+  // (laid out like a K tile), in the space of the stages
+  static constexpr int QST_BYTES = WIDE ? BM * LQ * 2 : 0;
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES + XCH_BYTES > QST_BYTES ? NS * STAGE_BYTES + XCH_BYTES : QST_BYTES;
+  static_assert(QST_BYTES % (1024 * NW) == 0, "Q staging: whole 1 KB loads, the same count per wave");
   static_assert(CK == 8 || CK == 16 || CK == 32 || CK == 72, "lq");
   static_assert(VK ? LV <= LQ : (CV == 8 || CV == 16 || CV == 32), "lv");
   static_assert(!WIDE || VK, "576-wide rows only with V inside K");
@@ -181,7 +186,7 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   constexpr int NQ = C::NQ;
   constexpr int NDB = C::NDB;
 
-  __shared__ __attribute__((aligned(1024))) char lds[NS * C::STAGE_BYTES + C::XCH_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
   __shared__ gptr<T> kptr[NS][BN];  // row pointer tables, slot kt % NS
   __shared__ gptr<T> vptr[NS][BN];
   __shared__ __attribute__((aligned(16))) int64_t slots[4][BN];  // row slots of later tiles, slot kt & 3
@@ -255,6 +260,25 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   // the chunk's range (so that every trip has the same loads in flight) read
   // the zero row, not the next chunk's keys
   const int key_load_last = min(key_last, kt1 * BN - 1);
+
+  // ---- 576-wide rows: the item's Q rows into LDS with whole 1 KB loads, 16
+  //      contiguous bytes per lane (loaded into registers directly, one
+  //      instruction touches 32 rows' cache lines for 32 bytes each, and on
+  //      MLA issuing the 18 per wave took ~8 us), in the K tile's layout:
+  //      row-major at 2 LQ bytes a row, chunk c at swz_k(row, c), so that the
+  //      operand reads below are those of the QK products
+  if constexpr (C::WIDE) {
+#pragma unroll
+    for (int i = 0; i < C::QST_BYTES / 1024 / C::NW; ++i) {
+      const unsigned pos = (unsigned)(i * C::NW + wv) * 64u + (unsigned)lane;  // 16-byte slot of this lane
+      const unsigned row = pos / C::CK;
+      const int cl = swz_k<C>((int)row, (int)(pos % C::CK));  // the logical chunk stored there
+      const int ri = it.t * BM + (int)row;
+      gptr<T> src = zrow + cl * 8;  // rows past the item: zeros
+      if (ri < R) src = (gptr<T>)a.q + (int64_t)(q0 + ri / G) * a.q_st + (int64_t)(g * G + ri % G) * a.q_sh + cl * 8;
+      load_lds_16((gptr<void>)src, lds_addr(lds + 1024 * (i * C::NW + wv)));
+    }
+  }
 
   // ---- slots of the first NS - 1 tables (waves 0 .. NS - 2 build one each):
   //      from the index array, or the zero row's 8 zero bytes
@@ -432,7 +456,22 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
   //      (requested after the first tables, so that those wait only for
   //      their slots and the Q rows arrive while tile kt0 is in flight)
   bf16x8 qr[NQ];
-  {
+  if constexpr (C::WIDE) {
+    // from the staged rows, once every wave's loads (and the table slots)
+    // have landed; a second barrier frees the staging space for the tiles
+    wait_all_mem();
+    barrier_fence();
+    const uint32_t flip = a.neg_q ? 0x80008000u : 0u;
+    const char* qs = lds + rg * 32 * LQ * 2;
+#pragma unroll
+    for (int ks = 0; ks < NQ; ++ks) {
+      const int ch = qk_chunk(ks) + hi;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qs + qi * LQ * 2 + swz_k<C>(qi, ch) * 16);
+      qr[ks] = valid ? __builtin_bit_cast(bf16x8, v ^ flip) : bf16x8{};
+    }
+    wait_lds();
+    barrier_fence();
+  } else {
     const uint32_t flip = a.neg_q ? 0x80008000u : 0u;
     gptr<T> qrow = (gptr<T>)a.q + (int64_t)(q0 + (valid ? r / G : 0)) * a.q_st +
                    (int64_t)(g * G + (valid ? r % G : 0)) * a.q_sh;
@@ -446,8 +485,11 @@ __global__ __launch_bounds__((DlCfg<LQ, LV, BN, VK, RG, SP, NS, DR>::NT), MINB) 
 
   if (kt0 < kt1) {
     // the tables published by a barrier that does not wait for the Q rows
-    wait_lds();
-    barrier_fence();
+    // (576-wide rows: the barriers above did)
+    if constexpr (!C::WIDE) {
+      wait_lds();
+      barrier_fence();
+    }
     // the groups that iterations kt0-NS+1 .. kt0-1 would have issued; tile
     // kt0 goes out while the Q rows are still arriving, and the full wait
     // after it (Q rows, slots, tile kt0) leaves no load the compiler tracks
