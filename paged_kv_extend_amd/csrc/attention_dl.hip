@@ -28,10 +28,16 @@
 //    workgroup.  At 128, waves 0-3 request the next tile's K rows after each
 //    barrier and waves 4-7 its V rows after their QK products (waves w and
 //    w+4 share a SIMD).  At 256 a wave holds all of its 32 rows' Q^T (64
-//    registers) and O^T (128) and takes 32-key tiles in three stages.
+//    registers) and O^T (128) and takes 32-key tiles in three stages; one
+//    half of the waves issues each tile's loads (the half without rows when
+//    the item leaves one).
 //  * When V is the first Lv columns of K (the MLA layout on page
 //    "cpu_graph_runner.py", qkv_proj_with_rope: v = k.narrow(-1, 0, lv)), only
-//    the K tile is loaded and the V^T operand is read from it.
+//    the K tile is loaded and the V^T operand is read from it; the Q rows of
+//    those 576-wide rows are staged through LDS with whole 1 KB loads.
+//  * A workgroup's start requests its first tables' slots before its Q rows
+//    and its first tile while they arrive; its end writes 16 bytes of
+//    output per lane.
 #include "device_common.h"
 #include "pkv_internal.h"
 
