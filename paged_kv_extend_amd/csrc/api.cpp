@@ -3,7 +3,7 @@
 // merge launch that combines the chunks of split items).  Checks use only
 // host-visible sizes, so no call reads device memory or waits for the device
 // -- except in the debug build (PKV_DEBUG), which first checks the index
-// arrays on the device and waits for the verdict.
+// arrays on the device and waits for the result.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -201,7 +201,7 @@ pkv::WsLayout ws_layout(const pkv_attn_desc_t* d, const pkv::Tiling& t, const pk
 
 #ifdef PKV_DEBUG
 // Debug build: validate the index arrays on the device before anything reads
-// them, then wait for the verdict (the one host sync of the library, in this
+// them, then wait for the result (the one host sync of the library, in this
 // build only).  flag: a device word of the workspace the launch sequence
 // does not use yet.
 int debug_check(int32_t* flag, const int32_t* qo_indptr, const int32_t* kv_indptr, const int64_t* kv_indices,
