@@ -296,7 +296,8 @@ __global__ __launch_bounds__((DecCfg<LQ, LV, VK, NW, NS>::NT), 1) void decode_ke
         // read, so that reads stay in flight ahead of the products (left to
         // itself the compiler reused one register and waited for each read
         // before its product: 18 LDS round trips per tile on 576-wide rows).
-        // The barrier keeps the softmax and the V^T reads out of these groups.
+        // The scheduling barrier after the groups keeps the softmax and the
+        // V^T reads out of them.
         {
           constexpr int PRE = NKK < 6 ? NKK : 6;
           __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);  // DS reads
